@@ -1,0 +1,156 @@
+"""Reference block allocator: block tables, on-demand allocation, shared blocks, copy-on-write.
+
+What the pages fix:
+  * KV cache is cut into fixed-size blocks, 16 tokens by default; each sequence owns a block table
+    mapping logical block i to a physical block; a new block is taken only when the last one is
+    full ([ch7] 7.1 「三个关键机制」; [day28] §三 3.1 and §四 4.2).
+  * the pool is a set of uniform blocks and any free block can serve any sequence; blocks return to
+    the pool when a sequence finishes ([ch7] 7.1 「消除碎片」; [day28] §四 4.2, §五).
+  * sequences with a common prefix point at the same physical blocks under a reference count; a
+    sequence that must write into a shared block first gets a new block, the content is copied and
+    the old block's count drops by one ([exp] 「PagedAttention：向操作系统借思路」;
+    [day28] §四 4.2 and §六 items 3-4).
+  * running out of blocks is still possible ([day28] FAQ Q3).
+
+Readings taken where the pages are silent:
+  * free list: a FIFO queue whose initial order is given; freed blocks join its tail in table order.
+  * slot of logical position p: table[p // b] * b + p % b.
+  * append is all-or-nothing: if the free list cannot cover every block it needs, nothing changes.
+"""
+from collections import deque
+from typing import Dict, List, Optional, Sequence, Tuple
+
+
+class AllocError(Exception):
+    """Invalid request (unknown or duplicate sequence id, bad count)."""
+
+
+class OutOfBlocks(Exception):
+    """Not enough free blocks; the allocator state is unchanged."""
+
+
+class RefAllocator:
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise AllocError("num_blocks and block_size must be positive")
+        order = list(range(num_blocks)) if free_order is None else [int(x) for x in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise AllocError("free_order must be a permutation of 0..num_blocks-1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free: deque = deque(order)
+        self.ref: List[int] = [0] * num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.lens: Dict[int, int] = {}
+
+    # -- sequence lifecycle -------------------------------------------------------------------
+    def add_seq(self, sid: int) -> None:
+        if sid in self.tables:
+            raise AllocError(f"sequence {sid} exists")
+        self.tables[sid] = []
+        self.lens[sid] = 0
+
+    def fork(self, parent: int, child: int) -> None:
+        """The child shares every block of the parent; each shared block's count rises by one."""
+        if parent not in self.tables:
+            raise AllocError(f"unknown sequence {parent}")
+        if child in self.tables:
+            raise AllocError(f"sequence {child} exists")
+        self.tables[child] = list(self.tables[parent])
+        self.lens[child] = self.lens[parent]
+        for blk in self.tables[child]:
+            self.ref[blk] += 1
+
+    def free_seq(self, sid: int) -> None:
+        """Drop the sequence; blocks whose count reaches zero go back to the tail of the free list."""
+        if sid not in self.tables:
+            raise AllocError(f"unknown sequence {sid}")
+        for blk in self.tables[sid]:
+            self.ref[blk] -= 1
+            if self.ref[blk] == 0:
+                self.free.append(blk)
+        del self.tables[sid]
+        del self.lens[sid]
+
+    def blocks_needed(self, sid: int, n: int) -> int:
+        """Free blocks an append of n tokens would take (new blocks plus one copy-on-write)."""
+        b = self.block_size
+        length = self.lens[sid]
+        table = self.tables[sid]
+        need = 0
+        if n > 0 and length % b != 0 and self.ref[table[length // b]] > 1:
+            need += 1
+        new_len = length + n
+        need += -(-new_len // b) - len(table)
+        return need
+
+    def append(self, sid: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
+        """Give slots to n new tokens of `sid`.
+
+        Returns (slots, cow_pairs): one slot per token, and the (source, destination) block pairs
+        whose content must be copied before the new tokens are written.
+        """
+        if sid not in self.tables:
+            raise AllocError(f"unknown sequence {sid}")
+        if n < 0:
+            raise AllocError("negative token count")
+        if self.blocks_needed(sid, n) > len(self.free):
+            raise OutOfBlocks(f"sequence {sid}: need {self.blocks_needed(sid, n)} blocks, "
+                              f"{len(self.free)} free")
+        b = self.block_size
+        table = self.tables[sid]
+        slots: List[int] = []
+        cow: List[Tuple[int, int]] = []
+        for _ in range(n):
+            p = self.lens[sid]
+            logical = p // b
+            if p % b == 0:
+                # first token of a new logical block: take the head of the free list
+                blk = self.free.popleft()
+                self.ref[blk] = 1
+                table.append(blk)
+            elif self.ref[table[logical]] > 1:
+                # writing into a block someone else also points at: copy it first
+                old = table[logical]
+                new = self.free.popleft()
+                self.ref[old] -= 1
+                self.ref[new] = 1
+                table[logical] = new
+                cow.append((old, new))
+            slots.append(table[logical] * b + p % b)
+            self.lens[sid] = p + 1
+        return slots, cow
+
+    # -- inspection ---------------------------------------------------------------------------
+    def table(self, sid: int) -> List[int]:
+        return list(self.tables[sid])
+
+    def length(self, sid: int) -> int:
+        return self.lens[sid]
+
+    def refcount(self, blk: int) -> int:
+        return self.ref[blk]
+
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def free_list(self) -> List[int]:
+        return list(self.free)
+
+    def check_invariants(self) -> None:
+        """Invariants the pages state: tail waste below one block ([day28] §四 4.2), every block is
+        either free or referenced ([ch7] 7.1 「消除碎片」), counts equal the number of tables holding
+        the block ([day28] §六 item 3)."""
+        b = self.block_size
+        count = [0] * self.num_blocks
+        for sid, tab in self.tables.items():
+            assert len(tab) == -(-self.lens[sid] // b), "table length != ceil(len / b)"
+            assert len(tab) * b - self.lens[sid] <= b - 1, "tail waste exceeds b - 1 slots"
+            for blk in tab:
+                count[blk] += 1
+        assert count == self.ref, "reference counts differ from table membership"
+        free = set(self.free)
+        assert len(free) == len(self.free), "duplicate block on the free list"
+        used = {i for i, c in enumerate(count) if c > 0}
+        assert not (free & used), "a referenced block is on the free list"
+        assert free | used == set(range(self.num_blocks)), "a block is neither free nor referenced"

@@ -1,0 +1,67 @@
+"""The physical KV pool: slot addressing, writing new tokens, block copies, gathering a sequence.
+
+Pool layout (a reading; the pages fix only that a block holds the K/V of b consecutive tokens and
+is contiguous inside, [day28] §三 3.1-3.2): K and V are two separate arrays, each
+[num_blocks][num_kv_heads][block_size][head_dim] of stored codes (uint32 fp32 bits, uint16 bf16
+bits or uint8 e4m3 codes).
+
+Slot of logical position p of a sequence with table T: T[p // b] * b + p % b, as in the
+block-table figure of [day28] §三 3.1 (table [7, 1, 3]: logical block 0 -> physical 7 holds
+tokens 0-15, block 1 -> physical 1 holds tokens 16-31, block 2 -> physical 3 holds 32-47).
+"""
+from typing import Sequence
+
+import numpy as np
+
+from .codecs import e4m3_quantise, f32_bits_to_f64, bf16_bits_to_f64
+
+
+def slot_of(table: Sequence[int], p: int, block_size: int) -> int:
+    """Slot (physical block * b + offset) of logical position p."""
+    return int(table[p // block_size]) * block_size + p % block_size
+
+
+def ref_cache_write(pool: np.ndarray, x_bits: np.ndarray, slots: Sequence[int], kv_dtype: str,
+                    act_dtype: str, scale: float = 1.0) -> None:
+    """Write token rows into their slots, in place.
+
+    pool   : [num_blocks, Hkv, b, D] stored codes
+    x_bits : [T, Hkv, D] bit patterns of the new rows in the activation dtype
+             (uint32 for fp32, uint16 for bf16)
+    slots  : [T] int; a negative slot means "skip this token"
+    For an fp8 pool each value is quantised with `scale` (codecs.e4m3_quantise); otherwise the
+    bit pattern is stored unchanged (pool dtype == activation dtype).
+    """
+    b = pool.shape[2]
+    for t, s in enumerate(slots):
+        s = int(s)
+        if s < 0:
+            continue
+        blk, off = s // b, s % b
+        if kv_dtype == "fp8":
+            if act_dtype == "bf16":
+                vals = bf16_bits_to_f64(x_bits[t]).astype(np.float32)
+            else:
+                vals = f32_bits_to_f64(x_bits[t]).astype(np.float32)
+            pool[blk, :, off, :] = e4m3_quantise(vals, scale)
+        else:
+            assert kv_dtype == act_dtype, "a non-fp8 pool stores the activation dtype"
+            pool[blk, :, off, :] = x_bits[t]
+
+
+def ref_copy_blocks(pool: np.ndarray, pairs: Sequence) -> None:
+    """Copy-on-write: block dst receives the content of block src, for each (src, dst) pair, in order
+    ([day28] §四 4.2, §六 item 4)."""
+    for src, dst in pairs:
+        pool[int(dst)] = pool[int(src)].copy()
+
+
+def gather_seq(pool_vals: np.ndarray, table: Sequence[int], length: int) -> np.ndarray:
+    """Contiguous [length, Hkv, D] K (or V) of a sequence, rebuilt through its block table
+    ([day28] §三 3.1: the kernel reaches scattered K/V by indirection through the table)."""
+    b = pool_vals.shape[2]
+    hkv, d = pool_vals.shape[1], pool_vals.shape[3]
+    out = np.empty((length, hkv, d), dtype=np.float64)
+    for p in range(length):
+        out[p] = pool_vals[int(table[p // b]), :, p % b, :]
+    return out
