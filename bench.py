@@ -1,0 +1,190 @@
+"""Benchmark of one paged-attention step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--block-size B]
+
+A step is the whole device path over one batch: copy-on-write block copies, the cache write of the
+step's new tokens, chunked prefill (when the workload has one) and paged decode, with every input
+already resident in HBM.  The default workload is the shared-prefix decode (256 sequences of a
+512-token shared prefix plus a private suffix of 512..2560 tokens, 40 query = 40 KV heads,
+head_dim 128, bf16, 16-token blocks, one copy-on-write per sequence).
+
+Prints one JSON line.  `value` is the decode's unique KV bytes per step (each physical block once)
+divided by the step time, in GB/s.  `roofline` prices the decode kernels (partition + merge),
+timed with HIP events on the launch stream, against the 8 TB/s HBM peak.  `cpu_baseline` is the
+fp64 CPU oracle timed on a bounded sample of the same workload on this host's cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synth import make_workload, poison_code, elem_bytes  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def decode_bytes(wl, tables: np.ndarray):
+    """(unique KV bytes, logical KV bytes, other bytes) read/written by one decode launch."""
+    b, e = wl.block_size, elem_bytes(wl.kv_dtype)
+    row = wl.num_kv_heads * wl.head_dim * e * 2              # K + V of one token, all KV heads
+    used = {}
+    logical = 0
+    for s, L in enumerate(wl.decode_lens):
+        L = int(L)
+        logical += L
+        for j in range(-(-L // b)):
+            blk = int(tables[s, j])
+            used[blk] = max(used.get(blk, 0), min(b, L - j * b))
+    unique_tokens = sum(used.values())
+    act = 2 if wl.act_dtype == "bf16" else 4
+    qo = 2 * len(wl.decode_lens) * wl.num_q_heads * wl.head_dim * act
+    tab = sum(-(-int(L) // b) for L in wl.decode_lens) * 4 + len(wl.decode_lens) * 4
+    return unique_tokens * row, logical * row, qo + tab
+
+
+def prefill_flops(wl) -> float:
+    """Causal pairs only: 4 * D * Hq * sum over chunk queries of the keys each one sees."""
+    tot = 0
+    for p, c in zip(wl.prefill_prior, wl.prefill_chunk):
+        p, c = int(p), int(c)
+        tot += c * p + c * (c + 1) // 2
+    return 4.0 * wl.head_dim * wl.num_q_heads * tot
+
+
+def cpu_baseline(wl, budget_s: float):
+    """fp64 oracle decode on a bounded sample of the workload's sequences (host cores)."""
+    from oracle import ref_decode
+    from oracle.run import logical_view, tensor_bits, act_values, _stored_values
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    lg = logical_view(wl)
+    order = np.random.default_rng(0).permutation(len(wl.decode_seqs))
+    done_seqs, done_bytes, spent = 0, 0, 0.0
+    row = wl.num_kv_heads * wl.head_dim * elem_bytes(wl.kv_dtype) * 2
+    for bi in order:
+        sid = wl.decode_seqs[bi]
+        L = int(wl.decode_lens[bi])
+        idx = torch.as_tensor(lg.token_rows(sid, L), dtype=torch.long, device=wl.k_tok.device)
+        k = _stored_values(tensor_bits(wl.k_tok.index_select(0, idx)), wl, "k")   # inputs staged untimed
+        v = _stored_values(tensor_bits(wl.v_tok.index_select(0, idx)), wl, "v")
+        q = act_values(tensor_bits(wl.q_decode[bi:bi + 1]), wl.act_dtype)
+        t = time.perf_counter()
+        ref_decode(q, [(k, v)], wl.scale)
+        spent += time.perf_counter() - t
+        done_seqs += 1
+        done_bytes += L * row
+        if spent >= budget_s:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_seqs} of {len(wl.decode_seqs)} decode sequences, all {wl.num_q_heads} query heads, "
+                      f"fp64 NumPy, {spent:.1f} s",
+            "decode_tokens_per_s_per_layer": round(done_seqs / spent, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="shared_prefix_bf16")
+    ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design note, not code)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    from paged_kv_cache_427_amd.engine import PagedKVEngine
+
+    dev = torch.device("cuda:0")
+    t_setup = time.time()
+    wl = make_workload(args.config, "full", device=dev, block_size=args.block_size)
+    eng = PagedKVEngine(wl, device=dev, poison=poison_code(wl.kv_dtype))
+    eng.build_history()
+    si = eng.prepare_step(args.partition)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.config}: setup {time.time() - t_setup:.1f}s, blocks {wl.num_blocks}, "
+          f"tokens {wl.num_tokens}", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    nev = 5
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        eng.copy_step(si)
+        if ev: ev[1].record(stream)
+        eng.write_step(si)
+        if ev: ev[2].record(stream)
+        eng.prefill_step(si)
+        if ev: ev[3].record(stream)
+        eng.decode_step(si)
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    parts = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(nev - 1)]
+                      for i in range(args.steps)])
+    ms_copy, ms_write, ms_prefill, ms_decode = parts.mean(axis=0)
+
+    res = {"metric": "paged decode KV-read GB/s (% of MI355X HBM peak); decode tokens/s per layer",
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": {"bf16": "bf16", "f32": "f32", "fp8": "fp8_e4m3 KV, bf16 q"}[wl.kv_dtype],
+           "data": "synthetic (seeded N(0,1) K/V/Q, lengths and block order as in the workload)"}
+    cfg = {"workload": args.config, "num_seqs": len(wl.decode_seqs) or len(wl.prefill_seqs),
+           "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+           "block_size": wl.block_size, "pool_blocks": wl.num_blocks, "kv_dtype": wl.kv_dtype,
+           "partition": si.dec_partition or 512}
+    tab = si.dec_tables.cpu().numpy() if si.dec_tables is not None else None
+    if tab is not None:
+        uniq, logical, other = decode_bytes(wl, tab)
+        res["value"] = round(uniq / (ms_step * 1e-3) / 1e9, 2)
+        res["decode_tokens_per_s_per_layer"] = round(len(wl.decode_lens) / (ms_step * 1e-3), 1)
+        achieved = (uniq + other) / (ms_decode * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                           "kernel": "pa_decode (partition kernel + merge kernel)",
+                           "algorithmic_bytes_per_launch": int(uniq + other)}
+        res["decode_logical_kv_GBps"] = round(logical / (ms_decode * 1e-3) / 1e9, 1)
+        cfg["mean_context"] = round(float(np.mean(wl.decode_lens)), 1)
+    else:
+        res["value"] = None
+    if wl.prefill_seqs:
+        fl = prefill_flops(wl)
+        res["prefill_tflops"] = round(fl / (ms_prefill * 1e-3) / 1e12, 1)
+        res["prefill_mfma_frac"] = round(fl / (ms_prefill * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+    res["kernel_ms"] = {"copy_blocks": round(ms_copy, 4), "cache_write": round(ms_write, 4),
+                        "prefill": round(ms_prefill, 4), "decode": round(ms_decode, 4)}
+    res["config"] = cfg
+    if not args.no_cpu_baseline and wl.decode_seqs:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+/*
+ * pa.h -- C ABI of libpa: paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages cited by title):
+ *   [ch7]   «第 7 章推理框架：vLLM 与 PagedAttention»
+ *   [exp]   «vLLM 与 PagedAttention：把 GPU 显存当操作系统内存管»
+ *   [day28] «GPU 学习日报 Day 28：vLLM 与 PagedAttention：GPU Memory 管理的艺术»
+ * The KV cache is cut into fixed-size blocks (16 tokens by default) that lie anywhere in a physical
+ * pool; each sequence's block table maps its logical blocks to physical ones; blocks of a common
+ * prefix are shared under a reference count and copied before a write (copy-on-write); attention
+ * reaches a sequence's scattered K/V through its table ([ch7] 7.1; [exp] PagedAttention section;
+ * [day28] §三 3.1-3.2, §四 4.2, §六).
+ *
+ * Conventions for every call:
+ *   - Every call returns pa_status; no exception or abort crosses this boundary.  On failure the
+ *     text of pa_last_error() (thread-local) says what was wrong.
+ *   - Device pointers are caller-owned (typically allocated by PyTorch) and must stay valid until
+ *     the work queued on `stream` has finished.  The library never allocates device memory.
+ *   - Host arguments are validated (null pointers, dtypes, shapes, sizes); values that live in
+ *     device memory (slots, tables, lengths, copy pairs) are NOT validated: an out-of-range value
+ *     there is undefined behaviour (the caller's allocator produces them; see pa_alloc_*).
+ *   - Launches are asynchronous on `stream` (a hipStream_t; NULL = the default stream), in order,
+ *     with no implicit synchronisation.  Calls that overlap on different streams and touch the same
+ *     pool blocks race.
+ *
+ * Pool layout (fixed by this ABI).  K and V live in two separate device arrays, each
+ *     [num_blocks][num_kv_heads][block_size][head_dim]
+ * of elements of `dtype`, row-major.  One (block, KV head) tile is block_size * head_dim elements
+ * contiguous in memory, so the tokens of one block are read with whole-cache-line loads and the
+ * only indirection is one table lookup per block ([day28] §三 3.2: contiguous inside a block, a
+ * pointer jump between blocks).  Token at slot s lies in block s / block_size, row
+ * s % block_size.  An fp8 pool stores OCP e4m3 codes; value = decode(code) * scale, with one fp32
+ * scale per pool (k_scale for K, v_scale for V).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,     /* a host argument is out of range or null */
+  PA_ERR_OOM = 2,         /* allocator: not enough free blocks (state unchanged) */
+  PA_ERR_HIP = 3,         /* the HIP runtime reported an error (launch or device query) */
+  PA_ERR_UNSUPPORTED = 4  /* a valid combination this build has no kernel for */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,      /* IEEE binary32 */
+  PA_BF16 = 1,     /* bfloat16 */
+  PA_FP8_E4M3 = 2  /* OCP 8-bit E4M3 ("FN"): bias 7, no infinities, max 448 (pools only) */
+} pa_dtype;
+
+/* A KV pool.  Supported: block_size in {8, 16, 32}; head_dim in {64, 128};
+ * dtype PA_F32, PA_BF16 or PA_FP8_E4M3; scales are used only for PA_FP8_E4M3 (must be > 0). */
+typedef struct pa_pool_desc {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;   /* pa_dtype */
+  float k_scale;
+  float v_scale;
+} pa_pool_desc;
+
+typedef void* pa_stream; /* hipStream_t */
+
+/* Short name of a status code (static string). */
+const char* pa_status_str(int32_t status);
+/* Detail of the last failure on this thread (static thread-local buffer; "" after success). */
+const char* pa_last_error(void);
+/* ABI version: (major << 16) | minor. */
+int32_t pa_version(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_cache_write -- scatter new tokens' K and V into their slots.
+ * [day28] FAQ Q4: K/V produced by prefill are written into pool blocks just as decode's are;
+ * [ch7] 7.1: each generated token's K/V goes into the sequence's current block.
+ *
+ *   k, v          device [num_tokens][num_kv_heads][head_dim] of in_dtype (PA_F32 or PA_BF16),
+ *                 contiguous rows
+ *   slot_mapping  device int64 [num_tokens]; token t goes to slot slot_mapping[t]; a negative slot
+ *                 skips the token
+ *   k_pool/v_pool device pools described by `pool`
+ * A PA_F32 / PA_BF16 pool must have dtype == in_dtype and receives the bits unchanged.  A
+ * PA_FP8_E4M3 pool receives, per element, e4m3(round_to_nearest_even(clamp(x * inv, -448, 448)))
+ * where inv = fp32(1 / scale) is rounded once on the host and the product is an fp32 multiply.
+ * Slots must be distinct among non-negative entries (duplicate slots race).
+ * num_tokens == 0 is a no-op.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_cache_write(const void* k, const void* v, int32_t in_dtype, int64_t num_tokens,
+                         const int64_t* slot_mapping, void* k_pool, void* v_pool,
+                         const pa_pool_desc* pool, pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_copy_blocks -- copy-on-write block copies ([day28] §四 4.2, §六 item 4: a sequence about to
+ * write a shared block gets a new block holding a copy of it).
+ *
+ *   pairs  device int32 [num_pairs][2] = (source block, destination block), as returned by
+ *          pa_alloc_append.  Whole K and V blocks (all KV heads) are copied.  Destinations must be
+ *          distinct and must not appear as a source in the same call (copies run concurrently).
+ * num_pairs == 0 is a no-op.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool, const int32_t* pairs,
+                         int32_t num_pairs, pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for these sizes.
+ *   partition_size 0 means the library's choice (the same choice pa_decode makes for 0).
+ * Zero bytes when every sequence fits one partition (max_context_len <= partition size).
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t max_context_len, int32_t partition_size, size_t* bytes);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_decode -- one query token per sequence attends to its cached context through its table.
+ * [day28] §三 3.1-3.2: the kernel gathers the scattered K/V by indirection through the block table,
+ * dotting the query with every cached key and combining the values.  For sequence s and query head
+ * h (KV head g = h / (num_q_heads / num_kv_heads)):
+ *     out[s,h,:] = sum_j softmax_j(scale * q[s,h,:] . K_s[j,g,:]) V_s[j,g,:],   0 <= j < L_s
+ * with K_s[j] = k_pool[table[s][j / b]][g][j % b] (times k_scale for fp8; V likewise).
+ *
+ *   q             device [num_seqs][num_q_heads][head_dim] of q_dtype (PA_F32 or PA_BF16)
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past ceil(L_s / b) unused
+ *   context_lens  device int32 [num_seqs]; L_s in [0, max_context_len]; L_s == 0 gives zeros
+ *   num_q_heads   multiple of pool->num_kv_heads; group size num_q_heads / num_kv_heads in {1,2,4,8}
+ *   scale         fp32 softmax scale (e.g. fp32(1/sqrt(head_dim)))
+ *   partition_size  tokens per context partition, a positive multiple of 32 (0 = library choice).  A
+ *                 sequence longer than one partition is processed partition by partition and
+ *                 merged by a second kernel (max, rescaled sums).
+ *   max_context_len  an upper bound of every L_s (sizes the launch)
+ *   workspace     device buffer of at least pa_decode_workspace_size(...) bytes (may be NULL when
+ *                 that size is 0); its content on entry does not matter
+ *   out           device [num_seqs][num_q_heads][head_dim] of out_dtype (PA_F32 or PA_BF16;
+ *                 bf16 rounds to nearest-even from the fp32 accumulator)
+ * Combinations: pool PA_F32 needs q PA_F32; pools PA_BF16 / PA_FP8_E4M3 need q PA_BF16.
+ * Results are deterministic (no atomics; fixed reduction order).
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
+                    const pa_pool_desc* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                    int32_t partition_size, int32_t max_context_len, void* workspace,
+                    size_t workspace_bytes, void* out, int32_t out_dtype, pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_prefill_chunk -- causal attention of a chunk of new query tokens per sequence over the
+ * sequence's paged context plus the chunk itself ([day28] FAQ Q4: prefill K/V are written into
+ * pool blocks; chunked prefill slices a long prompt and is scheduled together with decode).
+ * The chunk's own K/V must already be in the pool (pa_cache_write first).  Query i of sequence s
+ * sits at position P_s + i and attends keys 0 .. P_s + i inclusive, all read through the table.
+ *
+ *   q                  device [total_q][num_q_heads][head_dim] bf16, chunks back to back
+ *   query_start_loc    device int32 [num_seqs + 1]; chunk of s = rows [qsl[s], qsl[s+1])
+ *   prior_context_lens device int32 [num_seqs]; P_s tokens held before the chunk
+ *   max_chunk_len      upper bound of every chunk length (sizes the launch)
+ *   out                device [total_q][num_q_heads][head_dim], PA_BF16 or PA_F32
+ * Pools: PA_BF16 or PA_FP8_E4M3, head_dim 128.  The products run on bf16 MFMA with fp32
+ * accumulation (fp8 K/V are widened to bf16 exactly; scales are applied in fp32).
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_prefill_chunk(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
+                           const pa_pool_desc* pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* query_start_loc,
+                           const int32_t* prior_context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           float scale, int32_t max_chunk_len, void* out, int32_t out_dtype,
+                           pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Self-check of the device fp8 decoding: out[c] = value of e4m3 code c (c = 0..255) as decoded by
+ * the same conversion the attention kernels use (NaN codes give NaN).  out: device float [256].
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_fp8_decode_table(float* out, pa_stream stream);
+
+/* =============================================================================================
+ * Host block allocator (no GPU).  [ch7] 7.1 「三个关键机制」; [exp] PagedAttention section;
+ * [day28] §三 3.1, §四 4.2, §六, FAQ Q3.
+ *   - blocks of block_size token slots; a sequence takes a new block only when its last block is
+ *     full; the free list is a FIFO queue whose initial order the caller gives (any free block
+ *     serves any sequence); a finished sequence's blocks whose count drops to zero join its tail,
+ *     in table order;
+ *   - fork: the child shares all of the parent's blocks (each count + 1);
+ *   - append: a token landing in a block whose count is > 1 first moves the sequence to a fresh
+ *     block (copy-on-write); the (source, destination) pair is reported so the caller can run
+ *     pa_copy_blocks before writing the token;
+ *   - all-or-nothing: PA_ERR_OOM leaves the state unchanged.
+ * A handle is not thread-safe; use one per thread or lock around it.
+ * ============================================================================================= */
+typedef struct pa_allocator pa_allocator;
+
+/* initial_free_order: host int32 [num_blocks], a permutation of 0..num_blocks-1 (NULL = 0..N-1). */
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order,
+                          pa_allocator** out);
+void pa_alloc_destroy(pa_allocator* a);
+/* New empty sequence; PA_ERR_INVALID if the id exists. */
+pa_status pa_alloc_add_seq(pa_allocator* a, int64_t seq_id);
+/* child shares every block of parent; PA_ERR_INVALID if parent is unknown or child exists. */
+pa_status pa_alloc_fork(pa_allocator* a, int64_t parent_id, int64_t child_id);
+/* Slots for n_tokens new tokens of seq_id, written to host int64 slots_out[n_tokens]; the
+ * copy-on-write pairs (at most one per call) go to host int32 cow_pairs_out[cow_cap][2] and their
+ * count to *n_cow_out.  PA_ERR_OOM (state unchanged) if the free list is too short;
+ * PA_ERR_INVALID if cow_cap is too small for the copies needed. */
+pa_status pa_alloc_append(pa_allocator* a, int64_t seq_id, int32_t n_tokens, int64_t* slots_out,
+                          int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out);
+/* Appends for several distinct sequences in order, all-or-nothing across the batch.  slots_out
+ * receives sum(n_tokens) slots, sequence after sequence. */
+pa_status pa_alloc_append_batch(pa_allocator* a, const int64_t* seq_ids, const int32_t* n_tokens,
+                                int32_t num_seqs, int64_t* slots_out, int32_t* cow_pairs_out,
+                                int32_t cow_cap, int32_t* n_cow_out);
+/* Free blocks an append of n_tokens would take (new blocks plus a copy-on-write). */
+pa_status pa_alloc_blocks_needed(const pa_allocator* a, int64_t seq_id, int32_t n_tokens,
+                                 int32_t* out);
+/* Drop the sequence; blocks reaching count 0 join the free list. */
+pa_status pa_alloc_free_seq(pa_allocator* a, int64_t seq_id);
+pa_status pa_alloc_seq_len(const pa_allocator* a, int64_t seq_id, int64_t* len_out);
+/* The sequence's table into host int32 out[cap]; *n_out = its length (PA_ERR_INVALID if > cap). */
+pa_status pa_alloc_block_table(const pa_allocator* a, int64_t seq_id, int32_t* out, int32_t cap,
+                               int32_t* n_out);
+/* Tables of several sequences as rows of host int32 out[num_seqs][max_blocks], padded with `pad`. */
+pa_status pa_alloc_fill_tables(const pa_allocator* a, const int64_t* seq_ids, int32_t num_seqs,
+                               int32_t* out, int32_t max_blocks, int32_t pad);
+pa_status pa_alloc_refcount(const pa_allocator* a, int32_t block, int32_t* out);
+pa_status pa_alloc_stats(const pa_allocator* a, int32_t* num_free, int32_t* num_used,
+                         int64_t* total_refs);
+/* The free list in queue order into host int32 out[cap]; *n_out = its length. */
+pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,90 @@
+"""ctypes declarations of libpa.so (include/pa.h).  Loading fails loudly if the library is missing."""
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_HIP, PA_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+
+
+class PoolDesc(ctypes.Structure):
+    """pa_pool_desc: pools are [num_blocks][num_kv_heads][block_size][head_dim] of `dtype`."""
+    _fields_ = [("num_blocks", c_int32), ("block_size", c_int32), ("num_kv_heads", c_int32),
+                ("head_dim", c_int32), ("dtype", c_int32), ("k_scale", c_float), ("v_scale", c_float)]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class OutOfBlocks(PaError):
+    pass
+
+
+_STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID", 2: "PA_ERR_OOM", 3: "PA_ERR_HIP", 4: "PA_ERR_UNSUPPORTED"}
+
+_I32P = POINTER(c_int32)
+_I64P = POINTER(c_int64)
+
+_PROTOS = {
+    "pa_status_str": (c_char_p, [c_int32]),
+    "pa_last_error": (c_char_p, []),
+    "pa_version": (c_int32, []),
+    "pa_cache_write": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_void_p, c_void_p, c_void_p,
+                                 POINTER(PoolDesc), c_void_p]),
+    "pa_copy_blocks": (c_int32, [c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_int32, c_void_p]),
+    "pa_decode_workspace_size": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_size_t)]),
+    "pa_decode": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_int32,
+                            c_void_p, c_int32, c_int32, c_float, c_int32, c_int32, c_void_p, c_size_t,
+                            c_void_p, c_int32, c_void_p]),
+    "pa_prefill_chunk": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p,
+                                   c_int32, c_void_p, c_void_p, c_int32, c_int32, c_float, c_int32,
+                                   c_void_p, c_int32, c_void_p]),
+    "pa_fp8_decode_table": (c_int32, [c_void_p, c_void_p]),
+    "pa_alloc_create": (c_int32, [c_int32, c_int32, _I32P, POINTER(c_void_p)]),
+    "pa_alloc_destroy": (None, [c_void_p]),
+    "pa_alloc_add_seq": (c_int32, [c_void_p, c_int64]),
+    "pa_alloc_fork": (c_int32, [c_void_p, c_int64, c_int64]),
+    "pa_alloc_append": (c_int32, [c_void_p, c_int64, c_int32, _I64P, _I32P, c_int32, _I32P]),
+    "pa_alloc_append_batch": (c_int32, [c_void_p, _I64P, _I32P, c_int32, _I64P, _I32P, c_int32, _I32P]),
+    "pa_alloc_blocks_needed": (c_int32, [c_void_p, c_int64, c_int32, _I32P]),
+    "pa_alloc_free_seq": (c_int32, [c_void_p, c_int64]),
+    "pa_alloc_seq_len": (c_int32, [c_void_p, c_int64, _I64P]),
+    "pa_alloc_block_table": (c_int32, [c_void_p, c_int64, _I32P, c_int32, _I32P]),
+    "pa_alloc_fill_tables": (c_int32, [c_void_p, _I64P, c_int32, _I32P, c_int32, c_int32]),
+    "pa_alloc_refcount": (c_int32, [c_void_p, c_int32, _I32P]),
+    "pa_alloc_stats": (c_int32, [c_void_p, _I32P, _I32P, _I64P]),
+    "pa_alloc_free_list": (c_int32, [c_void_p, _I32P, c_int32, _I32P]),
+}
+
+EXPORTED = tuple(_PROTOS)
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises ImportError when libpa.so has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_427_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _PROTOS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != PA_OK:
+        msg = lib().pa_last_error().decode(errors="replace")
+        if status == PA_ERR_OOM:
+            raise OutOfBlocks(status, msg)
+        raise PaError(status, msg)

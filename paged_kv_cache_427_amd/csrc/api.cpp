@@ -1,0 +1,279 @@
+// C-ABI layer of libpa: argument validation, derived launch parameters, dispatch to the kernels.
+// Every entry point returns a pa_status; failures leave a message in a thread-local buffer.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+constexpr int kDefaultPartition = 512;
+constexpr int kMaxGridYZ = 65535;
+
+pa_status hip_fail(int e, const char* where) {
+  std::snprintf(g_err, sizeof g_err, "%s: %s", where, hipGetErrorString(static_cast<hipError_t>(e)));
+  return PA_ERR_HIP;
+}
+
+pa_status launch_status(int rc, const char* where) {
+  if (rc == 0) return pa_ok();
+  if (rc < 0) return pa_fail(PA_ERR_UNSUPPORTED, where);
+  return hip_fail(rc, where);
+}
+
+bool is_pow2_block(int b) { return b == 8 || b == 16 || b == 32; }
+
+pa_status check_pool(const pa_pool_desc* p, const char* who) {
+  static thread_local char msg[256];
+  if (!p) {
+    std::snprintf(msg, sizeof msg, "%s: pool descriptor is null", who);
+    return pa_fail(PA_ERR_INVALID, msg);
+  }
+  if (p->num_blocks <= 0 || p->num_kv_heads <= 0) {
+    std::snprintf(msg, sizeof msg, "%s: num_blocks and num_kv_heads must be positive", who);
+    return pa_fail(PA_ERR_INVALID, msg);
+  }
+  if (!is_pow2_block(p->block_size)) {
+    std::snprintf(msg, sizeof msg, "%s: block_size must be 8, 16 or 32 (got %d)", who, p->block_size);
+    return pa_fail(PA_ERR_INVALID, msg);
+  }
+  if (p->head_dim != 64 && p->head_dim != 128) {
+    std::snprintf(msg, sizeof msg, "%s: head_dim must be 64 or 128 (got %d)", who, p->head_dim);
+    return pa_fail(PA_ERR_INVALID, msg);
+  }
+  if (p->dtype != PA_F32 && p->dtype != PA_BF16 && p->dtype != PA_FP8_E4M3) {
+    std::snprintf(msg, sizeof msg, "%s: unknown pool dtype %d", who, p->dtype);
+    return pa_fail(PA_ERR_INVALID, msg);
+  }
+  if (p->dtype == PA_FP8_E4M3 && !(std::isfinite(p->k_scale) && p->k_scale > 0.f &&
+                                   std::isfinite(p->v_scale) && p->v_scale > 0.f)) {
+    std::snprintf(msg, sizeof msg, "%s: fp8 pool scales must be finite and positive", who);
+    return pa_fail(PA_ERR_INVALID, msg);
+  }
+  return PA_OK;
+}
+
+int elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : 1; }
+
+int64_t decode_max_parts(int32_t max_ctx, int32_t part) {
+  if (max_ctx <= 0) return 1;
+  return (static_cast<int64_t>(max_ctx) + part - 1) / part;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+pa_status pa_fail(pa_status st, const char* msg) {
+  std::snprintf(g_err, sizeof g_err, "%s", msg);
+  return st;
+}
+
+pa_status pa_ok() {
+  g_err[0] = '\0';
+  return PA_OK;
+}
+
+extern "C" {
+
+const char* pa_status_str(int32_t s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID: return "PA_ERR_INVALID";
+    case PA_ERR_OOM: return "PA_ERR_OOM";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+const char* pa_last_error(void) { return g_err; }
+
+int32_t pa_version(void) { return (1 << 16) | 0; }
+
+pa_status pa_cache_write(const void* k, const void* v, int32_t in_dtype, int64_t num_tokens,
+                         const int64_t* slots, void* k_pool, void* v_pool, const pa_pool_desc* pool,
+                         pa_stream stream) {
+  pa_status st = check_pool(pool, "pa_cache_write");
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return pa_fail(PA_ERR_INVALID, "pa_cache_write: negative num_tokens");
+  if (in_dtype != PA_F32 && in_dtype != PA_BF16)
+    return pa_fail(PA_ERR_INVALID, "pa_cache_write: in_dtype must be PA_F32 or PA_BF16");
+  if (pool->dtype != PA_FP8_E4M3 && pool->dtype != in_dtype)
+    return pa_fail(PA_ERR_INVALID, "pa_cache_write: an f32/bf16 pool must have the dtype of k and v");
+  if (num_tokens == 0) return pa_ok();
+  if (!k || !v || !slots || !k_pool || !v_pool) return pa_fail(PA_ERR_INVALID, "pa_cache_write: null pointer");
+  if (num_tokens * pool->num_kv_heads * (pool->head_dim / 4) > (int64_t(1) << 40))
+    return pa_fail(PA_ERR_INVALID, "pa_cache_write: too many tokens for one launch");
+  pa::CacheWriteArgs a{};
+  a.k = k;
+  a.v = v;
+  a.in_dtype = in_dtype;
+  a.num_tokens = num_tokens;
+  a.slots = slots;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_size = pool->block_size;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.pool_dtype = pool->dtype;
+  a.k_inv_scale = pool->dtype == PA_FP8_E4M3 ? 1.0f / pool->k_scale : 1.0f;
+  a.v_inv_scale = pool->dtype == PA_FP8_E4M3 ? 1.0f / pool->v_scale : 1.0f;
+  return launch_status(pa::launch_cache_write(a, stream), "pa_cache_write");
+}
+
+pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool, const int32_t* pairs,
+                         int32_t num_pairs, pa_stream stream) {
+  pa_status st = check_pool(pool, "pa_copy_blocks");
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return pa_fail(PA_ERR_INVALID, "pa_copy_blocks: negative num_pairs");
+  if (num_pairs == 0) return pa_ok();
+  if (!k_pool || !v_pool || !pairs) return pa_fail(PA_ERR_INVALID, "pa_copy_blocks: null pointer");
+  pa::CopyBlocksArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_bytes = static_cast<int64_t>(pool->num_kv_heads) * pool->block_size * pool->head_dim *
+                  elem_bytes(pool->dtype);
+  a.pairs = pairs;
+  a.num_pairs = num_pairs;
+  return launch_status(pa::launch_copy_blocks(a, stream), "pa_copy_blocks");
+}
+
+pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t max_context_len, int32_t partition_size, size_t* bytes) {
+  if (!bytes) return pa_fail(PA_ERR_INVALID, "pa_decode_workspace_size: bytes is null");
+  *bytes = 0;
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size < 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_workspace_size: negative or zero size");
+  if (partition_size != 0 && partition_size % 32 != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_workspace_size: partition_size must be a multiple of 32");
+  const int32_t part = partition_size ? partition_size : kDefaultPartition;
+  const int64_t mp = decode_max_parts(max_context_len, part);
+  if (mp <= 1) return pa_ok();
+  const size_t n = static_cast<size_t>(num_seqs) * num_q_heads * mp;
+  *bytes = 2 * align256(n * sizeof(float)) + align256(n * head_dim * sizeof(float));
+  return pa_ok();
+}
+
+pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
+                    const pa_pool_desc* pool, const int32_t* tables, int32_t max_blocks,
+                    const int32_t* lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                    int32_t partition_size, int32_t max_context_len, void* workspace,
+                    size_t workspace_bytes, void* out, int32_t out_dtype, pa_stream stream) {
+  pa_status st = check_pool(pool, "pa_decode");
+  if (st != PA_OK) return st;
+  if (num_seqs < 0) return pa_fail(PA_ERR_INVALID, "pa_decode: negative num_seqs");
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode: num_q_heads must be a positive multiple of num_kv_heads");
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: group size must be 1, 2, 4 or 8");
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return pa_fail(PA_ERR_INVALID, "pa_decode: bad q_dtype");
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return pa_fail(PA_ERR_INVALID, "pa_decode: bad out_dtype");
+  if ((pool->dtype == PA_F32) != (q_dtype == PA_F32))
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: an f32 pool needs f32 q; bf16/fp8 pools need bf16 q");
+  if (!std::isfinite(scale)) return pa_fail(PA_ERR_INVALID, "pa_decode: scale is not finite");
+  if (max_context_len < 0) return pa_fail(PA_ERR_INVALID, "pa_decode: negative max_context_len");
+  if (partition_size < 0 || (partition_size != 0 && partition_size % 32 != 0))
+    return pa_fail(PA_ERR_INVALID, "pa_decode: partition_size must be 0 or a positive multiple of 32");
+  const int64_t need_blocks = (static_cast<int64_t>(max_context_len) + pool->block_size - 1) / pool->block_size;
+  if (max_blocks < need_blocks)
+    return pa_fail(PA_ERR_INVALID, "pa_decode: max_blocks_per_seq < ceil(max_context_len / block_size)");
+  if (num_seqs > kMaxGridYZ || pool->num_kv_heads > kMaxGridYZ)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 65535 sequences or KV heads in one call");
+  if (num_seqs == 0) return pa_ok();
+  if (!q || !k_pool || !v_pool || !tables || !lens || !out)
+    return pa_fail(PA_ERR_INVALID, "pa_decode: null pointer");
+  const int32_t part = partition_size ? partition_size : kDefaultPartition;
+  const int64_t mp = decode_max_parts(max_context_len, part);
+  if (mp > (int64_t(1) << 30)) return pa_fail(PA_ERR_INVALID, "pa_decode: too many partitions");
+  size_t need = 0;
+  st = pa_decode_workspace_size(num_seqs, num_q_heads, pool->head_dim, max_context_len, part, &need);
+  if (st != PA_OK) return st;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return pa_fail(PA_ERR_INVALID, "pa_decode: workspace missing or smaller than pa_decode_workspace_size");
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.tables = tables;
+  a.max_blocks = max_blocks;
+  a.lens = lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  const float kscale = pool->dtype == PA_FP8_E4M3 ? pool->k_scale : 1.0f;
+  a.qk_scale = static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
+  a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+  a.part_tokens = part;
+  a.max_parts = static_cast<int32_t>(mp);
+  a.max_ctx = max_context_len;
+  if (mp > 1) {
+    const size_t n = static_cast<size_t>(num_seqs) * num_q_heads * mp;
+    char* w = static_cast<char*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(w);
+    a.ws_l = reinterpret_cast<float*>(w + align256(n * sizeof(float)));
+    a.ws_o = reinterpret_cast<float*>(w + 2 * align256(n * sizeof(float)));
+  }
+  a.out = out;
+  return launch_status(pa::launch_decode(a, pool->dtype, q_dtype, out_dtype, pool->block_size,
+                                         pool->head_dim, stream),
+                       "pa_decode: no kernel for this dtype / head_dim / block_size combination");
+}
+
+pa_status pa_prefill_chunk(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
+                           const pa_pool_desc* pool, const int32_t* tables, int32_t max_blocks,
+                           const int32_t* qsl, const int32_t* prior, int32_t num_seqs,
+                           int32_t num_q_heads, float scale, int32_t max_chunk_len, void* out,
+                           int32_t out_dtype, pa_stream stream) {
+  pa_status st = check_pool(pool, "pa_prefill_chunk");
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_chunk_len < 0) return pa_fail(PA_ERR_INVALID, "pa_prefill_chunk: negative size");
+  if (q_dtype != PA_BF16) return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: q must be PA_BF16");
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16)
+    return pa_fail(PA_ERR_INVALID, "pa_prefill_chunk: bad out_dtype");
+  if (pool->dtype == PA_F32 || pool->head_dim != 128)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: needs a bf16 or fp8 pool with head_dim 128");
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_prefill_chunk: num_q_heads must be a positive multiple of num_kv_heads");
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: group size must be 1, 2, 4 or 8");
+  if (!std::isfinite(scale)) return pa_fail(PA_ERR_INVALID, "pa_prefill_chunk: scale is not finite");
+  if (num_seqs > kMaxGridYZ || pool->num_kv_heads > kMaxGridYZ)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: more than 65535 sequences or KV heads");
+  if (num_seqs == 0 || max_chunk_len == 0) return pa_ok();
+  if (!q || !k_pool || !v_pool || !tables || !qsl || !prior || !out)
+    return pa_fail(PA_ERR_INVALID, "pa_prefill_chunk: null pointer");
+  if (max_blocks <= 0) return pa_fail(PA_ERR_INVALID, "pa_prefill_chunk: max_blocks_per_seq must be positive");
+  pa::PrefillArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.tables = tables;
+  a.max_blocks = max_blocks;
+  a.qsl = qsl;
+  a.prior = prior;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  const float kscale = pool->dtype == PA_FP8_E4M3 ? pool->k_scale : 1.0f;
+  a.qk_scale = static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
+  a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+  a.max_chunk = max_chunk_len;
+  a.out = out;
+  return launch_status(pa::launch_prefill(a, pool->dtype, out_dtype, pool->block_size, pool->head_dim, stream),
+                       "pa_prefill_chunk: no kernel for this combination");
+}
+
+pa_status pa_fp8_decode_table(float* out, pa_stream stream) {
+  if (!out) return pa_fail(PA_ERR_INVALID, "pa_fp8_decode_table: out is null");
+  return launch_status(pa::launch_fp8_table(out, stream), "pa_fp8_decode_table");
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal declarations shared by the C-ABI layer and the kernel launchers of libpa.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pa.h"
+
+// Records `msg` as this thread's last error and returns `st`.
+pa_status pa_fail(pa_status st, const char* msg);
+// Clears this thread's last error and returns PA_OK.
+pa_status pa_ok();
+
+namespace pa {
+
+// Dtype codes used as template arguments of the kernels.
+enum Dt : int { kF32 = PA_F32, kBF16 = PA_BF16, kFP8 = PA_FP8_E4M3 };
+
+struct CacheWriteArgs {
+  const void* k;
+  const void* v;
+  int in_dtype;
+  int64_t num_tokens;
+  const int64_t* slots;
+  void* k_pool;
+  void* v_pool;
+  int block_size;
+  int num_kv_heads;
+  int head_dim;
+  int pool_dtype;
+  float k_inv_scale;  // fp32(1 / k_scale), rounded once on the host
+  float v_inv_scale;
+};
+
+struct CopyBlocksArgs {
+  void* k_pool;
+  void* v_pool;
+  int64_t block_bytes;  // bytes of one block of one pool (all KV heads)
+  const int32_t* pairs;
+  int32_t num_pairs;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tables;
+  int32_t max_blocks;
+  const int32_t* lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  float qk_scale;        // scale * k_scale * log2(e): logits in base-2 units
+  float v_scale;
+  int32_t part_tokens;   // tokens per partition
+  int32_t max_parts;     // partitions of the longest sequence
+  int32_t max_ctx;       // bound on every context length (lengths are clamped to it on the device)
+  float* ws_m;           // [num_seqs][num_q_heads][max_parts]
+  float* ws_l;
+  float* ws_o;           // [num_seqs][num_q_heads][max_parts][head_dim]
+  void* out;
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tables;
+  int32_t max_blocks;
+  const int32_t* qsl;
+  const int32_t* prior;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  float qk_scale;        // scale * k_scale * log2(e)
+  float v_scale;
+  int32_t max_chunk;
+  void* out;
+};
+
+// Launchers return a hipError_t value as int (0 = success).
+int launch_cache_write(const CacheWriteArgs& a, void* stream);
+int launch_copy_blocks(const CopyBlocksArgs& a, void* stream);
+// Returns 0 on success, -1 when no kernel exists for the combination, else a hipError_t.
+int launch_decode(const DecodeArgs& a, int kv_dtype, int q_dtype, int out_dtype, int block_size,
+                  int head_dim, void* stream);
+int launch_prefill(const PrefillArgs& a, int kv_dtype, int out_dtype, int block_size, int head_dim,
+                   void* stream);
+int launch_fp8_table(float* out, void* stream);
+
+}  // namespace pa

@@ -1,0 +1,184 @@
+"""A paged-KV step driver: replays a workload's sequence operations on the host allocator and runs
+the device calls of one step (copy-on-write copies, cache write, chunked prefill, decode).
+
+Host side: pa_alloc_* (C++), which hands out slots and copy pairs.  Device side: the HIP kernels of
+libpa, called through the binding with torch-owned memory on one stream.
+"""
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3
+from .allocator import BlockAllocator
+from .ops import (make_pool_desc, pa_cache_write, pa_copy_blocks, pa_decode, pa_decode_workspace_size,
+                  pa_prefill_chunk)
+
+_PA = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
+_CODE_TORCH = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8}
+_VIEW = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+
+def _signed(code: int, bits: int) -> int:
+    return code - (1 << bits) if code >= (1 << (bits - 1)) else code
+
+
+@dataclass
+class StepInputs:
+    """Device-resident inputs of one step (everything the timed region needs)."""
+    cow_pairs: torch.Tensor                 # int32 [n, 2]
+    slots: torch.Tensor                     # int64 [step tokens]
+    k_new: torch.Tensor                     # [step tokens, Hkv, D]
+    v_new: torch.Tensor
+    dec_tables: Optional[torch.Tensor] = None
+    dec_lens: Optional[torch.Tensor] = None
+    dec_q: Optional[torch.Tensor] = None
+    dec_out: Optional[torch.Tensor] = None
+    dec_max_len: int = 0
+    dec_workspace: Optional[torch.Tensor] = None
+    dec_partition: int = 0
+    pre_tables: Optional[torch.Tensor] = None
+    pre_qsl: Optional[torch.Tensor] = None
+    pre_prior: Optional[torch.Tensor] = None
+    pre_q: Optional[torch.Tensor] = None
+    pre_out: Optional[torch.Tensor] = None
+    pre_max_chunk: int = 0
+    host_slots: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+    host_cow: np.ndarray = field(default_factory=lambda: np.zeros((0, 2), np.int32))
+
+
+class PagedKVEngine:
+    """Owns the two pools of one layer and the host allocator of a workload (package `synth`)."""
+
+    def __init__(self, wl, device: str = "cuda", poison: Optional[int] = None):
+        self.wl = wl
+        self.device = torch.device(device)
+        self.pool = make_pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
+                                   _PA[wl.kv_dtype], wl.k_scale, wl.v_scale)
+        shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+        bits = {"f32": 32, "bf16": 16, "fp8": 8}[wl.kv_dtype]
+        fill = 0 if poison is None else (_signed(poison, bits) if wl.kv_dtype != "fp8" else poison)
+        self.k_pool = torch.full(shape, fill, dtype=_CODE_TORCH[wl.kv_dtype], device=self.device).view(_VIEW[wl.kv_dtype])
+        self.v_pool = torch.full(shape, fill, dtype=_CODE_TORCH[wl.kv_dtype], device=self.device).view(_VIEW[wl.kv_dtype])
+        self.alloc = BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
+        self.k_tok = wl.k_tok.to(self.device)
+        self.v_tok = wl.v_tok.to(self.device)
+        self.history_slots = np.zeros(0, np.int64)
+
+    # -- host replay --------------------------------------------------------------------------
+    def _replay(self, ops: Sequence[Tuple], on_cow=None, slots_out=None) -> List[Tuple[int, int]]:
+        cows: List[Tuple[int, int]] = []
+        for op in ops:
+            kind = op[0]
+            if kind == "add":
+                self.alloc.add_seq(op[1])
+            elif kind == "fork":
+                self.alloc.fork(op[1], op[2])
+            elif kind == "free":
+                self.alloc.free_seq(op[1])
+            elif kind == "append":
+                _, sid, n, tok0 = op
+                slots, cow = self.alloc.append(sid, n)
+                if len(cow) and on_cow is not None:
+                    on_cow(cow)
+                cows.extend((int(a), int(b)) for a, b in cow)
+                if slots_out is not None:
+                    slots_out[tok0:tok0 + n] = slots
+            else:
+                raise ValueError(kind)
+        return cows
+
+    def build_history(self) -> None:
+        """Replay the history and write every history token into its slot."""
+        wl = self.wl
+        h0, h1 = wl.history_token_range()
+        slots = np.full(max(h1, 1), -1, dtype=np.int64)
+        written = [h0]
+
+        def flush_then_copy(cow):
+            # tokens appended so far must land before a copy reads their block
+            end = int(np.max(np.nonzero(slots >= 0)[0])) + 1 if (slots >= 0).any() else h0
+            self._write_rows(written[0], end, slots)
+            written[0] = end
+            pa_copy_blocks(self.k_pool, self.v_pool, self.pool,
+                           torch.as_tensor(np.asarray(cow, np.int32), device=self.device))
+
+        self._replay(wl.history, on_cow=flush_then_copy, slots_out=slots)
+        self._write_rows(written[0], h1, slots)
+        self.history_slots = slots[h0:h1].copy()
+
+    def _write_rows(self, a: int, b: int, slots: np.ndarray) -> None:
+        if b <= a:
+            return
+        sl = torch.as_tensor(slots[a:b], device=self.device)
+        pa_cache_write(self.k_tok[a:b], self.v_tok[a:b], sl, self.k_pool, self.v_pool, self.pool)
+
+    def prepare_step(self, partition_size: Optional[int] = None) -> StepInputs:
+        """Replay the step's allocator ops and stage every device input of the step."""
+        wl = self.wl
+        s0, s1 = wl.step_token_range()
+        slots = np.full(max(s1, 1), -1, dtype=np.int64)
+        cows = self._replay(wl.step, slots_out=slots)
+        step_slots = slots[s0:s1].copy()
+        dev = self.device
+        cow = np.asarray(cows, np.int32).reshape(-1, 2)
+        si = StepInputs(cow_pairs=torch.as_tensor(cow, device=dev),
+                        slots=torch.as_tensor(step_slots, device=dev),
+                        k_new=self.k_tok[s0:s1], v_new=self.v_tok[s0:s1],
+                        host_slots=step_slots, host_cow=cow)
+        part = wl.partition_size if partition_size is None else partition_size
+        if wl.decode_seqs:
+            lens = np.asarray(wl.decode_lens, np.int32)
+            max_len = int(lens.max())
+            tabs = [len(self.alloc.table(s)) for s in wl.decode_seqs]
+            mb = max(max(tabs), -(-max_len // wl.block_size), 1)
+            si.dec_tables = torch.as_tensor(self.alloc.fill_tables(wl.decode_seqs, mb), device=dev)
+            si.dec_lens = torch.as_tensor(lens, device=dev)
+            si.dec_q = wl.q_decode.to(dev)
+            si.dec_out = torch.empty_like(si.dec_q)
+            si.dec_max_len = max_len
+            ws = pa_decode_workspace_size(len(wl.decode_seqs), wl.num_q_heads, wl.head_dim, max_len, part)
+            si.dec_workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+            si.dec_partition = part
+        if wl.prefill_seqs:
+            prior = np.asarray(wl.prefill_prior, np.int32)
+            chunk = np.asarray(wl.prefill_chunk, np.int32)
+            tabs = [len(self.alloc.table(s)) for s in wl.prefill_seqs]
+            mb = max(max(tabs), 1)
+            si.pre_tables = torch.as_tensor(self.alloc.fill_tables(wl.prefill_seqs, mb), device=dev)
+            si.pre_qsl = torch.as_tensor(np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32), device=dev)
+            si.pre_prior = torch.as_tensor(prior, device=dev)
+            si.pre_q = wl.q_prefill.to(dev)
+            si.pre_out = torch.empty_like(si.pre_q)
+            si.pre_max_chunk = int(chunk.max())
+        return si
+
+    # -- device step --------------------------------------------------------------------------
+    def copy_step(self, si: StepInputs, stream=None) -> None:
+        pa_copy_blocks(self.k_pool, self.v_pool, self.pool, si.cow_pairs, stream)
+
+    def write_step(self, si: StepInputs, stream=None) -> None:
+        pa_cache_write(si.k_new, si.v_new, si.slots, self.k_pool, self.v_pool, self.pool, stream)
+
+    def decode_step(self, si: StepInputs, stream=None, out: Optional[torch.Tensor] = None) -> None:
+        if si.dec_q is None:
+            return
+        pa_decode(si.dec_q, self.k_pool, self.v_pool, self.pool, si.dec_tables, si.dec_lens, self.wl.scale,
+                  si.dec_out if out is None else out, si.dec_max_len, si.dec_partition, si.dec_workspace, stream)
+
+    def prefill_step(self, si: StepInputs, stream=None) -> None:
+        if si.pre_q is None:
+            return
+        pa_prefill_chunk(si.pre_q, self.k_pool, self.v_pool, self.pool, si.pre_tables, si.pre_qsl, si.pre_prior,
+                         self.wl.scale, si.pre_max_chunk, si.pre_out, stream)
+
+    def run_step(self, si: StepInputs, stream=None) -> None:
+        """One step: CoW copies, then the new tokens' cache write, then prefill and decode."""
+        self.copy_step(si, stream)
+        self.write_step(si, stream)
+        self.prefill_step(si, stream)
+        self.decode_step(si, stream)
+
+    def finish(self) -> None:
+        self._replay(self.wl.post)

@@ -1,0 +1,121 @@
+"""Python binding of libpa's device calls, with the names of the C ABI (include/pa.h).
+
+Argument marshalling only: torch tensors supply device memory and the current stream; every
+computation runs in the library's HIP kernels.  There is no fallback: without libpa.so, or without
+a GPU, these calls raise.
+"""
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3, PoolDesc, check, lib
+
+_TORCH_TO_PA = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
+                torch.float8_e4m3fn: PA_FP8_E4M3}
+
+
+def pa_dtype(t: torch.Tensor) -> int:
+    try:
+        return _TORCH_TO_PA[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def make_pool_desc(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: int,
+                   k_scale: float = 1.0, v_scale: float = 1.0) -> PoolDesc:
+    return PoolDesc(num_blocks, block_size, num_kv_heads, head_dim, dtype, k_scale, v_scale)
+
+
+def pool_torch_dtype(dtype: int) -> torch.dtype:
+    return {PA_F32: torch.float32, PA_BF16: torch.bfloat16, PA_FP8_E4M3: torch.uint8}[dtype]
+
+
+def pa_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_pool: torch.Tensor,
+                   v_pool: torch.Tensor, pool: PoolDesc, stream=None) -> None:
+    """Scatter rows k, v [T, Hkv, D] into their slots (int64 [T]; negative = skip)."""
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    n = int(slot_mapping.shape[0])
+    if k.shape != v.shape or (n and k.shape[0] != n):
+        raise ValueError("k, v and slot_mapping disagree in length")
+    if n == 0:
+        return
+    check(lib().pa_cache_write(_dev(k, "k"), _dev(v, "v"), pa_dtype(k), n, _dev(slot_mapping, "slot_mapping"),
+                               _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ctypes.byref(pool),
+                               _stream(stream)))
+
+
+def pa_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc, pairs: torch.Tensor,
+                   stream=None) -> None:
+    """Copy whole blocks src -> dst for each row of pairs (int32 [n, 2])."""
+    if pairs.dtype != torch.int32:
+        raise TypeError("pairs must be int32")
+    n = int(pairs.shape[0]) if pairs.numel() else 0
+    if n == 0:
+        return
+    check(lib().pa_copy_blocks(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ctypes.byref(pool),
+                               _dev(pairs, "pairs"), n, _stream(stream)))
+
+
+def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
+                             partition_size: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    check(lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size,
+                                         ctypes.byref(out)))
+    return int(out.value)
+
+
+def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc,
+              block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, out: torch.Tensor,
+              max_context_len: int, partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> None:
+    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over each sequence's paged context."""
+    num_seqs, num_q_heads, head_dim = q.shape
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    need = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib().pa_decode(_dev(q, "q"), pa_dtype(q), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                          ctypes.byref(pool), _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
+                          _dev(context_lens, "context_lens"), num_seqs, num_q_heads, float(scale),
+                          partition_size, int(max_context_len), ws_ptr, ws_bytes, _dev(out, "out"),
+                          pa_dtype(out), _stream(stream)))
+
+
+def pa_prefill_chunk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc,
+                     block_tables: torch.Tensor, query_start_loc: torch.Tensor,
+                     prior_context_lens: torch.Tensor, scale: float, max_chunk_len: int, out: torch.Tensor,
+                     stream=None) -> None:
+    """Causal attention of each sequence's chunk of queries over its paged context plus the chunk."""
+    num_seqs = int(prior_context_lens.shape[0])
+    check(lib().pa_prefill_chunk(_dev(q, "q"), pa_dtype(q), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                 ctypes.byref(pool), _dev(block_tables, "block_tables"),
+                                 int(block_tables.shape[1]), _dev(query_start_loc, "query_start_loc"),
+                                 _dev(prior_context_lens, "prior_context_lens"), num_seqs, int(q.shape[1]),
+                                 float(scale), int(max_chunk_len), _dev(out, "out"), pa_dtype(out),
+                                 _stream(stream)))
+
+
+def pa_fp8_decode_table(out: torch.Tensor, stream=None) -> None:
+    """out (float32 [256], device) <- the device's decoding of every e4m3 code."""
+    check(lib().pa_fp8_decode_table(_dev(out, "out"), _stream(stream)))
