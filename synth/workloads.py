@@ -282,7 +282,6 @@ def _shared_prefix_bf16(name, size, rng, gen, device, block_size):
 
 def _mixed_fp8(name, size, rng, gen, device, block_size):
     b = block_size or 16
-    hq, hkv, d = 32, 8, 128
     if size == "full":
         n_pre, n_dec = 16, 192
         prior = rng.integers(0, 4096, size=n_pre, endpoint=True)
@@ -294,11 +293,18 @@ def _mixed_fp8(name, size, rng, gen, device, block_size):
         prior[0] = 0
         chunk = rng.integers(33, 100, size=n_pre, endpoint=True)
         dlens = rng.integers(16, 400, size=n_dec, endpoint=True)
-    prior = [int(x) for x in prior]
-    chunk = [int(x) for x in chunk]
-    dlens = [int(x) for x in dlens]
+    return mixed_workload(name, size, rng, gen, device, hq=32, hkv=8, d=128, b=b, kv="fp8",
+                          prior=[int(x) for x in prior], chunk=[int(x) for x in chunk],
+                          dlens=[int(x) for x in dlens],
+                          notes="chunked prefill co-scheduled with decode over an fp8 e4m3 pool")
+
+
+def mixed_workload(name, size, rng, gen, device, *, hq, hkv, d, b, kv, prior, chunk, dlens, notes=""):
+    """Prefill sequences (prior context, then a chunk of new queries) plus decode sequences.
+    kv "fp8": per-tensor scales map the largest |K| (|V|) of all drawn rows to 448."""
+    n_pre, n_dec = len(prior), len(dlens)
     needed = sum(_ceil_div(p + c, b) for p, c in zip(prior, chunk)) + sum(_ceil_div(L + 1, b) for L in dlens)
-    nb = _pool_blocks(needed)
+    nb = _pool_blocks(max(needed, 1))
     free_order = rng.permutation(nb).astype(np.int32)
     pre_ids = list(range(n_pre))
     dec_ids = list(range(n_pre, n_pre + n_dec))
@@ -318,19 +324,21 @@ def _mixed_fp8(name, size, rng, gen, device, block_size):
     t = sc.next_tok
     n_q = sum(chunk)
     q_pre = _q(gen, device, n_q, hq, d, "bf16")
-    q_dec = _q(gen, device, n_dec, hq, d, "bf16")
+    q_dec = _q(gen, device, n_dec, hq, d, "bf16") if n_dec else None
     k, v = _draw_tokens(gen, device, t, hkv, d, "bf16")
     k = k.to(torch.bfloat16)
     v = v.to(torch.bfloat16)
-    # Per-tensor fp32 scales: the largest |K| (|V|) of the step maps to e4m3's largest finite value.
-    k_scale = _fp32(float(k.abs().max().float().item()) / 448.0)
-    v_scale = _fp32(float(v.abs().max().float().item()) / 448.0)
+    if kv == "fp8":
+        # Per-tensor fp32 scales: the largest |K| (|V|) of the step maps to e4m3's largest finite value.
+        k_scale = _fp32(float(k.abs().max().float().item()) / 448.0)
+        v_scale = _fp32(float(v.abs().max().float().item()) / 448.0)
+    else:
+        k_scale = v_scale = 1.0
     return Workload(
         name=name, size=size, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=b,
-        kv_dtype="fp8", act_dtype="bf16", num_blocks=nb, free_order=free_order,
+        kv_dtype=kv, act_dtype="bf16", num_blocks=nb, free_order=free_order,
         scale=_fp32(1.0 / math.sqrt(d)), k_scale=k_scale, v_scale=v_scale,
         history=history, step=step, post=[], k_tok=k, v_tok=v,
         decode_seqs=dec_ids, decode_lens=np.asarray(dlens, np.int32), q_decode=q_dec,
         prefill_seqs=pre_ids, prefill_prior=np.asarray(prior, np.int32),
-        prefill_chunk=np.asarray(chunk, np.int32), q_prefill=q_pre,
-        notes="chunked prefill co-scheduled with decode over an fp8 e4m3 pool")
+        prefill_chunk=np.asarray(chunk, np.int32), q_prefill=q_pre, notes=notes)

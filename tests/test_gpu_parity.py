@@ -28,19 +28,10 @@ def _say(*a):
 
 
 def _run(wl, partition=None):
-    from paged_kv_cache_427_amd import PaError
-    from paged_kv_cache_427_amd._lib import PA_ERR_UNSUPPORTED
     eng = _engine()(wl, poison=poison_code(wl.kv_dtype))
     eng.build_history()
     si = eng.prepare_step(partition)
-    eng.copy_step(si)
-    eng.write_step(si)
-    try:
-        eng.prefill_step(si)
-    except PaError as e:          # prefill kernel not built into this library yet
-        assert e.status == PA_ERR_UNSUPPORTED
-        si.pre_out = None
-    eng.decode_step(si)
+    eng.run_step(si)
     torch.cuda.synchronize()
     return eng, si
 
@@ -81,7 +72,7 @@ def test_small_workload_parity(name):
         err = _out_err(si.dec_out, ref.decode_out)
         _say(name, "decode max err", err)
         assert err <= tol
-    if wl.prefill_seqs and si.pre_out is not None:
+    if wl.prefill_seqs:
         err = _out_err(si.pre_out, ref.prefill_out)
         _say(name, "prefill max err", err)
         assert err <= tol
@@ -184,6 +175,26 @@ def test_group_of_eight_and_head_dim_64():
         assert _out_err(si.dec_out, ref.decode_out) <= TOL["bf16"], (hq, hkv, d)
 
 
+@pytest.mark.parametrize("kv,hq,hkv,b", [("bf16", 8, 8, 16), ("bf16", 16, 4, 32), ("fp8", 16, 2, 8),
+                                          ("bf16", 8, 1, 16)])
+def test_prefill_variants(kv, hq, hkv, b):
+    """Prefill over bf16 and fp8 pools, groups of 1/4/8, ragged chunks (1 query, a partial tile,
+    several tiles), empty prior context and a prior that ends mid-block."""
+    from synth.workloads import mixed_workload
+    rng = np.random.Generator(np.random.PCG64(7))
+    gen = torch.Generator().manual_seed(7)
+    wl = mixed_workload("mixed_fp8", "small", rng, gen, "cpu", hq=hq, hkv=hkv, d=128, b=b, kv=kv,
+                        prior=[0, 37, 5, 130], chunk=[1, 45, 150, 64], dlens=[9])
+    _say("prefill variant", kv, hq, hkv, b)
+    ref = run_paged(wl)
+    eng, si = _run(wl)
+    assert np.array_equal(tensor_bits(eng.k_pool), ref.k_pool)
+    err = _out_err(si.pre_out, ref.prefill_out)
+    _say("prefill variant max err", err)
+    assert err <= TOL[kv]
+    assert _out_err(si.dec_out, ref.decode_out) <= TOL[kv]
+
+
 # ---- full-size workloads: sampled outputs against the pool-free dense oracle ---------------------
 
 FULL = ["llama7b_bf16", "shared_prefix_bf16", "gqa_long_bf16", "mixed_fp8"]
@@ -198,9 +209,7 @@ def test_full_size_sampled(name):
     si = eng.prepare_step()
     if len(si.host_cow):
         k_before = eng.k_pool[torch.as_tensor(si.host_cow[:4, 0].astype(np.int64), device="cuda")].clone()
-    eng.copy_step(si)
-    eng.write_step(si)
-    eng.decode_step(si)
+    eng.run_step(si)
     torch.cuda.synchronize()
     lg = logical_view(wl)
     rng = np.random.default_rng(5)
@@ -239,7 +248,7 @@ def test_full_size_sampled(name):
         if wl.kv_dtype == "fp8":
             row = e4m3_quantise(act_values(row, wl.act_dtype).astype(np.float32), wl.k_scale)
         assert np.array_equal(got, row)
-    if wl.prefill_seqs and si.pre_out is not None:
+    if wl.prefill_seqs:
         worst = 0.0
         starts = np.concatenate([[0], np.cumsum(wl.prefill_chunk)])
         for si_ in rng.choice(len(wl.prefill_seqs), 3, replace=False):
