@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="after timing, run one device copy of this many GiB (a known-size kernel that "
+                         "calibrates hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -180,6 +183,15 @@ def main():
     res["kernel_ms"] = {"copy_blocks": round(ms_copy, 4), "cache_write": round(ms_write, 4),
                         "prefill": round(ms_prefill, 4), "decode": round(ms_decode, 4)}
     res["config"] = cfg
+    if args.copy_probe_gib > 0:
+        n = int(args.copy_probe_gib * 2**30) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = {"read": n * 4, "write": n * 4}
+        del src, dst
     if not args.no_cpu_baseline and wl.decode_seqs:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
