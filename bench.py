@@ -29,6 +29,26 @@ from synth import make_workload, poison_code, elem_bytes  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_427_amd", "csrc", "decode.hip")
+
+
+def measured_traffic(config: str, block_size):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary of this workload, or
+    None when there is none or the decode source changed since the counters were taken."""
+    import hashlib
+    import re
+    if block_size not in (None, 16):
+        return None
+    path = os.path.join(ROOT, "profiles", f"decode_{config}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_t = re.search(r"decode_traffic_bytes_per_launch: (\d+)", text)
+    m_h = re.search(r"decode_source_sha256_16: ([0-9a-f]+)", text)
+    if not (m_t and m_h):
+        return None
+    cur = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+    return int(m_t.group(1)) if cur == m_h.group(1) else None
 
 
 def decode_bytes(wl, tables: np.ndarray):
@@ -169,7 +189,8 @@ def main():
         res["decode_tokens_per_s_per_layer"] = round(len(wl.decode_lens) / (ms_step * 1e-3), 1)
         achieved = (uniq + other) / (ms_decode * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                           "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic(args.config, args.block_size),
                            "kernel": "pa_decode (partition kernel + merge kernel)",
                            "algorithmic_bytes_per_launch": int(uniq + other)}
         res["decode_logical_kv_GBps"] = round(logical / (ms_decode * 1e-3) / 1e9, 1)
