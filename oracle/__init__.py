@@ -21,7 +21,7 @@ from .codecs import (  # noqa: F401
 )
 from .allocator import RefAllocator, AllocError, OutOfBlocks  # noqa: F401
 from .logical import LogicalSeqs  # noqa: F401
-from .cache import slot_of, ref_cache_write, ref_copy_blocks, gather_seq  # noqa: F401
+from .cache import slot_of, pool_shape, ref_cache_write, ref_copy_blocks, gather_seq  # noqa: F401
 from .attention import (  # noqa: F401
     attend, ref_decode, ref_decode_split, partition_stats, merge_partitions, ref_prefill,
 )

@@ -1,9 +1,13 @@
 """The physical KV pool: slot addressing, writing new tokens, block copies, gathering a sequence.
 
 Pool layout (a reading; the pages fix only that a block holds the K/V of b consecutive tokens and
-is contiguous inside, [day28] §三 3.1-3.2): K and V are two separate arrays, each
-[num_blocks][num_kv_heads][block_size][head_dim] of stored codes (uint32 fp32 bits, uint16 bf16
-bits or uint8 e4m3 codes).
+is contiguous inside, [day28] §三 3.1-3.2): K and V are two separate arrays of stored codes
+(uint32 fp32 bits, uint16 bf16 bits or uint8 e4m3 codes).  Both are split into (block, KV head)
+tiles of b x head_dim codes, contiguous; the K tile is token-major and the V tile dim-major:
+  K pool: [num_blocks][num_kv_heads][block_size][head_dim]   (which="k")
+  V pool: [num_blocks][num_kv_heads][head_dim][block_size]   (which="v")
+so element (token offset o, dim d) of a tile sits at o * head_dim + d in K and d * block_size + o
+in V.
 
 Slot of logical position p of a sequence with table T: T[p // b] * b + p % b, as in the
 block-table figure of [day28] §三 3.1 (table [7, 1, 3]: logical block 0 -> physical 7 holds
@@ -21,18 +25,31 @@ def slot_of(table: Sequence[int], p: int, block_size: int) -> int:
     return int(table[p // block_size]) * block_size + p % block_size
 
 
+def pool_shape(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, which: str):
+    """Array shape of a K (which="k") or V (which="v") pool."""
+    if which == "k":
+        return (num_blocks, num_kv_heads, block_size, head_dim)
+    if which == "v":
+        return (num_blocks, num_kv_heads, head_dim, block_size)
+    raise ValueError(which)
+
+
+def _block_size(pool: np.ndarray, which: str) -> int:
+    return pool.shape[2] if which == "k" else pool.shape[3]
+
+
 def ref_cache_write(pool: np.ndarray, x_bits: np.ndarray, slots: Sequence[int], kv_dtype: str,
-                    act_dtype: str, scale: float = 1.0) -> None:
+                    act_dtype: str, scale: float = 1.0, which: str = "k") -> None:
     """Write token rows into their slots, in place.
 
-    pool   : [num_blocks, Hkv, b, D] stored codes
+    pool   : stored codes, laid out as pool_shape(..., which)
     x_bits : [T, Hkv, D] bit patterns of the new rows in the activation dtype
              (uint32 for fp32, uint16 for bf16)
     slots  : [T] int; a negative slot means "skip this token"
     For an fp8 pool each value is quantised with `scale` (codecs.e4m3_quantise); otherwise the
     bit pattern is stored unchanged (pool dtype == activation dtype).
     """
-    b = pool.shape[2]
+    b = _block_size(pool, which)
     for t, s in enumerate(slots):
         s = int(s)
         if s < 0:
@@ -43,10 +60,14 @@ def ref_cache_write(pool: np.ndarray, x_bits: np.ndarray, slots: Sequence[int], 
                 vals = bf16_bits_to_f64(x_bits[t]).astype(np.float32)
             else:
                 vals = f32_bits_to_f64(x_bits[t]).astype(np.float32)
-            pool[blk, :, off, :] = e4m3_quantise(vals, scale)
+            codes = e4m3_quantise(vals, scale)
         else:
             assert kv_dtype == act_dtype, "a non-fp8 pool stores the activation dtype"
-            pool[blk, :, off, :] = x_bits[t]
+            codes = x_bits[t]
+        if which == "k":
+            pool[blk, :, off, :] = codes
+        else:
+            pool[blk, :, :, off] = codes
 
 
 def ref_copy_blocks(pool: np.ndarray, pairs: Sequence) -> None:
@@ -56,12 +77,14 @@ def ref_copy_blocks(pool: np.ndarray, pairs: Sequence) -> None:
         pool[int(dst)] = pool[int(src)].copy()
 
 
-def gather_seq(pool_vals: np.ndarray, table: Sequence[int], length: int) -> np.ndarray:
-    """Contiguous [length, Hkv, D] K (or V) of a sequence, rebuilt through its block table
-    ([day28] §三 3.1: the kernel reaches scattered K/V by indirection through the table)."""
-    b = pool_vals.shape[2]
-    hkv, d = pool_vals.shape[1], pool_vals.shape[3]
+def gather_seq(pool_vals: np.ndarray, table: Sequence[int], length: int, which: str = "k") -> np.ndarray:
+    """Contiguous [length, Hkv, D] K (which="k") or V (which="v") of a sequence, rebuilt through its
+    block table ([day28] §三 3.1: the kernel reaches scattered K/V by indirection through the table)."""
+    b = _block_size(pool_vals, which)
+    hkv = pool_vals.shape[1]
+    d = pool_vals.shape[3] if which == "k" else pool_vals.shape[2]
     out = np.empty((length, hkv, d), dtype=np.float64)
     for p in range(length):
-        out[p] = pool_vals[int(table[p // b]), :, p % b, :]
+        blk, off = int(table[p // b]), p % b
+        out[p] = pool_vals[blk, :, off, :] if which == "k" else pool_vals[blk, :, :, off]
     return out

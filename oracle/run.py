@@ -17,7 +17,7 @@ from synth import poison_code
 
 from .allocator import RefAllocator
 from .attention import attend, ref_decode, ref_decode_split, ref_prefill
-from .cache import gather_seq, ref_cache_write, ref_copy_blocks
+from .cache import gather_seq, pool_shape, ref_cache_write, ref_copy_blocks
 from .codecs import bf16_bits_to_f64, decode_pool, e4m3_decode, e4m3_quantise, f32_bits_to_f64
 from .logical import LogicalSeqs
 
@@ -82,8 +82,8 @@ def run_paged(wl, split: Optional[int] = None) -> OracleResult:
     b, hkv, d = wl.block_size, wl.num_kv_heads, wl.head_dim
     code_dt = _CODE_DTYPE[wl.kv_dtype]
     poison = poison_code(wl.kv_dtype)   # input recipe: the initial content of every pool slot
-    k_pool = np.full((wl.num_blocks, hkv, b, d), poison, dtype=code_dt)
-    v_pool = np.full((wl.num_blocks, hkv, b, d), poison, dtype=code_dt)
+    k_pool = np.full(pool_shape(wl.num_blocks, hkv, b, d, "k"), poison, dtype=code_dt)
+    v_pool = np.full(pool_shape(wl.num_blocks, hkv, b, d, "v"), poison, dtype=code_dt)
     k_bits = tensor_bits(wl.k_tok)
     v_bits = tensor_bits(wl.v_tok)
     alloc = RefAllocator(wl.num_blocks, b, wl.free_order)
@@ -100,7 +100,7 @@ def run_paged(wl, split: Optional[int] = None) -> OracleResult:
             rows = list(range(op[3], op[3] + op[2]))
             sl = [h_slots[r] for r in rows]
             ref_cache_write(k_pool, k_bits[rows], sl, wl.kv_dtype, wl.act_dtype, wl.k_scale)
-            ref_cache_write(v_pool, v_bits[rows], sl, wl.kv_dtype, wl.act_dtype, wl.v_scale)
+            ref_cache_write(v_pool, v_bits[rows], sl, wl.kv_dtype, wl.act_dtype, wl.v_scale, which="v")
     h0, h1 = wl.history_token_range()
     history_slots = np.array([h_slots[r] for r in range(h0, h1)], dtype=np.int64)
 
@@ -114,7 +114,7 @@ def run_paged(wl, split: Optional[int] = None) -> OracleResult:
     s0, s1 = wl.step_token_range()
     step_slots = np.array([s_slots[r] for r in range(s0, s1)], dtype=np.int64)
     ref_cache_write(k_pool, k_bits[s0:s1], step_slots, wl.kv_dtype, wl.act_dtype, wl.k_scale)
-    ref_cache_write(v_pool, v_bits[s0:s1], step_slots, wl.kv_dtype, wl.act_dtype, wl.v_scale)
+    ref_cache_write(v_pool, v_bits[s0:s1], step_slots, wl.kv_dtype, wl.act_dtype, wl.v_scale, which="v")
 
     res = OracleResult(k_pool=k_pool, v_pool=v_pool, history_slots=history_slots, step_slots=step_slots,
                        step_cow=np.array(s_cow, dtype=np.int32).reshape(-1, 2),
@@ -126,7 +126,7 @@ def run_paged(wl, split: Optional[int] = None) -> OracleResult:
 
     if wl.decode_seqs:
         q = act_values(tensor_bits(wl.q_decode), wl.act_dtype)
-        kv = [(gather_seq(kv_k, alloc.table(sid), int(L)), gather_seq(kv_v, alloc.table(sid), int(L)))
+        kv = [(gather_seq(kv_k, alloc.table(sid), int(L)), gather_seq(kv_v, alloc.table(sid), int(L), "v"))
               for sid, L in zip(wl.decode_seqs, wl.decode_lens)]
         res.decode_out = ref_decode(q, kv, wl.scale)
         if split:
@@ -137,7 +137,7 @@ def run_paged(wl, split: Optional[int] = None) -> OracleResult:
         kv = []
         for sid, p, c in zip(wl.prefill_seqs, wl.prefill_prior, wl.prefill_chunk):
             n = int(p) + int(c)
-            kv.append((gather_seq(kv_k, alloc.table(sid), n), gather_seq(kv_v, alloc.table(sid), n)))
+            kv.append((gather_seq(kv_k, alloc.table(sid), n), gather_seq(kv_v, alloc.table(sid), n, "v")))
         res.prefill_out = ref_prefill(q, qsl, wl.prefill_prior, kv, wl.scale)
 
     for op in wl.post:
