@@ -12,7 +12,6 @@
 namespace {
 
 thread_local char g_err[512];
-constexpr int kDefaultPartition = 512;
 constexpr int kMaxGridYZ = 65535;
 
 pa_status hip_fail(int e, const char* where) {
@@ -59,6 +58,12 @@ pa_status check_pool(const pa_pool_desc* p, const char* who) {
 }
 
 int elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : 1; }
+
+// Tokens per decode partition: the caller's size, or (0) one partition spanning every sequence.
+int32_t decode_partition(int32_t max_ctx, int32_t partition_size) {
+  if (partition_size > 0) return partition_size;
+  return max_ctx > 0 ? (max_ctx + 15) / 16 * 16 : 16;
+}
 
 int64_t decode_max_parts(int32_t max_ctx, int32_t part) {
   if (max_ctx <= 0) return 1;
@@ -108,7 +113,7 @@ pa_status pa_cache_write(const void* k, const void* v, int32_t in_dtype, int64_t
     return pa_fail(PA_ERR_INVALID, "pa_cache_write: an f32/bf16 pool must have the dtype of k and v");
   if (num_tokens == 0) return pa_ok();
   if (!k || !v || !slots || !k_pool || !v_pool) return pa_fail(PA_ERR_INVALID, "pa_cache_write: null pointer");
-  if (num_tokens * pool->num_kv_heads * (pool->head_dim / 4) > (int64_t(1) << 40))
+  if (num_tokens * pool->num_kv_heads * (pool->head_dim / 4) > (int64_t(1) << 31))
     return pa_fail(PA_ERR_INVALID, "pa_cache_write: too many tokens for one launch");
   pa::CacheWriteArgs a{};
   a.k = k;
@@ -152,11 +157,9 @@ pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_
     return pa_fail(PA_ERR_INVALID, "pa_decode_workspace_size: negative or zero size");
   if (partition_size != 0 && partition_size % 32 != 0)
     return pa_fail(PA_ERR_INVALID, "pa_decode_workspace_size: partition_size must be a multiple of 32");
-  const int32_t part = partition_size ? partition_size : kDefaultPartition;
+  const int32_t part = decode_partition(max_context_len, partition_size);
   const int64_t mp = decode_max_parts(max_context_len, part);
-  if (mp <= 1) return pa_ok();
-  const size_t n = static_cast<size_t>(num_seqs) * num_q_heads * mp;
-  *bytes = 2 * align256(n * sizeof(float)) + align256(n * head_dim * sizeof(float));
+  *bytes = pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, mp, pa::decode_max_waves());
   return pa_ok();
 }
 
@@ -189,13 +192,17 @@ pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const vo
   if (num_seqs == 0) return pa_ok();
   if (!q || !k_pool || !v_pool || !tables || !lens || !out)
     return pa_fail(PA_ERR_INVALID, "pa_decode: null pointer");
-  const int32_t part = partition_size ? partition_size : kDefaultPartition;
+  // stream positions (KV heads x 16-key units of all sequences) must fit in 31 bits
+  if (static_cast<int64_t>(pool->num_kv_heads) * num_seqs * ((static_cast<int64_t>(max_context_len) + 15) / 16) >=
+      (int64_t(1) << 31))
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 2^31 16-key units of K/V in one call");
+  const int32_t part = decode_partition(max_context_len, partition_size);
   const int64_t mp = decode_max_parts(max_context_len, part);
   if (mp > (int64_t(1) << 30)) return pa_fail(PA_ERR_INVALID, "pa_decode: too many partitions");
   size_t need = 0;
-  st = pa_decode_workspace_size(num_seqs, num_q_heads, pool->head_dim, max_context_len, part, &need);
+  st = pa_decode_workspace_size(num_seqs, num_q_heads, pool->head_dim, max_context_len, partition_size, &need);
   if (st != PA_OK) return st;
-  if (need > 0 && (!workspace || workspace_bytes < need))
+  if (!workspace || workspace_bytes < need)
     return pa_fail(PA_ERR_INVALID, "pa_decode: workspace missing or smaller than pa_decode_workspace_size");
   pa::DecodeArgs a{};
   a.q = q;
@@ -213,13 +220,9 @@ pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const vo
   a.part_tokens = part;
   a.max_parts = static_cast<int32_t>(mp);
   a.max_ctx = max_context_len;
-  if (mp > 1) {
-    const size_t n = static_cast<size_t>(num_seqs) * num_q_heads * mp;
-    char* w = static_cast<char*>(workspace);
-    a.ws_m = reinterpret_cast<float*>(w);
-    a.ws_l = reinterpret_cast<float*>(w + align256(n * sizeof(float)));
-    a.ws_o = reinterpret_cast<float*>(w + 2 * align256(n * sizeof(float)));
-  }
+  char* w = static_cast<char*>(workspace);
+  a.ws_pref = reinterpret_cast<int32_t*>(w);
+  a.ws_part = reinterpret_cast<float*>(w + align256((static_cast<size_t>(num_seqs) + 1) * 4));
   a.out = out;
   return launch_status(pa::launch_decode(a, pool->dtype, q_dtype, out_dtype, pool->block_size,
                                          pool->head_dim, stream),

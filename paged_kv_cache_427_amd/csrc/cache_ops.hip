@@ -5,8 +5,10 @@
 // preceded by a copy of the block.  The slot of a token is table[p / b] * b + p % b (§三 3.1 figure);
 // the allocator computes it on the host, these kernels only follow it.
 //
-// Both kernels are HBM-bound streams of 16-byte vector loads and stores; the pool layout
-// [block][kv_head][row][dim] makes one (token, head) row R = head_dim * elem bytes contiguous.
+// All kernels here are HBM-bound streams.  In the K pool (tiles [row][dim]) a token's row for one head
+// is head_dim contiguous elements, written with 16-byte stores; in the V pool (tiles [dim][row]) a
+// token's values stride by block_size elements, and consecutive lanes take consecutive tokens so
+// that the tokens of one block land side by side in each dim row.
 #include <hip/hip_runtime.h>
 
 #include "pa_device.h"
@@ -17,10 +19,34 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One thread per 16-byte chunk of one stored (token, KV head) row, for K and for V.
+// Input elements -> stored codes of one pool element: the bits themselves for an fp32/bf16 pool,
+// one rounded fp32 product with the host-rounded reciprocal scale and then the e4m3 rounding for fp8.
+template <int IN>
+__device__ __forceinline__ void load_in8(const char* src, float (&x)[8]) {
+  if constexpr (IN == kBF16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(src);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_lo(ws[j]);
+      x[2 * j + 1] = bf16_hi(ws[j]);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 w = reinterpret_cast<const uint4*>(src)[h];
+      x[4 * h] = __uint_as_float(w.x);
+      x[4 * h + 1] = __uint_as_float(w.y);
+      x[4 * h + 2] = __uint_as_float(w.z);
+      x[4 * h + 3] = __uint_as_float(w.w);
+    }
+  }
+}
+
+// K pool (token-major tiles): one thread per 16-byte chunk of one stored (token, KV head) row.
 template <int IN, int POOL>
-__global__ void __launch_bounds__(kThreads) cache_write_kernel(CacheWriteArgs a, int log2_bs,
-                                                               int chunks_per_row) {
+__global__ void __launch_bounds__(kThreads) cache_write_k_kernel(CacheWriteArgs a, int log2_bs,
+                                                                 int chunks_per_row) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t total = a.num_tokens * a.num_kv_heads * chunks_per_row;
   if (idx >= total) return;
@@ -37,49 +63,84 @@ __global__ void __launch_bounds__(kThreads) cache_write_kernel(CacheWriteArgs a,
   constexpr int kElems = 16 / kOutElem;                 // elements per stored chunk
   const int64_t row_bytes = static_cast<int64_t>(a.head_dim) * kOutElem;
   const int64_t dst_off = ((blk * a.num_kv_heads + head) * (1 << log2_bs) + off) * row_bytes + c * 16;
-  const int64_t src_elem = row * a.head_dim + static_cast<int64_t>(c) * kElems;
+  const char* src = static_cast<const char*>(a.k) + (row * a.head_dim + static_cast<int64_t>(c) * kElems) * kInElem;
+  char* dst = static_cast<char*>(a.k_pool) + dst_off;
   if constexpr (POOL == IN) {
-    const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const char*>(a.k) + src_elem * kInElem);
-    const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) + src_elem * kInElem);
-    *reinterpret_cast<uint4*>(static_cast<char*>(a.k_pool) + dst_off) = *ks;
-    *reinterpret_cast<uint4*>(static_cast<char*>(a.v_pool) + dst_off) = *vs;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   } else {
     static_assert(POOL == kFP8, "only fp8 pools convert");
-    constexpr int kIn16 = kElems * kInElem / 16;         // 16-byte input loads per output chunk
+    uint32_t packed[4];
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const char* src = static_cast<const char*>(which ? a.v : a.k) + src_elem * kInElem;
-      const float inv = which ? a.v_inv_scale : a.k_inv_scale;
-      float x[kElems];
+    for (int h = 0; h < 2; ++h) {
+      float x[8];
+      load_in8<IN>(src + h * 8 * kInElem, x);
 #pragma unroll
-      for (int i = 0; i < kIn16; ++i) {
-        const uint4 w = reinterpret_cast<const uint4*>(src)[i];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (IN == kBF16) {
-            x[i * 8 + 2 * j] = bf16_lo(ws[j]);
-            x[i * 8 + 2 * j + 1] = bf16_hi(ws[j]);
-          } else {
-            x[i * 4 + j] = __uint_as_float(ws[j]);
-          }
-        }
-      }
-      uint32_t packed[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         uint32_t p = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // one rounded fp32 product, then the e4m3 rounding
-          const float y = __fmul_rn(x[4 * i + j], inv);
-          p |= f32_to_e4m3(y) << (8 * j);
-        }
-        packed[i] = p;
+        for (int j = 0; j < 4; ++j) p |= f32_to_e4m3(__fmul_rn(x[4 * i + j], a.k_inv_scale)) << (8 * j);
+        packed[2 * h + i] = p;
       }
-      *reinterpret_cast<uint4*>(static_cast<char*>(which ? a.v_pool : a.k_pool) + dst_off) =
-          make_uint4(packed[0], packed[1], packed[2], packed[3]);
     }
+    *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  }
+}
+
+// V pool (dim-major tiles: element (row o, dim d) of a tile at d * block_size + o).  One thread per
+// (token, KV head, group of 8 dims); the 64 lanes of a wave take 64 consecutive tokens of the same
+// head and dims, so tokens that fill one block store to adjacent addresses of each dim row.
+template <int IN, int POOL>
+__global__ void __launch_bounds__(kThreads) cache_write_v_kernel(CacheWriteArgs a, int log2_bs) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int groups = a.head_dim / 8;
+  const int64_t t_blocks = (a.num_tokens + 63) / 64;
+  if (idx >= t_blocks * 64 * a.num_kv_heads * groups) return;
+  const int lane = static_cast<int>(idx & 63);
+  int64_t rest = idx >> 6;
+  const int dg = static_cast<int>(rest % groups);
+  rest /= groups;
+  const int head = static_cast<int>(rest % a.num_kv_heads);
+  const int64_t t = (rest / a.num_kv_heads) * 64 + lane;
+  if (t >= a.num_tokens) return;
+  const int64_t slot = a.slots[t];
+  if (slot < 0) return;
+  const int bs = 1 << log2_bs;
+  const int64_t blk = slot >> log2_bs;
+  const int off = static_cast<int>(slot & (bs - 1));
+  constexpr int kOutElem = POOL == kF32 ? 4 : POOL == kBF16 ? 2 : 1;
+  constexpr int kInElem = IN == kF32 ? 4 : 2;
+  const char* src = static_cast<const char*>(a.v) +
+                    ((t * a.num_kv_heads + head) * a.head_dim + 8 * dg) * static_cast<int64_t>(kInElem);
+  // element (off, d) of tile (blk, head)
+  char* tile = static_cast<char*>(a.v_pool) +
+               (blk * a.num_kv_heads + head) * static_cast<int64_t>(bs) * a.head_dim * kOutElem;
+  char* dst = tile + (static_cast<int64_t>(8 * dg) * bs + off) * kOutElem;
+  const int64_t dstep = static_cast<int64_t>(bs) * kOutElem;
+  if constexpr (POOL == IN) {
+    if constexpr (IN == kBF16) {
+      const uint4 w = *reinterpret_cast<const uint4*>(src);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<uint16_t*>(dst + (2 * j) * dstep) = static_cast<uint16_t>(ws[j] & 0xffffu);
+        *reinterpret_cast<uint16_t*>(dst + (2 * j + 1) * dstep) = static_cast<uint16_t>(ws[j] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 w = reinterpret_cast<const uint4*>(src)[h];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(dst + (4 * h + j) * dstep) = ws[j];
+      }
+    }
+  } else {
+    static_assert(POOL == kFP8, "only fp8 pools convert");
+    float x[8];
+    load_in8<IN>(src, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint8_t*>(dst + j * dstep) = static_cast<uint8_t>(f32_to_e4m3(__fmul_rn(x[j], a.v_inv_scale)));
   }
 }
 
@@ -115,18 +176,25 @@ int ilog2(int x) {
 int launch_cache_write(const CacheWriteArgs& a, void* stream) {
   const int out_elem = a.pool_dtype == kF32 ? 4 : a.pool_dtype == kBF16 ? 2 : 1;
   const int chunks = a.head_dim * out_elem / 16;
-  const int64_t total = a.num_tokens * a.num_kv_heads * chunks;
-  const dim3 grid(static_cast<unsigned>((total + kThreads - 1) / kThreads));
+  const int64_t total_k = a.num_tokens * a.num_kv_heads * chunks;
+  const int64_t total_v = (a.num_tokens + 63) / 64 * 64 * a.num_kv_heads * (a.head_dim / 8);
+  const dim3 gk(static_cast<unsigned>((total_k + kThreads - 1) / kThreads));
+  const dim3 gv(static_cast<unsigned>((total_v + kThreads - 1) / kThreads));
   const int lb = ilog2(a.block_size);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.pool_dtype == kF32)
-    hipLaunchKernelGGL((cache_write_kernel<kF32, kF32>), grid, dim3(kThreads), 0, s, a, lb, chunks);
-  else if (a.pool_dtype == kBF16)
-    hipLaunchKernelGGL((cache_write_kernel<kBF16, kBF16>), grid, dim3(kThreads), 0, s, a, lb, chunks);
-  else if (a.in_dtype == kBF16)
-    hipLaunchKernelGGL((cache_write_kernel<kBF16, kFP8>), grid, dim3(kThreads), 0, s, a, lb, chunks);
-  else
-    hipLaunchKernelGGL((cache_write_kernel<kF32, kFP8>), grid, dim3(kThreads), 0, s, a, lb, chunks);
+  if (a.pool_dtype == kF32) {
+    hipLaunchKernelGGL((cache_write_k_kernel<kF32, kF32>), gk, dim3(kThreads), 0, s, a, lb, chunks);
+    hipLaunchKernelGGL((cache_write_v_kernel<kF32, kF32>), gv, dim3(kThreads), 0, s, a, lb);
+  } else if (a.pool_dtype == kBF16) {
+    hipLaunchKernelGGL((cache_write_k_kernel<kBF16, kBF16>), gk, dim3(kThreads), 0, s, a, lb, chunks);
+    hipLaunchKernelGGL((cache_write_v_kernel<kBF16, kBF16>), gv, dim3(kThreads), 0, s, a, lb);
+  } else if (a.in_dtype == kBF16) {
+    hipLaunchKernelGGL((cache_write_k_kernel<kBF16, kFP8>), gk, dim3(kThreads), 0, s, a, lb, chunks);
+    hipLaunchKernelGGL((cache_write_v_kernel<kBF16, kFP8>), gv, dim3(kThreads), 0, s, a, lb);
+  } else {
+    hipLaunchKernelGGL((cache_write_k_kernel<kF32, kFP8>), gk, dim3(kThreads), 0, s, a, lb, chunks);
+    hipLaunchKernelGGL((cache_write_v_kernel<kF32, kFP8>), gv, dim3(kThreads), 0, s, a, lb);
+  }
   return static_cast<int>(hipGetLastError());
 }
 

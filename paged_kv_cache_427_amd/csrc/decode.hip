@@ -5,23 +5,32 @@
 // coalesced reads inside it -- and dots the query with every cached key; §七 notes the indirection
 // costs a little.  softmax(scale * q K^T) V is the textbook form of what the pages describe in words.
 //
-// Design (HBM-bound: at most 8 flop per byte of K/V, far below the MI355X ridge):
-//  * one workgroup of 4 wave64s owns one context partition of one KV head and serves all G query
-//    heads of that group, so each K/V byte is read once.  Workgroups are numbered so that all work
-//    of one KV head lands on one XCD (dispatch is round-robin over the 8 XCDs): blocks shared by
-//    many sequences (a common prefix) are then re-read from that XCD's L2, not from HBM.
-//  * waves take the partition's blocks round-robin; the table entry is a wave-uniform scalar load.
-//  * a block tile (block_size rows x head_dim) is read with 16-byte loads in which every group of NL
-//    lanes covers 16*NL contiguous bytes of one token row (whole 128-byte lines); the next block's
-//    K/V is in flight while the current one is consumed (two register stages, unrolled by two).
-//  * bf16 and fp8 pools: q.k and p.v run on packed bf16 dot products (v_dot2_f32_bf16, fp32
-//    accumulation); fp8 codes widen exactly to bf16.  The probabilities fed to p.v are rounded to
-//    bf16, and the running sum uses the same rounded values, as MFMA attention kernels do.
-//    fp32 pools keep exact fp32 FMAs.
-//  * logits are reduced over the NL lanes of a row with DPP; every lane keeps its own running max,
-//    exp-sum and output partial (base-2 online softmax) for the tokens it saw.  The running max is
-//    raised only when a logit exceeds it by more than 2^8 (so exp stays <= 256), which makes the
-//    rescale of the accumulators rare.  Lanes, then waves (through LDS), merge once per partition.
+// Design (HBM-bound: at most 8 flop per byte of K/V, far below the MI355X ridge, so the goal is to
+// keep the vector ALUs out of the way of the loads):
+//  * a work item is one context partition of one KV head, for all G query heads of that group, so
+//    each K/V byte is read once; a persistent grid of workgroups (4 wave64s each, as many as are
+//    resident at once) loops over the items.  Items are numbered so that all work of one KV head
+//    lands on one XCD (initial dispatch is round-robin over the 8 XCDs): blocks shared by many
+//    sequences (a common prefix) are then re-read from that XCD's L2, not from HBM.
+//  * a wave takes 16-key units of the partition round-robin; the unit's table entry is a
+//    wave-uniform scalar load.  Both products of a unit run on 16x16 MFMA tiles fed straight from
+//    the loads, with no LDS staging:
+//      S^T[key][head] = K[key][:] . Q[head][:]     A = K rows (token-major tile), B = Q^T
+//      O^T[dim][head] += V^T[dim][key] P^T[key][head]   A = V^T rows (dim-major tile), B = P^T
+//    The G query heads occupy columns 0..G-1 of the 16 (the rest are zero).  The S^T accumulator
+//    layout -- lane l holds keys 4*(l/16)+r of the unit for head l%16 -- is, after rounding to bf16,
+//    exactly the B operand of the 16x16x16 P.V product, so the scores never cross lanes.
+//  * bf16 pools use v_mfma_f32_16x16x32_bf16 (S) and v_mfma_f32_16x16x16_bf16 (P.V); fp8 codes
+//    widen exactly to bf16 first (v_cvt_scalef32_pk_bf16_fp8, scales kept in fp32); fp32 pools use
+//    v_mfma_f32_16x16x4_f32.  The
+//    probabilities are rounded to bf16 for the bf16/fp8 products and the running sum uses the same
+//    rounded values; the fp32 path keeps fp32 probabilities.
+//  * base-2 online softmax with one running max per head.  The max is raised only when a logit
+//    exceeds it by more than 2^8 (so every exp stays <= 256); that test is one wave-wide ballot, and
+//    only then are the lanes' maxima exchanged and the accumulators rescaled.  Each lane keeps a
+//    partial exp-sum of its own keys; lanes, then waves (through LDS), merge once per partition.
+//  * a ring of register stages keeps the next units' K/V in flight while one is consumed (2 for
+//    bf16, 4 for fp8), within a register budget that leaves 3 workgroups per CU.
 //  * a sequence with several partitions writes (max, sum, normalised partial) per partition and a
 //    second kernel merges them; a single-partition sequence writes its output directly.
 #include <hip/hip_runtime.h>
@@ -35,65 +44,48 @@
 namespace pa {
 namespace {
 
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr float kSlack = 8.0f;   // log2 of the growth allowed before the accumulators are rescaled
+constexpr int kUnit = 16;          // keys per unit of one wave (one 16x16 S^T tile)
+constexpr float kSlack = 8.0f;     // log2 of the growth allowed before the accumulators are rescaled
 
 template <int KV>
-struct KvChunk;
-
-template <>
-struct KvChunk<kF32> {
-  static constexpr int kElem = 4, kN = 4;
-  __device__ static void cvt(const uint4& c, float* f) {
-    f[0] = __uint_as_float(c.x);
-    f[1] = __uint_as_float(c.y);
-    f[2] = __uint_as_float(c.z);
-    f[3] = __uint_as_float(c.w);
-  }
+struct Elem {
+  static constexpr int kBytes = KV == kF32 ? 4 : KV == kBF16 ? 2 : 1;
 };
 
-template <>
-struct KvChunk<kBF16> {
-  static constexpr int kElem = 2, kN = 8;
-  __device__ static void cvt(const uint4& c, float* f) {
-    f[0] = bf16_lo(c.x); f[1] = bf16_hi(c.x);
-    f[2] = bf16_lo(c.y); f[3] = bf16_hi(c.y);
-    f[4] = bf16_lo(c.z); f[5] = bf16_hi(c.z);
-    f[6] = bf16_lo(c.w); f[7] = bf16_hi(c.w);
-  }
-  // packed bf16 pairs: pair i = elements (2i, 2i+1)
-  __device__ static void pairs(const uint4& c, uint32_t* p) {
-    p[0] = c.x; p[1] = c.y; p[2] = c.z; p[3] = c.w;
-  }
+// Workgroups per CU that the register budget of a kernel allows.
+template <int KV, int D>
+struct Pipe {
+  static constexpr int kOcc = KV == kF32 ? 2 : 3;
 };
 
-template <>
-struct KvChunk<kFP8> {
-  static constexpr int kElem = 1, kN = 16;
-  __device__ static void cvt(const uint4& c, float* f) {
-    fp8x2_to_f32<false>(c.x, f[0], f[1]);  fp8x2_to_f32<true>(c.x, f[2], f[3]);
-    fp8x2_to_f32<false>(c.y, f[4], f[5]);  fp8x2_to_f32<true>(c.y, f[6], f[7]);
-    fp8x2_to_f32<false>(c.z, f[8], f[9]);  fp8x2_to_f32<true>(c.z, f[10], f[11]);
-    fp8x2_to_f32<false>(c.w, f[12], f[13]); fp8x2_to_f32<true>(c.w, f[14], f[15]);
-  }
-  __device__ static void pairs(const uint4& c, uint32_t* p) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
-      p[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
-    }
-  }
-};
-
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+// S^T products: 16 keys x 32 dims (bf16) or 16 keys x 4 dims (fp32) per MFMA.
+__device__ __forceinline__ f32x4 mma_s(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_s(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// P.V product of one 16-dim tile over the unit's 16 keys (bf16 operands, 4 keys per lane group).
+__device__ __forceinline__ f32x4 mma_pv(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, make_uint2(a0, a1)),
+                                                   __builtin_bit_cast(s16x4, make_uint2(b0, b1)), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// Codes in bytes 0,1 (HI = false) or 2,3 (HI = true) of w -> two bf16 in one dword (exact).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
+}
 
 __device__ __forceinline__ void store_out(void* out, int64_t i, float x, bool bf16) {
   if (bf16)
@@ -102,449 +94,569 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float x, bool bf
     static_cast<float*>(out)[i] = x;
 }
 
-// Lane geometry of one (block, KV head) tile.
-template <int KV, int D, int BS>
-struct Geo {
-  static constexpr int kE = KvChunk<KV>::kElem;
-  static constexpr int kRow = D * kE;                 // bytes of one token row
-  static constexpr int kC = kRow / 16;                // 16-byte chunks per row
-  static constexpr int kNL = kC < 8 ? kC : 8;         // lanes sharing one row in a load
-  static constexpr int kTPI = 64 / kNL;               // rows per wave load
-  static constexpr int kTG = BS / kTPI;               // row groups per block
-  static constexpr int kCPL = kC / kNL;               // chunks per lane per row
-  static constexpr int kEPC = KvChunk<KV>::kN;        // elements per chunk
-  static constexpr int kDL = kCPL * kEPC;             // dims per lane
-  static constexpr bool kOk = (BS % kTPI == 0) && kTG >= 1 && (kC % kNL == 0);
+// Raw registers of one 16-key unit, as loaded by one lane (i = lane % 16, kg = lane / 16).
+//  k[c]: key i of the unit, 16 bytes at byte 64c + 16kg of its row
+//        (bf16: dims 32c+8kg..+8; fp8: dims 64c+16kg..+16; fp32: dims 16c+4kg..+4)
+//  v[t]: dim 16t + i, keys 4kg .. 4kg+3 of the unit (VW dwords)
+template <int KV, int D>
+struct UnitRegs {
+  static constexpr int E = Elem<KV>::kBytes;
+  static constexpr int KL = D * E / 64;   // 16-byte K loads per unit
+  static constexpr int VW = E;            // dwords per 4-key V piece
+  uint4 k[KL];
+  uint32_t v[D / 16][VW];
 };
 
-// Partner value across lanes `MASK` apart (lane ^ MASK).
-template <int MASK>
-__device__ __forceinline__ float xor_lane(float x) {
-  if constexpr (MASK == 8) {
-    return dpp<0x128>(x);               // row_ror:8 -- lane i <- lane i+8 within each 16
+template <int VW>
+__device__ __forceinline__ void load_piece(uint32_t (&dst)[VW], const char* p) {
+  if constexpr (VW == 1) {
+    dst[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (VW == 2) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    dst[0] = w.x; dst[1] = w.y;
   } else {
-    return shfl_xor(x, MASK);
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
   }
 }
 
-// Per-lane running state and one block's worth of work.
-template <int KV, int D, int BS, int G>
-struct DecodeLane {
-  using Gm = Geo<KV, D, BS>;
-  static constexpr int NL = Gm::kNL, TPI = Gm::kTPI, TG = Gm::kTG, CPL = Gm::kCPL, EPC = Gm::kEPC,
-                       DL = Gm::kDL, ROW = Gm::kRow;
-  static constexpr bool kPacked = KV != kF32;
-  static constexpr int PPC = EPC / 2;                 // bf16 pairs per chunk (packed path)
+// One (sequence, KV head) segment as the loads see it.
+struct SeqView {
+  const char* kbase;       // K pool + this KV head's tile offset
+  const char* vbase;
+  const int32_t* tab;      // this sequence's block table
+  int64_t blk_stride;      // bytes of one block of one pool (all KV heads)
+  int nblk;                // valid table entries: ceil(L / BS)
+};
 
-  float qf[G][kPacked ? 1 : DL];                      // fp32 path: q * scale
-  uint32_t qp[G][kPacked ? CPL * PPC : 1];            // packed path: raw bf16 pairs of q
-  float m[G], l[G], acc[G][DL];
+// Physical blocks of the unit starting at key U: one block, or two for 8-token blocks.  A block
+// past the sequence's last one (only possible in an 8-token-block unit that ends the sequence) is
+// replaced by the last one; its keys are masked afterwards.
+struct UnitBlocks {
+  int64_t b0, b1;
+};
 
-  __device__ __forceinline__ void consume(uint4 (&kc)[TG][CPL], uint4 (&vc)[TG][CPL], int row0, int t1,
-                                          int tokset, float qk_scale) {
-    // ---- logits of this lane's rows, reduced over the NL lanes that share each row ----
-    float s[G][TG];
+template <int BS>
+__device__ __forceinline__ UnitBlocks unit_blocks(const SeqView& sv, int U) {
+  const int j0 = U / BS;
+  UnitBlocks ub;
+  ub.b0 = sv.tab[j0];
+  ub.b1 = BS == 8 ? static_cast<int64_t>(sv.tab[min(j0 + 1, sv.nblk - 1)]) : ub.b0;
+  return ub;
+}
+
+// Issues the loads of the unit starting at key U (a multiple of 16) from its blocks `ub`.
+template <int KV, int D, int BS>
+__device__ __forceinline__ void load_unit(UnitRegs<KV, D>& R, const SeqView& sv, const UnitBlocks& ub, int U,
+                                          int i, int kg) {
+  using R_t = UnitRegs<KV, D>;
+  constexpr int E = R_t::E, KL = R_t::KL, VW = R_t::VW;
+  const char* krow;
+  const char* vrow;
+  if constexpr (BS == 8) {
+    // keys 0-7 of the unit in b0, 8-15 in b1
+    const int64_t pk = (i >> 3) ? ub.b1 : ub.b0;
+    const int64_t pv = (kg >> 1) ? ub.b1 : ub.b0;
+    krow = sv.kbase + pk * sv.blk_stride + (i & 7) * (D * E);
+    vrow = sv.vbase + pv * sv.blk_stride + (4 * (kg & 1)) * E;
+  } else {
+    const int off = U % BS;
+    krow = sv.kbase + ub.b0 * sv.blk_stride + (off + i) * (D * E);
+    vrow = sv.vbase + ub.b0 * sv.blk_stride + (off + 4 * kg) * E;
+  }
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg) {
+  for (int c = 0; c < KL; ++c) R.k[c] = *reinterpret_cast<const uint4*>(krow + 64 * c + 16 * kg);
 #pragma unroll
-      for (int g = 0; g < G; ++g) s[g][tg] = 0.f;
+  for (int t = 0; t < D / 16; ++t) load_piece<VW>(R.v[t], vrow + (16 * t + i) * BS * E);
+}
+
+template <int KV, int D, int G>
+struct DecodeState {
+  static constexpr int NQB = KV == kF32 ? D / 4 : D / 32;   // MFMAs per 16-key S^T tile
+  typedef typename std::conditional<KV == kF32, float, bf16x8>::type QOp;
+  QOp qb[NQB];         // Q^T operand of each S^T MFMA (zero for columns >= G)
+  f32x4 o[D / 16];     // O^T: lane holds dims 16t + 4kg + r for head lane % 16
+  float m;             // running max (base-2 logits) of head lane % 16; equal across the 4 lane groups
+  float l;             // this lane's partial exp-sum
+
+  __device__ __forceinline__ void reset() {
 #pragma unroll
-      for (int cr = 0; cr < CPL; ++cr) {
-        if constexpr (kPacked) {
-          uint32_t kp[PPC];
-          KvChunk<KV>::pairs(kc[tg][cr], kp);
+    for (int t = 0; t < D / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+  }
+
+  __device__ __forceinline__ void consume(UnitRegs<KV, D>& R, int U, int t1, int kg, int col,
+                                          float qk_scale) {
+    using R_t = UnitRegs<KV, D>;
+    constexpr int KL = R_t::KL;
+    // ---- S^T of the unit: lane holds keys 4kg + r for head col ----
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int i = 0; i < PPC; ++i) s[g][tg] = dot2(qp[g][cr * PPC + i], kp[i], s[g][tg]);
-        } else {
-          float kf[EPC];
-          KvChunk<KV>::cvt(kc[tg][cr], kf);
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) s[g][tg] = fmaf(qf[g][cr * EPC + e], kf[e], s[g][tg]);
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        s[g][tg] = group_sum<NL>(s[g][tg]);
-        if constexpr (kPacked) s[g][tg] *= qk_scale;
+    for (int c = 0; c < KL; ++c) {
+      const uint4 w = R.k[c];
+      if constexpr (KV == kBF16) {
+        s = mma_s(__builtin_bit_cast(bf16x8, w), qb[c], s);
+      } else if constexpr (KV == kFP8) {
+        s = mma_s(as_bf16x8(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
+                            fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y)),
+                  qb[2 * c], s);
+        s = mma_s(as_bf16x8(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
+                            fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w)),
+                  qb[2 * c + 1], s);
+      } else {
+        s = mma_s(__uint_as_float(w.x), qb[4 * c + 0], s);
+        s = mma_s(__uint_as_float(w.y), qb[4 * c + 1], s);
+        s = mma_s(__uint_as_float(w.z), qb[4 * c + 2], s);
+        s = mma_s(__uint_as_float(w.w), qb[4 * c + 3], s);
       }
     }
-    // ---- rows past the partition end (only in its last block): -inf logits, zero values ----
-    if (row0 + BS > t1) {
+    // ---- base-2 logits; keys at or past the partition end are masked (last unit only) ----
+    float x[4];
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) {
-        const bool ok = row0 + tg * TPI + tokset < t1;
+    for (int r = 0; r < 4; ++r) x[r] = s[r] * qk_scale;
+    if (U + kUnit > t1) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) s[g][tg] = ok ? s[g][tg] : -INFINITY;
+      for (int r = 0; r < 4; ++r)
+        if (U + 4 * kg + r >= t1) x[r] = -INFINITY;
+      // masked keys may hold any bits (even NaN): zero their values so that 0 * v stays 0
 #pragma unroll
-        for (int cr = 0; cr < CPL; ++cr)
-          if (!ok) vc[tg][cr] = make_uint4(0, 0, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        if (U + 4 * kg + e < t1) continue;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          if constexpr (KV == kF32) {
+            R.v[t][e] = 0u;
+          } else if constexpr (KV == kBF16) {
+            R.v[t][e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          } else {
+            R.v[t][0] &= ~(0xffu << (8 * e));
+          }
+        }
       }
     }
     // ---- running max: raised only when a logit exceeds it by more than the slack ----
-    bool grow = false;
-    float mx[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      mx[g] = s[g][0];
-#pragma unroll
-      for (int tg = 1; tg < TG; ++tg) mx[g] = fmaxf(mx[g], s[g][tg]);
-      grow |= mx[g] > m[g] + kSlack;
-    }
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    const bool grow = col < G && mx > m + kSlack;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));                  // max over the head's 16 keys
+      const float mn = mx > m + kSlack ? mx : m;
+      const float alpha = mn == m ? 1.f : __builtin_amdgcn_exp2f(m - mn);   // 0 when m was -inf
+      m = mn;
+      l *= alpha;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float mn = mx[g] > m[g] + kSlack ? mx[g] : m[g];
-        const float alpha = mn == m[g] ? 1.f : fast_exp2(m[g] - mn);   // 0 when m was -inf
-        m[g] = mn;
-        l[g] *= alpha;
-#pragma unroll
-        for (int i = 0; i < DL; ++i) acc[g][i] *= alpha;
-      }
+      for (int t = 0; t < D / 16; ++t) o[t] *= alpha;
     }
-    // ---- probabilities and the value accumulation ----
+    const float ms = m == -INFINITY ? 0.f : m;
+    float p[4];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float ms = m[g] == -INFINITY ? 0.f : m[g];
+    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - ms);   // 0 for masked keys
+    // ---- O^T += V^T P^T ----
+    if constexpr (KV == kF32) {
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) s[g][tg] = fast_exp2(s[g][tg] - ms);   // 0 for -inf logits
-    }
-    if constexpr (kPacked) {
-      // round p to bf16 once; the sum and the p.v products use the same rounded value
-      uint32_t pb[G][TG];
+      for (int e = 0; e < 4; ++e) l += p[e];
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int t = 0; t < D / 16; ++t)
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-          pb[g][tg] = f32_to_bf16_bits(s[g][tg]);
-          l[g] += __uint_as_float(pb[g][tg] << 16);
-        }
-#pragma unroll
-      for (int tg = 0; tg + 1 < TG; tg += 2) {
-        uint32_t pp[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) pp[g] = pb[g][tg] | (pb[g][tg + 1] << 16);
-#pragma unroll
-        for (int cr = 0; cr < CPL; ++cr) {
-          uint32_t va[PPC], vb[PPC];
-          KvChunk<KV>::pairs(vc[tg][cr], va);
-          KvChunk<KV>::pairs(vc[tg + 1][cr], vb);
-#pragma unroll
-          for (int i = 0; i < PPC; ++i) {
-            const uint32_t even = __builtin_amdgcn_perm(vb[i], va[i], 0x05040100u);  // dim 2i of both rows
-            const uint32_t odd = __builtin_amdgcn_perm(vb[i], va[i], 0x07060302u);   // dim 2i+1
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-              acc[g][cr * EPC + 2 * i] = dot2(even, pp[g], acc[g][cr * EPC + 2 * i]);
-              acc[g][cr * EPC + 2 * i + 1] = dot2(odd, pp[g], acc[g][cr * EPC + 2 * i + 1]);
-            }
-          }
-        }
-      }
-      if constexpr (TG % 2 == 1) {
-        constexpr int tg = TG - 1;
-#pragma unroll
-        for (int cr = 0; cr < CPL; ++cr) {
-          float vf[EPC];
-          KvChunk<KV>::cvt(vc[tg][cr], vf);
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float p = __uint_as_float(pb[g][tg] << 16);
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[g][cr * EPC + e] = fmaf(p, vf[e], acc[g][cr * EPC + e]);
-          }
-        }
-      }
+        for (int e = 0; e < 4; ++e) o[t] = mma_s(__uint_as_float(R.v[t][e]), p[e], o[t]);
     } else {
+      uint32_t pb[2];
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) {
+      for (int e = 0; e < 2; ++e) {
+        const __bf16 lo = static_cast<__bf16>(p[2 * e]);
+        const __bf16 hi = static_cast<__bf16>(p[2 * e + 1]);
+        l += static_cast<float>(lo) + static_cast<float>(hi);
+        pb[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+      }
 #pragma unroll
-        for (int g = 0; g < G; ++g) l[g] += s[g][tg];
-#pragma unroll
-        for (int cr = 0; cr < CPL; ++cr) {
-          float vf[EPC];
-          KvChunk<KV>::cvt(vc[tg][cr], vf);
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[g][cr * EPC + e] = fmaf(s[g][tg], vf[e], acc[g][cr * EPC + e]);
+      for (int t = 0; t < D / 16; ++t) {
+        if constexpr (KV == kBF16) {
+          o[t] = mma_pv(R.v[t][0], R.v[t][1], pb[0], pb[1], o[t]);
+        } else {
+          o[t] = mma_pv(fp8x2_to_bf16x2<false>(R.v[t][0]), fp8x2_to_bf16x2<true>(R.v[t][0]), pb[0], pb[1], o[t]);
         }
       }
     }
   }
 };
 
-template <int TG, int CPL>
-__device__ __forceinline__ void load_tile(uint4 (&kc)[TG][CPL], uint4 (&vc)[TG][CPL], const char* kb,
-                                          const char* vb, const int (&off)[TG][CPL]) {
-#pragma unroll
-  for (int tg = 0; tg < TG; ++tg)
-#pragma unroll
-    for (int cr = 0; cr < CPL; ++cr) {
-      kc[tg][cr] = *reinterpret_cast<const uint4*>(kb + off[tg][cr]);
-      vc[tg][cr] = *reinterpret_cast<const uint4*>(vb + off[tg][cr]);
-    }
-}
+// A length outside [0, max_ctx] is clamped so that table, workspace and output stay in bounds.
+__device__ __forceinline__ int clamped_len(const DecodeArgs& a, int seq) { return min(max(a.lens[seq], 0), a.max_ctx); }
 
-// Work item of workgroup `id`: (partition, KV head, sequence), partitions fastest.  With xcd_map
-// the KV head's index within its group of 8 equals id % 8, so every workgroup of one KV head runs on
-// the same XCD; each XCD walks its heads one at a time, sequence by sequence, so blocks shared by the
-// sequences of that head stay in its L2 while reads of private blocks keep HBM busy.
-__device__ __forceinline__ void decode_item(const DecodeArgs& a, int xcd_map, int& part, int& kvh, int& seq) {
-  const int id = blockIdx.x;
-  if (xcd_map) {
-    const int x = id % 8;
-    const int j = id / 8;
-    part = j % a.max_parts;
-    const int r = j / a.max_parts;
-    seq = r % a.num_seqs;
-    kvh = (r / a.num_seqs) * 8 + x;
-  } else {
-    part = id % a.max_parts;
-    const int r = id / a.max_parts;
-    kvh = r % a.num_kv_heads;
-    seq = r / a.num_kv_heads;
+// ---- work plan: units (16 keys) of every sequence, as a prefix sum --------------------------------
+constexpr int kPlanThreads = 1024;
+
+// One workgroup: pref[s] = sum over sequences s' < s of ceil(L_s' / 16).
+__global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(DecodeArgs a) {
+  __shared__ int csum[kPlanThreads];
+  const int n = a.num_seqs;
+  const int tid = threadIdx.x;
+  const int chunk = (n + kPlanThreads - 1) / kPlanThreads;
+  const int s0 = min(tid * chunk, n), s1 = min(s0 + chunk, n);
+  int local = 0;
+  for (int s = s0; s < s1; ++s) local += (clamped_len(a, s) + kUnit - 1) / kUnit;
+  csum[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off *= 2) {
+    const int v = tid >= off ? csum[tid - off] : 0;
+    __syncthreads();
+    csum[tid] += v;
+    __syncthreads();
+  }
+  int run = csum[tid] - local;
+  if (tid == 0) a.ws_pref[0] = 0;
+  for (int s = s0; s < s1; ++s) {
+    run += (clamped_len(a, s) + kUnit - 1) / kUnit;
+    a.ws_pref[s + 1] = run;
   }
 }
 
-template <int KV, int D, int BS, int G, typename QT>
-__global__ void __launch_bounds__(kThreads) decode_part_kernel(DecodeArgs a, int out_bf16, int xcd_map) {
-  using Lane = DecodeLane<KV, D, BS, G>;
-  constexpr int NL = Lane::NL, TPI = Lane::TPI, TG = Lane::TG, CPL = Lane::CPL, EPC = Lane::EPC,
-                DL = Lane::DL, ROW = Lane::ROW, PPC = Lane::PPC;
-  constexpr int TILE = BS * ROW;                      // bytes of one (block, head) tile
+// ---- stream decode -----------------------------------------------------------------------------
+// Position in a unit stream: KV head slot hh of the stream, sequence, unit j of nj in the sequence.
+struct Cursor {
+  int hh, seq, j, nj;
+};
 
-  int part, kvh, seq;
-  decode_item(a, xcd_map, part, kvh, seq);
-  // a length outside [0, max_ctx] is clamped so that table, workspace and output stay in bounds
-  const int L = min(max(a.lens[seq], 0), a.max_ctx);
-  const int n_parts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 1;
-  if (part >= n_parts) return;
+// The cursor at stream position r (the sequence holding unit r % useq of KV head slot r / useq).
+__device__ __forceinline__ Cursor locate(const int32_t* pref, int n, int useq, int r) {
+  Cursor c;
+  c.hh = r / useq;
+  const int rem = r - c.hh * useq;
+  int lo = 0, hi = n - 1;                 // largest s with pref[s] <= rem; then pref[s + 1] > rem
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pref[mid] <= rem) lo = mid; else hi = mid - 1;
+  }
+  c.seq = lo;
+  c.j = rem - pref[lo];
+  c.nj = pref[lo + 1] - pref[lo];
+  return c;
+}
 
+// Next stream position (sequences without units are skipped).  Only called while a next position exists.
+__device__ __forceinline__ void advance(Cursor& c, const int32_t* pref, int n) {
+  if (++c.j < c.nj) return;
+  c.j = 0;
+  do {
+    if (++c.seq == n) {
+      c.seq = 0;
+      ++c.hh;
+    }
+    c.nj = pref[c.seq + 1] - pref[c.seq];
+  } while (c.nj == 0);
+}
+
+template <int KV, int D, int BS>
+__device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int seq, int kvh) {
+  constexpr int TILE = BS * D * Elem<KV>::kBytes;      // bytes of one (block, head) tile
+  SeqView sv;
+  sv.kbase = static_cast<const char*>(a.k_pool) + static_cast<int64_t>(kvh) * TILE;
+  sv.vbase = static_cast<const char*>(a.v_pool) + static_cast<int64_t>(kvh) * TILE;
+  sv.tab = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+  sv.blk_stride = static_cast<int64_t>(a.num_kv_heads) * TILE;
+  sv.nblk = (clamped_len(a, seq) + BS - 1) / BS;
+  return sv;
+}
+
+// Q^T operands of (seq, KV head): column i holds query head kvh*G + i (zeros for i >= G); the k-slots
+// of lane group kg follow the dims of its K loads.
+template <int KV, int D, int G, typename QArr>
+__device__ __forceinline__ void load_q(QArr& qb, const DecodeArgs& a, int seq, int kvh, int i, int kg) {
+  using QT = typename std::conditional<KV == kF32, float, uint16_t>::type;
+  const bool live = i < G;
+  const QT* qrow = static_cast<const QT*>(a.q) +
+                   (static_cast<int64_t>(seq) * a.num_q_heads + kvh * G + (live ? i : 0)) * D;
+  if constexpr (KV == kF32) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const float4 w = live ? *reinterpret_cast<const float4*>(qrow + 16 * c + 4 * kg) : make_float4(0.f, 0.f, 0.f, 0.f);
+      qb[4 * c] = w.x; qb[4 * c + 1] = w.y; qb[4 * c + 2] = w.z; qb[4 * c + 3] = w.w;
+    }
+  } else {
+    constexpr int DPC = KV == kBF16 ? 32 : 64;          // dims covered by one K load of the 4 lane groups
+    constexpr int SUB = KV == kBF16 ? 1 : 2;            // MFMAs per K load
+#pragma unroll
+    for (int c = 0; c < D / DPC; ++c)
+#pragma unroll
+      for (int h = 0; h < SUB; ++h) {
+        const int d0 = DPC * c + (DPC / 4) * kg + 8 * h;
+        const uint4 w = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
+        qb[SUB * c + h] = __builtin_bit_cast(bf16x8, w);
+      }
+  }
+}
+
+// Streams and slots.  Stream x holds the KV heads h with h % streams == x, head slot hh = h / streams;
+// its positions are hh * useq + pref[seq] + j.  A piece is a maximal run of one wave's positions
+// inside one partition of one segment; it is written to slot
+//   (hh * num_seqs + seq) * max_parts + partition + (wave index in the stream)
+// which is unique: along a stream, later pieces have a larger (segment, partition) term and a wave
+// index at least as large.
+struct StreamGeo {
+  int x, nh, useq, wi;
+  int64_t share;
+};
+
+// Writes the piece [j0, j0 + np) of segment (c.hh, c.seq): the final output when the piece is the
+// whole segment, else its partial record.
+template <int KV, int D, int G>
+__device__ __forceinline__ void finish_piece(const DecodeArgs& a, int out_bf16, const StreamGeo& geo,
+                                             DecodeState<KV, D, G>& st, const Cursor& c, int j0, int np, int PU,
+                                             int i, int kg) {
+  float l = st.l;
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
+  const int kvh = geo.x + a.streams * c.hh;
+  if (i >= G) return;
+  if (j0 == 0 && np == c.nj) {
+    const float inv = l > 0.f ? a.v_scale / l : 0.f;
+    const int64_t base = (static_cast<int64_t>(c.seq) * a.num_q_heads + kvh * G + i) * D;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const int d = 16 * t + 4 * kg;
+      const float x0 = st.o[t][0] * inv, x1 = st.o[t][1] * inv, x2 = st.o[t][2] * inv, x3 = st.o[t][3] * inv;
+      if (out_bf16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + base + d) =
+            make_uint2(f32_to_bf16_bits(x0) | (f32_to_bf16_bits(x1) << 16), f32_to_bf16_bits(x2) | (f32_to_bf16_bits(x3) << 16));
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + base + d) = make_float4(x0, x1, x2, x3);
+      }
+    }
+  } else {
+    const int64_t slot = geo.x * a.stream_slots +
+                         (static_cast<int64_t>(c.hh) * a.num_seqs + c.seq) * a.max_parts + j0 / PU + geo.wi;
+    float* rec = a.ws_part + (slot * G + i) * (D + 4);
+    if (kg == 0) *reinterpret_cast<float4*>(rec) = make_float4(st.m, l, 0.f, 0.f);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      *reinterpret_cast<float4*>(rec + 4 + 16 * t + 4 * kg) = make_float4(st.o[t][0], st.o[t][1], st.o[t][2], st.o[t][3]);
+  }
+}
+
+// Moves the load cursor to the next stream position and issues that unit's loads into R (at the
+// wave's last position it reloads that unit, unused); entering a new segment also loads the
+// segment's Q operands into qnext.
+template <int KV, int D, int BS, int G, typename QArr>
+__device__ __forceinline__ void load_step(const DecodeArgs& a, const StreamGeo& geo, UnitRegs<KV, D>& R, Cursor& lc,
+                                          SeqView& lv, int& lpos, int last, QArr& qnext, int i, int kg) {
+  if (lpos < last) {
+    ++lpos;
+    advance(lc, a.ws_pref, a.num_seqs);
+    if (lc.j == 0) {
+      const int kvh = geo.x + a.streams * lc.hh;
+      lv = seq_view<KV, D, BS>(a, lc.seq, kvh);
+      load_q<KV, D, G>(qnext, a, lc.seq, kvh, i, kg);
+    }
+  }
+  const int U = lc.j * kUnit;
+  load_unit<KV, D, BS>(R, lv, unit_blocks<BS>(lv, U), U, i, kg);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Consumes the np units of one piece (keys from U0 on); R holds the first of them on entry and the
+// unit after the piece on exit: each consume is followed by the loads of the next stream position.
+template <int KV, int D, int BS, int G, typename QArr>
+__device__ __forceinline__ void run_piece(const DecodeArgs& a, const StreamGeo& geo, DecodeState<KV, D, G>& st,
+                                          UnitRegs<KV, D>& R, Cursor& lc, SeqView& lv, int& lpos, int last,
+                                          QArr& qnext, int U0, int L, int np, int i, int kg) {
+#pragma unroll 1
+  for (int q = 0; q < np; ++q) {
+    st.consume(R, U0 + kUnit * q, L, kg, i, a.qk_scale);
+    load_step<KV, D, BS, G>(a, geo, R, lc, lv, lpos, last, qnext, i, kg);
+  }
+}
+
+// Persistent grid of waves over the unit streams.  Every wave takes an equal contiguous share of its
+// stream (so the work is balanced to one unit) and runs one register ring across the segments of
+// its share, with the next segment's Q and table entries fetched while the current one is consumed:
+// no wave ever waits for a fresh start.  With streams == 8 the KV heads of stream x are served by
+// the workgroups on XCD x (initial dispatch is round-robin over the 8 XCDs), so blocks shared by many
+// sequences (a common prefix) are re-read from that XCD's L2, not from HBM.
+template <int KV, int D, int BS, int G>
+__global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_kernel(DecodeArgs a, int out_bf16) {
+  using St = DecodeState<KV, D, G>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tokset = lane / NL;
-  const int cl = lane % NL;
-  const int t0 = part * a.part_tokens;
-  const int t1 = min(L, t0 + a.part_tokens);
-  const int blk0 = t0 / BS;
-  const int blk1 = (t1 + BS - 1) / BS;
+  const int i = lane & 15;         // row of an MFMA operand / column (head) of an accumulator
+  const int kg = lane >> 4;        // k-group of an operand / row group of an accumulator
+  const int n = a.num_seqs;
+  const int32_t* pref = a.ws_pref;
 
-  Lane st;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const QT* qrow = static_cast<const QT*>(a.q) + (static_cast<int64_t>(seq) * a.num_q_heads + kvh * G + g) * D;
-#pragma unroll
-    for (int cr = 0; cr < CPL; ++cr) {
-      const int d0 = (cr * NL + cl) * EPC;
-      if constexpr (Lane::kPacked) {
-        const uint32_t* q32 = reinterpret_cast<const uint32_t*>(qrow + d0);
-#pragma unroll
-        for (int i = 0; i < PPC; ++i) st.qp[g][cr * PPC + i] = q32[i];
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) st.qf[g][cr * EPC + e] = static_cast<float>(qrow[d0 + e]) * a.qk_scale;
-      }
-    }
-    st.m[g] = -INFINITY;
-    st.l[g] = 0.f;
-#pragma unroll
-    for (int i = 0; i < DL; ++i) st.acc[g][i] = 0.f;
-  }
+  StreamGeo geo;
+  geo.x = blockIdx.x % a.streams;
+  geo.nh = a.num_kv_heads / a.streams;
+  geo.useq = pref[n];
+  geo.wi = (blockIdx.x / a.streams) * kWaves + wave;
+  const int total = geo.nh * geo.useq;
+  geo.share = (static_cast<int64_t>(total) + a.stream_waves - 1) / a.stream_waves;
+  const int r0 = static_cast<int>(min(static_cast<int64_t>(total), geo.wi * geo.share));
+  const int r1 = static_cast<int>(min(static_cast<int64_t>(total), (geo.wi + 1) * geo.share));
+  if (r0 >= r1) return;
+  const int PU = a.part_tokens / kUnit;
 
-  const char* kbase = static_cast<const char*>(a.k_pool) + static_cast<int64_t>(kvh) * TILE;
-  const char* vbase = static_cast<const char*>(a.v_pool) + static_cast<int64_t>(kvh) * TILE;
-  const int32_t* tab = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
-  const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * TILE;
-  int off[TG][CPL];
-#pragma unroll
-  for (int tg = 0; tg < TG; ++tg)
-#pragma unroll
-    for (int cr = 0; cr < CPL; ++cr) off[tg][cr] = (tg * TPI + tokset) * ROW + (cr * NL + cl) * 16;
+  St st;
+  typename St::QOp qnext[St::NQB];
+  Cursor cc = locate(pref, n, geo.useq, r0);            // consume cursor
+  Cursor lc = cc;                                      // load cursor
+  int lpos = r0;
+  SeqView lv = seq_view<KV, D, BS>(a, lc.seq, geo.x + a.streams * lc.hh);
+  load_q<KV, D, G>(st.qb, a, cc.seq, geo.x + a.streams * cc.hh, i, kg);
+  UnitRegs<KV, D> R;
+  load_unit<KV, D, BS>(R, lv, unit_blocks<BS>(lv, lc.j * kUnit), lc.j * kUnit, i, kg);
 
-  // two register stages, unrolled so that no stage is copied into the other
-  uint4 ka[TG][CPL], va[TG][CPL], kb2[TG][CPL], vb2[TG][CPL];
-  int b = blk0 + wave;
-  if (b < blk1) {
-    const int64_t base = tab[b] * blk_stride;
-    load_tile<TG, CPL>(ka, va, kbase + base, vbase + base, off);
-  }
-  for (; b < blk1; b += 2 * kWaves) {
-    const int b1 = b + kWaves;
-    if (b1 < blk1) {
-      const int64_t base = tab[b1] * blk_stride;
-      load_tile<TG, CPL>(kb2, vb2, kbase + base, vbase + base, off);
-    }
-    st.consume(ka, va, b * BS, t1, tokset, a.qk_scale);
-    if (b1 >= blk1) break;
-    const int b2 = b1 + kWaves;
-    if (b2 < blk1) {
-      const int64_t base = tab[b2] * blk_stride;
-      load_tile<TG, CPL>(ka, va, kbase + base, vbase + base, off);
-    }
-    st.consume(kb2, vb2, b1 * BS, t1, tokset, a.qk_scale);
-  }
-
-  // ---- merge the lanes of different row sets (same dims) inside the wave ----
+#pragma unroll 1
+  for (int p = r0; p < r1;) {
+    // the piece: the rest of this partition of this segment, within the wave's share
+    const int np = min(min(r1 - p, cc.nj - cc.j), PU - cc.j % PU);
+    const int L = clamped_len(a, cc.seq);
+    st.reset();
+    run_piece<KV, D, BS, G>(a, geo, st, R, lc, lv, lpos, r1 - 1, qnext, cc.j * kUnit, L, np, i, kg);
+    finish_piece<KV, D, G>(a, out_bf16, geo, st, cc, cc.j, np, PU, i, kg);
+    p += np;
+    if (p < r1) {
+      const bool new_seg = cc.j + np == cc.nj;
+#pragma unroll 1
+      for (int k = 0; k < np; ++k) advance(cc, pref, n);
+      if (new_seg) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    auto merge = [&](auto mask_tag) {
-      constexpr int MASK = decltype(mask_tag)::value;
-      const float mo = xor_lane<MASK>(st.m[g]);
-      const float lo = xor_lane<MASK>(st.l[g]);
-      const float mn = fmaxf(st.m[g], mo);
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      const float a1 = fast_exp2(st.m[g] - ms);
-      const float a2 = fast_exp2(mo - ms);
-      st.l[g] = st.l[g] * a1 + lo * a2;
-#pragma unroll
-      for (int i = 0; i < DL; ++i) st.acc[g][i] = st.acc[g][i] * a1 + xor_lane<MASK>(st.acc[g][i]) * a2;
-      st.m[g] = mn;
-    };
-    if constexpr (NL <= 4) merge(std::integral_constant<int, 4>());
-    if constexpr (NL <= 8) merge(std::integral_constant<int, 8>());
-    merge(std::integral_constant<int, 16>());
-    merge(std::integral_constant<int, 32>());
-  }
-
-  // ---- merge the waves through LDS ----
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-  __shared__ float sm_o[kWaves][G][D];
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      sm_m[wave][g] = st.m[g];
-      sm_l[wave][g] = st.l[g];
-    }
-  }
-  if (tokset == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int cr = 0; cr < CPL; ++cr)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) sm_o[wave][g][(cr * NL + cl) * EPC + e] = st.acc[g][cr * EPC + e];
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int g = idx / D;
-    const int d = idx % D;
-    float mm = sm_m[0][g];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][g]);
-    const float ms = mm == -INFINITY ? 0.f : mm;
-    float lsum = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(sm_m[w][g] - ms);
-      lsum += sm_l[w][g] * f;
-      o += sm_o[w][g][d] * f;
-    }
-    const float res = lsum > 0.f ? o / lsum * a.v_scale : 0.f;
-    const int h = kvh * G + g;
-    const int64_t sh = static_cast<int64_t>(seq) * a.num_q_heads + h;
-    if (n_parts == 1) {
-      store_out(a.out, sh * D + d, res, out_bf16 != 0);
-    } else {
-      const int64_t pi = sh * a.max_parts + part;
-      a.ws_o[pi * D + d] = res;
-      if (d == 0) {
-        a.ws_m[pi] = mm;
-        a.ws_l[pi] = lsum;
+        for (int c = 0; c < St::NQB; ++c) st.qb[c] = qnext[c];
       }
     }
   }
 }
 
-// Merge of partitions: out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max m).
+// Merge of the partial records of every (sequence, query head) whose segment was split into
+// pieces: out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M) * v_scale, M = max_p m_p.  Segments
+// served by one piece were written by the stream kernel; empty sequences (L = 0) get zeros here.
 template <int D>
-__global__ void __launch_bounds__(D) decode_reduce_kernel(DecodeArgs a, int out_bf16) {
+__global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_bf16) {
+  const int G = a.num_q_heads / a.num_kv_heads;
   const int h = blockIdx.x % a.num_q_heads;
   const int seq = blockIdx.x / a.num_q_heads;
-  const int L = min(max(a.lens[seq], 0), a.max_ctx);
-  const int n_parts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 1;
-  if (n_parts <= 1) return;
+  const int kvh = h / G, g = h % G;
   const int d = threadIdx.x;
-  const int64_t sh = static_cast<int64_t>(seq) * a.num_q_heads + h;
-  const float* mp = a.ws_m + sh * a.max_parts;
-  const float* lp = a.ws_l + sh * a.max_parts;
-  const float* op = a.ws_o + sh * a.max_parts * D;
+  const int32_t* pref = a.ws_pref;
+  const int n = a.num_seqs;
+  const int nj = pref[seq + 1] - pref[seq];
+  const int64_t oi = (static_cast<int64_t>(seq) * a.num_q_heads + h) * D + d;
+  if (nj == 0) {
+    store_out(a.out, oi, 0.f, out_bf16 != 0);
+    return;
+  }
+  const int x = kvh % a.streams, hh = kvh / a.streams;
+  const int useq = pref[n];
+  const int64_t total = static_cast<int64_t>(a.num_kv_heads / a.streams) * useq;
+  const int64_t share = (total + a.stream_waves - 1) / a.stream_waves;
+  const int64_t S = static_cast<int64_t>(hh) * useq + pref[seq];
+  const int PU = a.part_tokens / kUnit;
+  const int nparts = (nj + PU - 1) / PU;
+  if (nparts == 1 && S / share == (S + nj - 1) / share) return;
+  const int64_t seg = (static_cast<int64_t>(hh) * n + seq) * a.max_parts + x * a.stream_slots;
   float mm = -INFINITY;
-  for (int p = 0; p < n_parts; ++p) mm = fmaxf(mm, mp[p]);
+  for (int k = 0; k < nparts; ++k) {
+    const int64_t u0 = S + static_cast<int64_t>(k) * PU, u1 = S + min((k + 1) * PU, nj) - 1;
+    for (int64_t w = u0 / share; w <= u1 / share; ++w)
+      mm = fmaxf(mm, a.ws_part[((seg + k + w) * G + g) * (D + 4)]);
+  }
   const float ms = mm == -INFINITY ? 0.f : mm;
-  float wsum = 0.f, o = 0.f;
-  for (int p = 0; p < n_parts; ++p) {
-    const float w = lp[p] * fast_exp2(mp[p] - ms);
-    wsum += w;
-    o += w * op[static_cast<int64_t>(p) * D + d];
-  }
-  store_out(a.out, sh * D + d, wsum > 0.f ? o / wsum : 0.f, out_bf16 != 0);
-}
-
-template <int KV, int D, int BS, int G, typename QT>
-int launch_one(const DecodeArgs& a, int out_bf16, hipStream_t s) {
-  if constexpr (!Geo<KV, D, BS>::kOk) {
-    return -1;
-  } else {
-    const int64_t wgs = static_cast<int64_t>(a.max_parts) * a.num_kv_heads * a.num_seqs;
-    if (wgs > 0x7fffffff) return -1;
-    const int xcd_map = a.num_kv_heads % 8 == 0;
-    hipLaunchKernelGGL((decode_part_kernel<KV, D, BS, G, QT>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s,
-                       a, out_bf16, xcd_map);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return static_cast<int>(e);
-    if (a.max_parts > 1) {
-      const int64_t rw = static_cast<int64_t>(a.num_q_heads) * a.num_seqs;
-      hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(static_cast<unsigned>(rw)), dim3(D), 0, s, a, out_bf16);
-      e = hipGetLastError();
+  float lsum = 0.f, o = 0.f;
+  for (int k = 0; k < nparts; ++k) {
+    const int64_t u0 = S + static_cast<int64_t>(k) * PU, u1 = S + min((k + 1) * PU, nj) - 1;
+    for (int64_t w = u0 / share; w <= u1 / share; ++w) {
+      const float* rec = a.ws_part + ((seg + k + w) * G + g) * (D + 4);
+      const float f = __builtin_amdgcn_exp2f(rec[0] - ms);
+      lsum += rec[1] * f;
+      o += rec[4 + d] * f;
     }
-    return static_cast<int>(e);
   }
+  store_out(a.out, oi, lsum > 0.f ? o / lsum * a.v_scale : 0.f, out_bf16 != 0);
 }
 
-template <int KV, int D, int BS, typename QT>
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return n;
+}
+
+constexpr int kMaxOcc = 3;   // the largest Pipe<>::kOcc
+
+template <int KV, int D, int BS, int G>
+int launch_one(const DecodeArgs& a0, int out_bf16, hipStream_t s) {
+  DecodeArgs a = a0;
+  const int64_t wgs = static_cast<int64_t>(device_cus()) * Pipe<KV, D>::kOcc / 8 * 8;   // resident, multiple of 8
+  a.streams = a.num_kv_heads % 8 == 0 ? 8 : 1;
+  a.stream_waves = static_cast<int32_t>(wgs / a.streams * kWaves);
+  a.stream_slots = static_cast<int64_t>(a.num_kv_heads / a.streams) * a.num_seqs * a.max_parts + a.stream_waves;
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return static_cast<int>(e);
+  hipLaunchKernelGGL((decode_stream_kernel<KV, D, BS, G>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s,
+                     a, out_bf16);
+  e = hipGetLastError();
+  if (e != hipSuccess) return static_cast<int>(e);
+  const int64_t rw = static_cast<int64_t>(a.num_q_heads) * a.num_seqs;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<unsigned>(rw)), dim3(D), 0, s, a, out_bf16);
+  return static_cast<int>(hipGetLastError());
+}
+
+template <int KV, int D, int BS>
 int pick_group(const DecodeArgs& a, int out_bf16, hipStream_t s) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_one<KV, D, BS, 1, QT>(a, out_bf16, s);
-    case 2: return launch_one<KV, D, BS, 2, QT>(a, out_bf16, s);
-    case 4: return launch_one<KV, D, BS, 4, QT>(a, out_bf16, s);
-    case 8: return launch_one<KV, D, BS, 8, QT>(a, out_bf16, s);
+    case 1: return launch_one<KV, D, BS, 1>(a, out_bf16, s);
+    case 2: return launch_one<KV, D, BS, 2>(a, out_bf16, s);
+    case 4: return launch_one<KV, D, BS, 4>(a, out_bf16, s);
+    case 8: return launch_one<KV, D, BS, 8>(a, out_bf16, s);
     default: return -1;
   }
 }
 
-template <int KV, int D, typename QT>
+template <int KV, int D>
 int pick_block(const DecodeArgs& a, int bs, int out_bf16, hipStream_t s) {
   switch (bs) {
-    case 8: return pick_group<KV, D, 8, QT>(a, out_bf16, s);
-    case 16: return pick_group<KV, D, 16, QT>(a, out_bf16, s);
-    case 32: return pick_group<KV, D, 32, QT>(a, out_bf16, s);
+    case 8: return pick_group<KV, D, 8>(a, out_bf16, s);
+    case 16: return pick_group<KV, D, 16>(a, out_bf16, s);
+    case 32: return pick_group<KV, D, 32>(a, out_bf16, s);
     default: return -1;
   }
 }
 
-template <int KV, typename QT>
+template <int KV>
 int pick_dim(const DecodeArgs& a, int bs, int d, int out_bf16, hipStream_t s) {
   switch (d) {
-    case 64: return pick_block<KV, 64, QT>(a, bs, out_bf16, s);
-    case 128: return pick_block<KV, 128, QT>(a, bs, out_bf16, s);
+    case 64: return pick_block<KV, 64>(a, bs, out_bf16, s);
+    case 128: return pick_block<KV, 128>(a, bs, out_bf16, s);
     default: return -1;
   }
 }
 
 }  // namespace
 
+int decode_max_waves() { return device_cus() * kMaxOcc * kWaves; }
+
+size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t max_parts,
+                              int64_t waves) {
+  const int64_t pref = ((num_seqs + 1) * 4 + 255) / 256 * 256;
+  const int64_t g = num_q_heads < 8 ? num_q_heads : 8;   // G <= 8 and G <= num_q_heads
+  const int64_t records = num_q_heads * num_seqs * max_parts + waves * g;
+  return static_cast<size_t>(pref + records * (head_dim + 4) * 4);
+}
+
 int launch_decode(const DecodeArgs& a, int kv_dtype, int q_dtype, int out_dtype, int block_size,
                   int head_dim, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int ob = out_dtype == kBF16;
-  if (kv_dtype == kF32 && q_dtype == kF32) return pick_dim<kF32, float>(a, block_size, head_dim, ob, s);
-  if (kv_dtype == kBF16 && q_dtype == kBF16) return pick_dim<kBF16, uint16_t>(a, block_size, head_dim, ob, s);
-  if (kv_dtype == kFP8 && q_dtype == kBF16) return pick_dim<kFP8, uint16_t>(a, block_size, head_dim, ob, s);
+  if (a.part_tokens % kUnit != 0 || a.part_tokens <= 0) return -1;
+  if (kv_dtype == kF32 && q_dtype == kF32) return pick_dim<kF32>(a, block_size, head_dim, ob, s);
+  if (kv_dtype == kBF16 && q_dtype == kBF16) return pick_dim<kBF16>(a, block_size, head_dim, ob, s);
+  if (kv_dtype == kFP8 && q_dtype == kBF16) return pick_dim<kFP8>(a, block_size, head_dim, ob, s);
   return -1;
 }
 

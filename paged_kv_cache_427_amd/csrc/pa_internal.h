@@ -52,14 +52,23 @@ struct DecodeArgs {
   int32_t num_kv_heads;
   float qk_scale;        // scale * k_scale * log2(e): logits in base-2 units
   float v_scale;
-  int32_t part_tokens;   // tokens per partition
+  int32_t part_tokens;   // tokens per partition (a multiple of 16; no sequence crosses one when it
+                         // covers max_ctx)
   int32_t max_parts;     // partitions of the longest sequence
   int32_t max_ctx;       // bound on every context length (lengths are clamped to it on the device)
-  float* ws_m;           // [num_seqs][num_q_heads][max_parts]
-  float* ws_l;
-  float* ws_o;           // [num_seqs][num_q_heads][max_parts][head_dim]
+  int32_t streams;       // unit streams: 8 (one per XCD; KV head h in stream h % 8) or 1
+  int32_t stream_waves;  // waves per stream
+  int64_t stream_slots;  // partial-record slots per stream
+  int32_t* ws_pref;      // [num_seqs + 1] units (16 keys) of sequences before s, for one KV head
+  float* ws_part;        // [streams * stream_slots][G][head_dim + 4]: max, sum, -, -, unnormalised o
   void* out;
 };
+
+// Bytes of the decode workspace for a launch of `waves` waves (see pa_decode_workspace_size).
+size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t max_parts,
+                              int64_t waves);
+// Waves of one decode launch on the current device (an upper bound for any dtype).
+int decode_max_waves();
 
 struct PrefillArgs {
   const void* q;

@@ -11,17 +11,22 @@
 //  * a workgroup of 4 wave64s owns 128 (query, head) rows of one KV-head group: 128/G queries of
 //    the G query heads that share the KV head, so one K/V tile in LDS serves every head of the group;
 //    each wave owns 32 rows;
-//  * key tiles of 64 positions are gathered through the block table (one lookup per block row),
-//    widened to bf16 (fp8 e4m3 codes convert exactly; scales stay in fp32) and stored in LDS: K as
-//    [key][dim], V transposed as [dim][key], double-buffered so the next tile's global loads are in
-//    flight during the current tile's MFMAs;
+//  * key tiles of 64 positions are gathered through the block table and stored in LDS as bf16 (fp8
+//    e4m3 codes convert exactly; scales stay in fp32), double-buffered so that the next tile's global
+//    loads are in flight during the current tile's MFMAs.  Every load instruction of a wave reads
+//    inside one pool block, so the table entries are wave-uniform scalar loads, and every load is
+//    issued unconditionally, so that the only wait for them is the one before the LDS store.  K
+//    tiles are stored [key][dim]; the V pool's dim-major tiles give [dim][key] rows directly, so V
+//    needs no transposition, only a fixed permutation of the keys inside each 16-key group;
 //  * scores are formed transposed, S^T = K Q^T (A = K rows from LDS, B = Q held in registers), so the
 //    fp32 result layout (each lane owns one query row and 16 keys) becomes, after bf16 rounding,
 //    exactly the B operand of O^T = V^T P^T; softmax statistics need one cross-half lane exchange;
-//  * the rescale of the output accumulators is skipped while the running max has grown by less than
-//    2^8 (base-2 logits), which keeps every exp bounded by 256;
-//  * the grid is remapped so all query tiles of one (sequence, KV head) run on the same XCD and share
-//    its L2.
+//  * logits are scaled and shifted by one fma before the exp; the rescale of the output accumulators
+//    is skipped while the running max has grown by less than 2^8 (base-2 logits), which keeps every
+//    exp bounded by 256;
+//  * work order: sequences longest first (when there are at most 64), the query tiles of each
+//    (sequence, KV head) from the last (longest) to the first, and all tiles of one KV head on one
+//    XCD so that they share its L2.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -40,103 +45,156 @@ constexpr int kKT = 64;          // keys per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 128;       // (query, head) rows per workgroup
-constexpr int kKStride = kD * 2 + 16;    // bytes per K row in LDS (padding spreads banks)
-constexpr int kVStride = kKT * 2 + 8;    // bytes per V^T row in LDS
+constexpr int kKStride = kD * 2 + 16;    // bytes per K row in LDS (the padding spreads banks)
+constexpr int kVStride = kKT * 2 + 16;   // bytes per V^T row in LDS
 constexpr int kKBytes = kKT * kKStride;
 constexpr int kVBytes = kD * kVStride;
 constexpr int kBufBytes = kKBytes + kVBytes;
 constexpr float kRescaleSlack = 8.0f;    // log2 of the largest unrescaled growth
+constexpr int kMaxRanked = 64;           // sequences ordered by length when there are at most this many
 
-template <int KV>
-struct Src;
-template <>
-struct Src<kBF16> {
-  static constexpr int kElem = 2, kEPC = 8;     // elements per 16-byte chunk
-};
-template <>
-struct Src<kFP8> {
-  static constexpr int kElem = 1, kEPC = 16;
-};
+// Inside each 16-key group of a V^T row, key k sits at LDS position k with bits 2 and 3 swapped:
+// keys 0-3, 8-11 | 4-7, 12-15.  The P^T operand of lane half h holds keys 4h..4h+3 and 8+4h..8+4h+3
+// of the group (the S^T accumulator layout), which are then the 8 contiguous positions 8h..8h+7.
 
-// Global -> registers for one key tile: each thread owns `kUnits` (key pair, 16-byte chunk) units.
+__device__ __forceinline__ uint32_t fp8x2_lo(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t fp8x2_hi(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
+// Global -> registers -> LDS for one 64-key tile.
+//   K: 16-byte chunks of pool rows; chunk id = u * 256 + thread -> key id / CPR, chunk id % CPR.
+//   V: 16-key pieces of a dim row; piece id = u * 256 + thread -> key group id / 128, dim id % 128.
+// Both id orders keep each wave's loads of one instruction inside one pool block.
 template <int KV, int BS>
 struct TileLoader {
-  static constexpr int kRowBytes = kD * Src<KV>::kElem;
-  static constexpr int kChunks = kRowBytes / 16;             // chunks per key row
-  static constexpr int kUnits = (kKT / 2) * kChunks / kThreads;
-  uint4 k0[kUnits], k1[kUnits], v0[kUnits], v1[kUnits];
+  static constexpr int kE = KV == kBF16 ? 2 : 1;
+  static constexpr int kRowBytes = kD * kE;
+  static constexpr int kCPR = kRowBytes / 16;           // K chunks per key row
+  static constexpr int kKU = kKT * kCPR / kThreads;     // K chunks per thread (fp8 2, bf16 4)
+  static constexpr int kVU = 4 * kD / kThreads;         // V pieces per thread (2)
+  static constexpr int kVW = 16 * kE / 4;               // dwords of one 16-key piece (fp8 4, bf16 8)
+  uint4 k[kKU];
+  uint32_t v[kVU][kVW];
 
-  __device__ void load(const char* kpool, const char* vpool, const int32_t* tab, int64_t blk_stride,
-                       int64_t head_off, int tile, int n_keys) {
+  // Tile keys [key0, key0 + 64).  Every load is issued unconditionally, so that the only wait for
+  // them is the one before store(); a block past the last one holding a key < n_keys is read as
+  // that last block (its keys are masked: scores by the causal mask, values zeroed in store()).
+  __device__ __forceinline__ void load(const char* kpool, const char* vpool, const int32_t* tab,
+                                       int64_t blk_stride, int64_t head_off, int key0, int n_keys,
+                                       int wave, int lane) {
+    const int jlast = (n_keys - 1) / BS;
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-      const int unit = threadIdx.x + kThreads * u;
-      const int kp = unit / kChunks;
-      const int ch = unit % kChunks;
+    for (int u = 0; u < kKU; ++u) {
+      // keys of this wave's instruction: key0 + (u*256 + 64*wave) / CPR .. + 64/CPR (one block)
+      const int kw = key0 + (u * kThreads + 64 * wave) / kCPR;
+      const int key = key0 + (u * kThreads + 64 * wave + lane) / kCPR;
+      const int ch = lane % kCPR;
+      const int64_t phys = tab[min(kw / BS, jlast)];
+      k[u] = *reinterpret_cast<const uint4*>(kpool + phys * blk_stride + head_off +
+                                             static_cast<int64_t>(key % BS) * kRowBytes + ch * 16);
+    }
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int key = tile * kKT + 2 * kp + half;
-        uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (key < n_keys) {
-          const int64_t off = static_cast<int64_t>(tab[key / BS]) * blk_stride + head_off +
-                              static_cast<int64_t>(key % BS) * kRowBytes + ch * 16;
-          kk = *reinterpret_cast<const uint4*>(kpool + off);
-          vv = *reinterpret_cast<const uint4*>(vpool + off);
+    for (int u = 0; u < kVU; ++u) {
+      const int g16 = 2 * u + (wave >> 1);              // 16-key group of the tile
+      const int dim = 64 * (wave & 1) + lane;
+      const int kg = key0 + 16 * g16;                   // first key of the group
+      if constexpr (BS >= 16) {
+        const int64_t phys = tab[min(kg / BS, jlast)];
+        const char* row = vpool + phys * blk_stride + head_off + static_cast<int64_t>(dim) * BS * kE +
+                          (kg % BS) * kE;
+#pragma unroll
+        for (int j = 0; j < kVW / 4; ++j) {
+          const uint4 w = reinterpret_cast<const uint4*>(row)[j];
+          v[u][4 * j] = w.x; v[u][4 * j + 1] = w.y; v[u][4 * j + 2] = w.z; v[u][4 * j + 3] = w.w;
         }
-        if (half == 0) { k0[u] = kk; v0[u] = vv; } else { k1[u] = kk; v1[u] = vv; }
+      } else {
+        // two 8-key blocks
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int64_t phys = tab[min(kg / 8 + hb, jlast)];
+          const char* row = vpool + phys * blk_stride + head_off + static_cast<int64_t>(dim) * 8 * kE;
+          if constexpr (kE == 1) {
+            const uint2 w = *reinterpret_cast<const uint2*>(row);
+            v[u][2 * hb] = w.x; v[u][2 * hb + 1] = w.y;
+          } else {
+            const uint4 w = *reinterpret_cast<const uint4*>(row);
+            v[u][4 * hb] = w.x; v[u][4 * hb + 1] = w.y; v[u][4 * hb + 2] = w.z; v[u][4 * hb + 3] = w.w;
+          }
+        }
       }
     }
   }
 
-  // Widen to bf16 and store: K row-major, V transposed (one dword = the two keys of a pair).
-  __device__ void store(char* buf) const {
+  // Widen to bf16 and write the tile to LDS.  Values of keys >= n_keys may hold any bits (even
+  // NaN, or another block's data): they are zeroed so that 0 * v stays 0.
+  __device__ __forceinline__ void store(char* buf, int key0, int n_keys, int wave, int lane) {
     char* ks = buf;
     char* vt = buf + kKBytes;
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-      const int unit = threadIdx.x + kThreads * u;
-      const int kp = unit / kChunks;
-      const int ch = unit % kChunks;
-      constexpr int EPC = Src<KV>::kEPC;
-      uint32_t kb0[EPC / 2], kb1[EPC / 2], vb0[EPC / 2], vb1[EPC / 2];
-      widen(k0[u], kb0);
-      widen(k1[u], kb1);
-      widen(v0[u], vb0);
-      widen(v1[u], vb1);
-      const int d0 = ch * EPC;
-#pragma unroll
-      for (int i = 0; i < EPC / 8; ++i) {
-        *reinterpret_cast<uint4*>(ks + (2 * kp) * kKStride + (d0 + 8 * i) * 2) =
-            make_uint4(kb0[4 * i], kb0[4 * i + 1], kb0[4 * i + 2], kb0[4 * i + 3]);
-        *reinterpret_cast<uint4*>(ks + (2 * kp + 1) * kKStride + (d0 + 8 * i) * 2) =
-            make_uint4(kb1[4 * i], kb1[4 * i + 1], kb1[4 * i + 2], kb1[4 * i + 3]);
-      }
-#pragma unroll
-      for (int i = 0; i < EPC / 2; ++i) {
-        const uint32_t lo = (vb0[i] & 0xffffu) | (vb1[i] << 16);           // dim d0 + 2i
-        const uint32_t hi = (vb0[i] >> 16) | (vb1[i] & 0xffff0000u);       // dim d0 + 2i + 1
-        *reinterpret_cast<uint32_t*>(vt + (d0 + 2 * i) * kVStride + 4 * kp) = lo;
-        *reinterpret_cast<uint32_t*>(vt + (d0 + 2 * i + 1) * kVStride + 4 * kp) = hi;
+    for (int u = 0; u < kKU; ++u) {
+      const int id = u * kThreads + 64 * wave + lane;
+      const int key = id / kCPR;
+      const int ch = id % kCPR;
+      char* dst = ks + key * kKStride;
+      if constexpr (kE == 2) {
+        *reinterpret_cast<uint4*>(dst + ch * 16) = k[u];
+      } else {
+        const uint4 c = k[u];
+        *reinterpret_cast<uint4*>(dst + ch * 32) = make_uint4(fp8x2_lo(c.x), fp8x2_hi(c.x), fp8x2_lo(c.y), fp8x2_hi(c.y));
+        *reinterpret_cast<uint4*>(dst + ch * 32 + 16) =
+            make_uint4(fp8x2_lo(c.z), fp8x2_hi(c.z), fp8x2_lo(c.w), fp8x2_hi(c.w));
       }
     }
-  }
-
-  // 16 bytes of stored codes -> packed bf16 pairs (element 2i in the low half of out[i]).
-  __device__ static void widen(const uint4& c, uint32_t* out) {
-    if constexpr (KV == kBF16) {
-      out[0] = c.x; out[1] = c.y; out[2] = c.z; out[3] = c.w;
-    } else {
-      const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
-        auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
-        out[2 * i] = __builtin_bit_cast(uint32_t, lo);
-        out[2 * i + 1] = __builtin_bit_cast(uint32_t, hi);
+    for (int u = 0; u < kVU; ++u) {
+      const int g16 = 2 * u + (wave >> 1);
+      const int dim = 64 * (wave & 1) + lane;
+      const int valid = n_keys - (key0 + 16 * g16);      // keys of the group below n_keys
+      if (valid < 16) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (e < valid) continue;
+          if constexpr (kE == 1)
+            v[u][e / 4] &= ~(0xffu << (8 * (e % 4)));
+          else
+            v[u][e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
       }
+      uint32_t d[8];   // bf16 pairs: d[m] = keys 2m, 2m+1 of the group
+      if constexpr (kE == 2) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) d[m] = v[u][m];
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          d[2 * m] = fp8x2_lo(v[u][m]);
+          d[2 * m + 1] = fp8x2_hi(v[u][m]);
+        }
+      }
+      char* dst = vt + dim * kVStride + g16 * 32;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[4], d[5]);        // keys 0-3, 8-11
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(d[2], d[3], d[6], d[7]);   // keys 4-7, 12-15
     }
   }
 };
+
+// Sequence of length rank r (0 = most keys; ties by index), for num_seqs <= kMaxRanked.  Every wave
+// computes it on its own: lane s ranks sequence s against all others.
+__device__ __forceinline__ int seq_of_rank(const PrefillArgs& a, int r, int lane) {
+  const int n = a.num_seqs;
+  int mine = -1;
+  if (lane < n) mine = a.prior[lane] + a.qsl[lane + 1] - a.qsl[lane];
+  int rank = 0;
+  for (int s = 0; s < n; ++s) {
+    const int other = a.prior[s] + a.qsl[s + 1] - a.qsl[s];
+    rank += (other > mine) || (other == mine && s < lane);
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < n && rank == r);
+  return hit ? static_cast<int>(__builtin_ctzll(hit)) : 0;
+}
 
 template <int KV, int BS, int G>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int out_bf16, int num_qtiles,
@@ -144,22 +202,29 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   constexpr int QT = kRows / G;      // queries per workgroup
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
 
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
   // ---- which (sequence, KV head, query tile) ----
-  const int groups = a.num_seqs * a.num_kv_heads;
-  int grp, qt;
+  int rank, kvh, qt;
   if (xcd_remap) {
-    // workgroup i runs on XCD i % 8; give that XCD whole groups so their tiles share its L2
+    // workgroup i runs on XCD i % 8; that XCD takes the KV heads congruent to it, so all query
+    // tiles of one (sequence, KV head) share its L2
     const int x = blockIdx.x % 8;
     const int j = blockIdx.x / 8;
-    grp = x + 8 * (j / num_qtiles);
     qt = num_qtiles - 1 - j % num_qtiles;   // longest tiles first
+    const int rr = j / num_qtiles;
+    const int hpx = a.num_kv_heads / 8;
+    rank = rr / hpx;
+    kvh = (rr % hpx) * 8 + x;
   } else {
-    grp = blockIdx.x / num_qtiles;
     qt = num_qtiles - 1 - blockIdx.x % num_qtiles;
+    const int rr = blockIdx.x / num_qtiles;
+    rank = rr / a.num_kv_heads;
+    kvh = rr % a.num_kv_heads;
   }
-  if (grp >= groups) return;
-  const int seq = grp / a.num_kv_heads;
-  const int kvh = grp % a.num_kv_heads;
+  if (rank >= a.num_seqs) return;
+  const int seq = a.num_seqs <= kMaxRanked ? seq_of_rank(a, rank, lane) : rank;
   const int q_base = a.qsl[seq];
   const int C = a.qsl[seq + 1] - q_base;
   const int q0 = qt * QT;
@@ -169,8 +234,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   const int n_keys = P + q_end;
   const int n_tiles = (n_keys + kKT - 1) / kKT;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;
   const int row = wave * 32 + (lane & 31);
   const int g = row / QT;
@@ -194,9 +257,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   const char* kpool = static_cast<const char*>(a.k_pool);
   const char* vpool = static_cast<const char*>(a.v_pool);
   const int32_t* tab = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
-  constexpr int kRowBytes = TileLoader<KV, BS>::kRowBytes;
-  const int64_t head_off = static_cast<int64_t>(kvh) * BS * kRowBytes;
-  const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * BS * kRowBytes;
+  constexpr int kTile = BS * TileLoader<KV, BS>::kRowBytes;   // bytes of one (block, head) tile
+  const int64_t head_off = static_cast<int64_t>(kvh) * kTile;
+  const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * kTile;
 
   f32x16 o[4];
 #pragma unroll
@@ -205,15 +268,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m_run = -INFINITY;   // running max (base-2 logits) of this row, the one the accumulators use
   float l_run = 0.f;
+  const float c2 = a.qk_scale;
 
   TileLoader<KV, BS> ld;
-  ld.load(kpool, vpool, tab, blk_stride, head_off, 0, n_keys);
-  ld.store(smem);
+  ld.load(kpool, vpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+  ld.store(smem, 0, n_keys, wave, lane);
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     char* buf = smem + (t & 1) * kBufBytes;
-    if (t + 1 < n_tiles) ld.load(kpool, vpool, tab, blk_stride, head_off, t + 1, n_keys);
+    // the last iteration re-reads its own tile (unused), so that the load is unconditional
+    ld.load(kpool, vpool, tab, blk_stride, head_off, min(t + 1, n_tiles - 1) * kKT, n_keys, wave, lane);
 
     // ---- S^T = K Q^T for two 32-key halves ----
     f32x16 s[2];
@@ -229,28 +294,28 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
       }
     }
 
-    // ---- scale, causal mask, running max ----
+    // ---- causal mask (tiles crossing the diagonal only), running max of the raw scores ----
     const int key_base = t * kKT;
-    const bool diag = key_base + kKT - 1 > P + q0;
+    if (key_base + kKT - 1 > P + q0) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key_base + sb * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+          s[sb][r] = key <= qpos ? s[sb][r] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[sb][r] * a.qk_scale;
-        if (diag) {
-          const int key = key_base + sb * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-          x = key <= qpos ? x : -INFINITY;
-        }
-        s[sb][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+    mx = fmaxf(mx, shfl_xor(mx, 32)) * c2;     // base-2 logit units (c2 > 0)
     // rescale only when the max moved by more than the slack (wave-uniform decision)
     const bool grow = mx > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? mx : m_run;
-      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -258,16 +323,16 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
-    const float ms = m_run == -INFINITY ? 0.f : m_run;
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
 
-    // ---- P^T = 2^(S^T - m) as bf16 B operands; row sums ----
+    // ---- P^T = 2^(c2 S^T - m) as bf16 B operands; row sums ----
     bf16x8 pb[4];
     float lsum = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(s[c / 2][8 * (c % 2) + e] - ms);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c / 2][8 * (c % 2) + e], c2, nm));
         lsum += p;
         pb[c][e] = static_cast<__bf16>(p);
       }
@@ -276,18 +341,15 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const char* vrow = buf + kKBytes + (dt * 32 + (lane & 31)) * kVStride;
+      const char* vrow = buf + kKBytes + (dt * 32 + (lane & 31)) * kVStride + 16 * h;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        // k-slots 0..3 <- keys 16c + 4h + 0..3, slots 4..7 <- keys 16c + 8 + 4h + 0..3
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (16 * c + 4 * h) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (16 * c + 8 + 4 * h) * 2);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + 32 * c);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], o[dt], 0, 0, 0);
       }
     }
 
-    if (t + 1 < n_tiles) ld.store(smem + ((t + 1) & 1) * kBufBytes);
+    if (t + 1 < n_tiles) ld.store(smem + ((t + 1) & 1) * kBufBytes, (t + 1) * kKT, n_keys, wave, lane);
     __syncthreads();
   }
 
@@ -317,7 +379,7 @@ int launch_g(const PrefillArgs& a, int out_bf16, hipStream_t s) {
   constexpr int QT = kRows / G;
   const int num_qtiles = (a.max_chunk + QT - 1) / QT;
   const int64_t groups = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads;
-  const int xcd_remap = groups % 8 == 0;
+  const int xcd_remap = a.num_kv_heads % 8 == 0;
   const int64_t wgs = groups * num_qtiles;
   if (wgs > 0x7fffffff) return -1;
   hipLaunchKernelGGL((prefill_kernel<KV, BS, G>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s, a,

@@ -56,11 +56,13 @@ class PagedKVEngine:
         self.device = torch.device(device)
         self.pool = make_pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
                                    _PA[wl.kv_dtype], wl.k_scale, wl.v_scale)
-        shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+        # K tiles are [block_size][head_dim] (token-major), V tiles [head_dim][block_size] (dim-major)
+        k_shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+        v_shape = (wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.block_size)
         bits = {"f32": 32, "bf16": 16, "fp8": 8}[wl.kv_dtype]
         fill = 0 if poison is None else (_signed(poison, bits) if wl.kv_dtype != "fp8" else poison)
-        self.k_pool = torch.full(shape, fill, dtype=_CODE_TORCH[wl.kv_dtype], device=self.device).view(_VIEW[wl.kv_dtype])
-        self.v_pool = torch.full(shape, fill, dtype=_CODE_TORCH[wl.kv_dtype], device=self.device).view(_VIEW[wl.kv_dtype])
+        self.k_pool = torch.full(k_shape, fill, dtype=_CODE_TORCH[wl.kv_dtype], device=self.device).view(_VIEW[wl.kv_dtype])
+        self.v_pool = torch.full(v_shape, fill, dtype=_CODE_TORCH[wl.kv_dtype], device=self.device).view(_VIEW[wl.kv_dtype])
         self.alloc = BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
         self.k_tok = wl.k_tok.to(self.device)
         self.v_tok = wl.v_tok.to(self.device)

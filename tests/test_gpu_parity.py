@@ -93,7 +93,7 @@ def test_tiny_reads_back_the_written_token():
     torch.cuda.synchronize()
     kv = decode_pool(ref.k_pool, "f32"), decode_pool(ref.v_pool, "f32")
     q = act_values(tensor_bits(wl.q_decode), "f32")
-    seqs = [(gather_seq(kv[0], ref.tables[s], int(L) + 1), gather_seq(kv[1], ref.tables[s], int(L) + 1))
+    seqs = [(gather_seq(kv[0], ref.tables[s], int(L) + 1), gather_seq(kv[1], ref.tables[s], int(L) + 1, "v"))
             for s, L in zip(wl.decode_seqs, wl.decode_lens)]
     assert _out_err(out, ref_decode(q, seqs, wl.scale)) <= TOL["f32"]
 
@@ -248,6 +248,12 @@ def test_full_size_sampled(name):
         if wl.kv_dtype == "fp8":
             row = e4m3_quantise(act_values(row, wl.act_dtype).astype(np.float32), wl.k_scale)
         assert np.array_equal(got, row)
+        # V tiles are dim-major: the token's values are column slot % b of its tile
+        got_v = tensor_bits(eng.v_pool[slot // wl.block_size, :, :, slot % wl.block_size])
+        row_v = tensor_bits(wl.v_tok[s0 + t])
+        if wl.kv_dtype == "fp8":
+            row_v = e4m3_quantise(act_values(row_v, wl.act_dtype).astype(np.float32), wl.v_scale)
+        assert np.array_equal(got_v, row_v)
     if wl.prefill_seqs:
         worst = 0.0
         starts = np.concatenate([[0], np.cumsum(wl.prefill_chunk)])

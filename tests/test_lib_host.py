@@ -227,10 +227,16 @@ def test_prefill_validation():
 
 
 def test_workspace_size_formula():
+    """The decode workspace holds the per-sequence unit prefix (256-byte aligned) and one partial record
+    of head_dim + 4 floats per (query head, sequence, partition) plus a bounded number per wave."""
     n = ctypes.c_size_t()
-    assert lib().pa_decode_workspace_size(4, 8, 128, 512, 512, ctypes.byref(n)) == 0 and n.value == 0
-    assert lib().pa_decode_workspace_size(4, 8, 128, 513, 512, ctypes.byref(n)) == 0
-    parts = 2
-    entries = 4 * 8 * parts
-    align = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert n.value == 2 * align(entries * 4) + align(entries * 128 * 4)
+    L = lib()
+    assert L.pa_decode_workspace_size(4, 8, 128, 512, 512, ctypes.byref(n)) == 0
+    one_part = n.value
+    assert L.pa_decode_workspace_size(4, 8, 128, 513, 512, ctypes.byref(n)) == 0
+    two_parts = n.value
+    assert two_parts - one_part == 8 * 4 * (128 + 4) * 4      # one more partition per (head, sequence)
+    assert L.pa_decode_workspace_size(4, 8, 128, 4000, 0, ctypes.byref(n)) == 0
+    assert n.value == one_part                                 # 0 = no partition cuts
+    assert one_part >= 256 + 8 * 4 * (128 + 4) * 4
+    assert L.pa_decode_workspace_size(4, 8, 128, 512, 48, ctypes.byref(n)) == PA_ERR_INVALID
