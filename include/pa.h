@@ -23,14 +23,17 @@
  *     with no implicit synchronisation.  Calls that overlap on different streams and touch the same
  *     pool blocks race.
  *
- * Pool layout (fixed by this ABI).  K and V live in two separate device arrays, each
- *     [num_blocks][num_kv_heads][block_size][head_dim]
- * of elements of `dtype`, row-major.  One (block, KV head) tile is block_size * head_dim elements
- * contiguous in memory, so the tokens of one block are read with whole-cache-line loads and the
- * only indirection is one table lookup per block ([day28] §三 3.2: contiguous inside a block, a
- * pointer jump between blocks).  Token at slot s lies in block s / block_size, row
- * s % block_size.  An fp8 pool stores OCP e4m3 codes; value = decode(code) * scale, with one fp32
- * scale per pool (k_scale for K, v_scale for V).
+ * Pool layout (fixed by this ABI).  K and V live in two separate device arrays of elements of
+ * `dtype`, row-major:
+ *     K: [num_blocks][num_kv_heads][block_size][head_dim]   (token-major tiles)
+ *     V: [num_blocks][num_kv_heads][head_dim][block_size]   (dim-major tiles)
+ * One (block, KV head) tile is block_size * head_dim elements contiguous in memory, so the tokens of
+ * one block are read with whole-cache-line loads and the only indirection is one table lookup per
+ * block ([day28] §三 3.2: contiguous inside a block, a pointer jump between blocks).  Inside a tile,
+ * element (row o, dim d) sits at o * head_dim + d in K and at d * block_size + o in V: K rows feed
+ * the q.k products dim-contiguous, V columns feed the p.v products key-contiguous.  Token at slot s
+ * lies in block s / block_size, row s % block_size.  An fp8 pool stores OCP e4m3 codes;
+ * value = decode(code) * scale, with one fp32 scale per pool (k_scale for K, v_scale for V).
  */
 #ifndef PA_H_
 #define PA_H_
@@ -110,9 +113,12 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool, c
                          int32_t num_pairs, pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
- * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for these sizes.
+ * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for these sizes, on the
+ * current device (the size depends on its compute-unit count).
  *   partition_size 0 means the library's choice (the same choice pa_decode makes for 0).
- * Zero bytes when every sequence fits one partition (max_context_len <= partition size).
+ * The workspace holds the per-sequence work plan and the partial (max, sum, unnormalised output)
+ * records of context pieces, one record of head_dim + 4 floats per (query head, sequence,
+ * partition) plus a bounded number per resident wave.
  * ------------------------------------------------------------------------------------------- */
 pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t max_context_len, int32_t partition_size, size_t* bytes);
@@ -130,12 +136,13 @@ pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_
  *   context_lens  device int32 [num_seqs]; L_s in [0, max_context_len]; L_s == 0 gives zeros
  *   num_q_heads   multiple of pool->num_kv_heads; group size num_q_heads / num_kv_heads in {1,2,4,8}
  *   scale         fp32 softmax scale (e.g. fp32(1/sqrt(head_dim)))
- *   partition_size  tokens per context partition, a positive multiple of 32 (0 = library choice).  A
- *                 sequence longer than one partition is processed partition by partition and
- *                 merged by a second kernel (max, rescaled sums).
- *   max_context_len  an upper bound of every L_s (sizes the launch)
- *   workspace     device buffer of at least pa_decode_workspace_size(...) bytes (may be NULL when
- *                 that size is 0); its content on entry does not matter
+ *   partition_size  tokens per context partition, a positive multiple of 32, or 0 (library choice:
+ *                 no partition boundaries).  The context of every (sequence, KV head) is split into
+ *                 pieces for load balance; no piece crosses a partition boundary, and a second
+ *                 kernel merges the pieces of each output (max, rescaled sums).
+ *   max_context_len  an upper bound of every L_s (sizes the launch and the workspace)
+ *   workspace     device buffer of at least pa_decode_workspace_size(...) bytes; its content on
+ *                 entry does not matter.  Calls that share a workspace must not overlap.
  *   out           device [num_seqs][num_q_heads][head_dim] of out_dtype (PA_F32 or PA_BF16;
  *                 bf16 rounds to nearest-even from the fp32 accumulator)
  * Combinations: pool PA_F32 needs q PA_F32; pools PA_BF16 / PA_FP8_E4M3 need q PA_BF16.

@@ -11,7 +11,8 @@ PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 
 
 class PoolDesc(ctypes.Structure):
-    """pa_pool_desc: pools are [num_blocks][num_kv_heads][block_size][head_dim] of `dtype`."""
+    """pa_pool_desc: K pools are [num_blocks][num_kv_heads][block_size][head_dim] of `dtype`, V pools
+    [num_blocks][num_kv_heads][head_dim][block_size]."""
     _fields_ = [("num_blocks", c_int32), ("block_size", c_int32), ("num_kv_heads", c_int32),
                 ("head_dim", c_int32), ("dtype", c_int32), ("k_scale", c_float), ("v_scale", c_float)]
 

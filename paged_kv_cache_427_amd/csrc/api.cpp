@@ -62,7 +62,7 @@ int elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : 1; }
 // Tokens per decode partition: the caller's size, or (0) one partition spanning every sequence.
 int32_t decode_partition(int32_t max_ctx, int32_t partition_size) {
   if (partition_size > 0) return partition_size;
-  return max_ctx > 0 ? (max_ctx + 15) / 16 * 16 : 16;
+  return max_ctx > 0 ? (max_ctx + 31) / 32 * 32 : 32;   // a multiple of the 32-key decode unit
 }
 
 int64_t decode_max_parts(int32_t max_ctx, int32_t part) {
@@ -192,7 +192,7 @@ pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const vo
   if (num_seqs == 0) return pa_ok();
   if (!q || !k_pool || !v_pool || !tables || !lens || !out)
     return pa_fail(PA_ERR_INVALID, "pa_decode: null pointer");
-  // stream positions (KV heads x 16-key units of all sequences) must fit in 31 bits
+  // stream positions (KV heads x 32-key units of all sequences) must fit in 31 bits
   if (static_cast<int64_t>(pool->num_kv_heads) * num_seqs * ((static_cast<int64_t>(max_context_len) + 15) / 16) >=
       (int64_t(1) << 31))
     return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 2^31 16-key units of K/V in one call");

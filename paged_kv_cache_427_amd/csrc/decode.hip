@@ -45,12 +45,11 @@ namespace pa {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kUnit = 16;          // keys per unit of one wave (one 16x16 S^T tile)
+constexpr int kUnit = 32;          // keys per unit of one wave (two 16x16 S^T tiles)
 constexpr float kSlack = 8.0f;     // log2 of the growth allowed before the accumulators are rescaled
 
 template <int KV>
@@ -64,19 +63,13 @@ struct Pipe {
   static constexpr int kOcc = KV == kF32 ? 2 : 3;
 };
 
-// S^T products: 16 keys x 32 dims (bf16) or 16 keys x 4 dims (fp32) per MFMA.
+// 16x16 MFMA tiles: 32-deep bf16 products (S^T over 32 dims; P.V over 32 keys) or 4-deep fp32 ones.
 __device__ __forceinline__ f32x4 mma_s(const bf16x8& a, const bf16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mma_s(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-// P.V product of one 16-dim tile over the unit's 16 keys (bf16 operands, 4 keys per lane group).
-__device__ __forceinline__ f32x4 mma_pv(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, make_uint2(a0, a1)),
-                                                   __builtin_bit_cast(s16x4, make_uint2(b0, b1)), c, 0, 0, 0);
-}
-
 // Codes in bytes 0,1 (HI = false) or 2,3 (HI = true) of w -> two bf16 in one dword (exact).
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
@@ -94,17 +87,17 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float x, bool bf
     static_cast<float*>(out)[i] = x;
 }
 
-// Raw registers of one 16-key unit, as loaded by one lane (i = lane % 16, kg = lane / 16).
-//  k[c]: key i of the unit, 16 bytes at byte 64c + 16kg of its row
-//        (bf16: dims 32c+8kg..+8; fp8: dims 64c+16kg..+16; fp32: dims 16c+4kg..+4)
-//  v[t]: dim 16t + i, keys 4kg .. 4kg+3 of the unit (VW dwords)
+// Raw registers of one 32-key unit, as loaded by one lane (i = lane % 16, kg = lane / 16).
+//  k[t][c]: key 16t + i of the unit, 16 bytes at byte 64c + 16kg of its row
+//           (bf16: dims 32c+8kg..+8; fp8: dims 64c+16kg..+16; fp32: dims 16c+4kg..+4)
+//  v[d][p]: dim 16d + i, keys 16p + 4kg .. +4 of the unit (VW dwords)
 template <int KV, int D>
 struct UnitRegs {
   static constexpr int E = Elem<KV>::kBytes;
-  static constexpr int KL = D * E / 64;   // 16-byte K loads per unit
+  static constexpr int KL = D * E / 64;   // 16-byte K loads per 16-key tile
   static constexpr int VW = E;            // dwords per 4-key V piece
-  uint4 k[KL];
-  uint32_t v[D / 16][VW];
+  uint4 k[2][KL];
+  uint32_t v[D / 16][2][VW];
 };
 
 template <int VW>
@@ -129,45 +122,56 @@ struct SeqView {
   int nblk;                // valid table entries: ceil(L / BS)
 };
 
-// Physical blocks of the unit starting at key U: one block, or two for 8-token blocks.  A block
-// past the sequence's last one (only possible in an 8-token-block unit that ends the sequence) is
-// replaced by the last one; its keys are masked afterwards.
+// Physical blocks of the unit starting at key U (32 keys: 4, 2 or 1 blocks of 8, 16 or 32 tokens).
+// A block past the sequence's last one (only in a unit that ends the sequence) is replaced by the
+// last one; its keys are masked afterwards.
+template <int BS>
 struct UnitBlocks {
-  int64_t b0, b1;
+  static constexpr int N = kUnit / BS;
+  int64_t b[N];
 };
 
 template <int BS>
-__device__ __forceinline__ UnitBlocks unit_blocks(const SeqView& sv, int U) {
+__device__ __forceinline__ UnitBlocks<BS> unit_blocks(const SeqView& sv, int U) {
   const int j0 = U / BS;
-  UnitBlocks ub;
-  ub.b0 = sv.tab[j0];
-  ub.b1 = BS == 8 ? static_cast<int64_t>(sv.tab[min(j0 + 1, sv.nblk - 1)]) : ub.b0;
+  UnitBlocks<BS> ub;
+#pragma unroll
+  for (int q = 0; q < UnitBlocks<BS>::N; ++q) ub.b[q] = sv.tab[min(j0 + q, sv.nblk - 1)];
   return ub;
 }
 
-// Issues the loads of the unit starting at key U (a multiple of 16) from its blocks `ub`.
+// Issues the loads of the unit starting at key U (a multiple of 32) from its blocks `ub`.
 template <int KV, int D, int BS>
-__device__ __forceinline__ void load_unit(UnitRegs<KV, D>& R, const SeqView& sv, const UnitBlocks& ub, int U,
-                                          int i, int kg) {
+__device__ __forceinline__ void load_unit(UnitRegs<KV, D>& R, const SeqView& sv, const UnitBlocks<BS>& ub, int i,
+                                          int kg) {
   using R_t = UnitRegs<KV, D>;
   constexpr int E = R_t::E, KL = R_t::KL, VW = R_t::VW;
-  const char* krow;
-  const char* vrow;
-  if constexpr (BS == 8) {
-    // keys 0-7 of the unit in b0, 8-15 in b1
-    const int64_t pk = (i >> 3) ? ub.b1 : ub.b0;
-    const int64_t pv = (kg >> 1) ? ub.b1 : ub.b0;
-    krow = sv.kbase + pk * sv.blk_stride + (i & 7) * (D * E);
-    vrow = sv.vbase + pv * sv.blk_stride + (4 * (kg & 1)) * E;
-  } else {
-    const int off = U % BS;
-    krow = sv.kbase + ub.b0 * sv.blk_stride + (off + i) * (D * E);
-    vrow = sv.vbase + ub.b0 * sv.blk_stride + (off + 4 * kg) * E;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const char* krow;                                   // key 16t + i of the unit
+    if constexpr (BS == 8) {
+      krow = sv.kbase + ((i >> 3) ? ub.b[2 * t + 1] : ub.b[2 * t]) * sv.blk_stride + (i & 7) * (D * E);
+    } else if constexpr (BS == 16) {
+      krow = sv.kbase + ub.b[t] * sv.blk_stride + i * (D * E);
+    } else {
+      krow = sv.kbase + ub.b[0] * sv.blk_stride + (16 * t + i) * (D * E);
+    }
+#pragma unroll
+    for (int c = 0; c < KL; ++c) R.k[t][c] = *reinterpret_cast<const uint4*>(krow + 64 * c + 16 * kg);
   }
 #pragma unroll
-  for (int c = 0; c < KL; ++c) R.k[c] = *reinterpret_cast<const uint4*>(krow + 64 * c + 16 * kg);
+  for (int p = 0; p < 2; ++p) {
+    const char* vrow;                                   // keys 16p + 4kg .. +4 of the unit
+    if constexpr (BS == 8) {
+      vrow = sv.vbase + ((kg >> 1) ? ub.b[2 * p + 1] : ub.b[2 * p]) * sv.blk_stride + (4 * (kg & 1)) * E;
+    } else if constexpr (BS == 16) {
+      vrow = sv.vbase + ub.b[p] * sv.blk_stride + (4 * kg) * E;
+    } else {
+      vrow = sv.vbase + ub.b[0] * sv.blk_stride + (16 * p + 4 * kg) * E;
+    }
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) load_piece<VW>(R.v[t], vrow + (16 * t + i) * BS * E);
+    for (int d = 0; d < D / 16; ++d) load_piece<VW>(R.v[d][p], vrow + (16 * d + i) * BS * E);
+  }
 }
 
 template <int KV, int D, int G>
@@ -190,93 +194,104 @@ struct DecodeState {
                                           float qk_scale) {
     using R_t = UnitRegs<KV, D>;
     constexpr int KL = R_t::KL;
-    // ---- S^T of the unit: lane holds keys 4kg + r for head col ----
-    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- S^T of the unit's two 16-key tiles: lane holds keys 16t + 4kg + r for head col ----
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KL; ++c) {
-      const uint4 w = R.k[c];
-      if constexpr (KV == kBF16) {
-        s = mma_s(__builtin_bit_cast(bf16x8, w), qb[c], s);
-      } else if constexpr (KV == kFP8) {
-        s = mma_s(as_bf16x8(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
-                            fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y)),
-                  qb[2 * c], s);
-        s = mma_s(as_bf16x8(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
-                            fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w)),
-                  qb[2 * c + 1], s);
-      } else {
-        s = mma_s(__uint_as_float(w.x), qb[4 * c + 0], s);
-        s = mma_s(__uint_as_float(w.y), qb[4 * c + 1], s);
-        s = mma_s(__uint_as_float(w.z), qb[4 * c + 2], s);
-        s = mma_s(__uint_as_float(w.w), qb[4 * c + 3], s);
-      }
-    }
-    // ---- base-2 logits; keys at or past the partition end are masked (last unit only) ----
-    float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = s[r] * qk_scale;
-    if (U + kUnit > t1) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (U + 4 * kg + r >= t1) x[r] = -INFINITY;
-      // masked keys may hold any bits (even NaN): zero their values so that 0 * v stays 0
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (U + 4 * kg + e < t1) continue;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          if constexpr (KV == kF32) {
-            R.v[t][e] = 0u;
-          } else if constexpr (KV == kBF16) {
-            R.v[t][e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          } else {
-            R.v[t][0] &= ~(0xffu << (8 * e));
-          }
+      for (int t = 0; t < 2; ++t) {
+        const uint4 w = R.k[t][c];
+        if constexpr (KV == kBF16) {
+          s[t] = mma_s(__builtin_bit_cast(bf16x8, w), qb[c], s[t]);
+        } else if constexpr (KV == kFP8) {
+          s[t] = mma_s(as_bf16x8(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
+                                 fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y)),
+                       qb[2 * c], s[t]);
+          s[t] = mma_s(as_bf16x8(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
+                                 fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w)),
+                       qb[2 * c + 1], s[t]);
+        } else {
+          s[t] = mma_s(__uint_as_float(w.x), qb[4 * c + 0], s[t]);
+          s[t] = mma_s(__uint_as_float(w.y), qb[4 * c + 1], s[t]);
+          s[t] = mma_s(__uint_as_float(w.z), qb[4 * c + 2], s[t]);
+          s[t] = mma_s(__uint_as_float(w.w), qb[4 * c + 3], s[t]);
         }
       }
     }
+    // ---- base-2 logits; keys at or past the context end are masked (last unit only) ----
+    float x[8];   // x[4t + r]: key 16t + 4kg + r of the unit
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[4 * t + r] = s[t][r] * qk_scale;
+    if (U + kUnit > t1) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (U + 16 * t + 4 * kg + r >= t1) x[4 * t + r] = -INFINITY;
+      // masked keys may hold any bits (even NaN): zero their values so that 0 * v stays 0
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (U + 16 * p + 4 * kg + e < t1) continue;
+#pragma unroll
+          for (int d = 0; d < D / 16; ++d) {
+            if constexpr (KV == kF32) {
+              R.v[d][p][e] = 0u;
+            } else if constexpr (KV == kBF16) {
+              R.v[d][p][e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            } else {
+              R.v[d][p][0] &= ~(0xffu << (8 * e));
+            }
+          }
+        }
+    }
     // ---- running max: raised only when a logit exceeds it by more than the slack ----
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     const bool grow = col < G && mx > m + kSlack;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));                  // max over the head's 16 keys
+      mx = fmaxf(mx, shfl_xor(mx, 32));                  // max over the head's 32 keys
       const float mn = mx > m + kSlack ? mx : m;
       const float alpha = mn == m ? 1.f : __builtin_amdgcn_exp2f(m - mn);   // 0 when m was -inf
       m = mn;
       l *= alpha;
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) o[t] *= alpha;
+      for (int d = 0; d < D / 16; ++d) o[d] *= alpha;
     }
     const float ms = m == -INFINITY ? 0.f : m;
-    float p[4];
+    float p[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - ms);   // 0 for masked keys
-    // ---- O^T += V^T P^T ----
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - ms);   // 0 for masked keys
+    // ---- O^T += V^T P^T: k-slot e of lane group kg is key 16(e/4) + 4kg + e%4 ----
     if constexpr (KV == kF32) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) l += p[e];
+      for (int e = 0; e < 8; ++e) l += p[e];
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t)
+      for (int d = 0; d < D / 16; ++d)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[t] = mma_s(__uint_as_float(R.v[t][e]), p[e], o[t]);
+        for (int e = 0; e < 8; ++e) o[d] = mma_s(__uint_as_float(R.v[d][e / 4][e % 4]), p[e], o[d]);
     } else {
-      uint32_t pb[2];
+      bf16x8 pb;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const __bf16 lo = static_cast<__bf16>(p[2 * e]);
-        const __bf16 hi = static_cast<__bf16>(p[2 * e + 1]);
-        l += static_cast<float>(lo) + static_cast<float>(hi);
-        pb[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+      for (int e = 0; e < 8; ++e) {
+        pb[e] = static_cast<__bf16>(p[e]);
+        l += static_cast<float>(pb[e]);
       }
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
+      for (int d = 0; d < D / 16; ++d) {
+        bf16x8 va;
         if constexpr (KV == kBF16) {
-          o[t] = mma_pv(R.v[t][0], R.v[t][1], pb[0], pb[1], o[t]);
+          va = as_bf16x8(R.v[d][0][0], R.v[d][0][1], R.v[d][1][0], R.v[d][1][1]);
         } else {
-          o[t] = mma_pv(fp8x2_to_bf16x2<false>(R.v[t][0]), fp8x2_to_bf16x2<true>(R.v[t][0]), pb[0], pb[1], o[t]);
+          va = as_bf16x8(fp8x2_to_bf16x2<false>(R.v[d][0][0]), fp8x2_to_bf16x2<true>(R.v[d][0][0]),
+                         fp8x2_to_bf16x2<false>(R.v[d][1][0]), fp8x2_to_bf16x2<true>(R.v[d][1][0]));
         }
+        o[d] = mma_s(va, pb, o[d]);
       }
     }
   }
@@ -451,7 +466,7 @@ __device__ __forceinline__ void load_step(const DecodeArgs& a, const StreamGeo& 
     }
   }
   const int U = lc.j * kUnit;
-  load_unit<KV, D, BS>(R, lv, unit_blocks<BS>(lv, U), U, i, kg);
+  load_unit<KV, D, BS>(R, lv, unit_blocks<BS>(lv, U), i, kg);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -504,7 +519,7 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
   SeqView lv = seq_view<KV, D, BS>(a, lc.seq, geo.x + a.streams * lc.hh);
   load_q<KV, D, G>(st.qb, a, cc.seq, geo.x + a.streams * cc.hh, i, kg);
   UnitRegs<KV, D> R;
-  load_unit<KV, D, BS>(R, lv, unit_blocks<BS>(lv, lc.j * kUnit), lc.j * kUnit, i, kg);
+  load_unit<KV, D, BS>(R, lv, unit_blocks<BS>(lv, lc.j * kUnit), i, kg);
 
 #pragma unroll 1
   for (int p = r0; p < r1;) {
