@@ -12,8 +12,9 @@
 //    the G query heads that share the KV head, so one K/V tile in LDS serves every head of the group;
 //    each wave owns 32 rows;
 //  * key tiles of 64 positions are gathered through the block table and stored in LDS as bf16 (fp8
-//    e4m3 codes convert exactly; scales stay in fp32), double-buffered so that the next tile's global
-//    loads are in flight during the current tile's MFMAs.  Every load instruction of a wave reads
+//    e4m3 codes convert exactly; scales stay in fp32), double-buffered in LDS and in registers: the
+//    loads of tile t + 2 are issued while tile t is computed, so each has two iterations to arrive
+//    (the kernel is bound by that latency, not by its MFMAs, when a load has only one).  Every load instruction of a wave reads
 //    inside one pool block, so the table entries are wave-uniform scalar loads, and every load is
 //    issued unconditionally, so that the only wait for them is the one before the LDS store.  K
 //    tiles are stored [key][dim]; the V pool's dim-major tiles give [dim][key] rows directly, so V
@@ -49,7 +50,6 @@ constexpr int kKStride = kD * 2 + 16;    // bytes per K row in LDS (the padding 
 constexpr int kVStride = kKT * 2 + 16;   // bytes per V^T row in LDS
 constexpr int kKBytes = kKT * kKStride;
 constexpr int kVBytes = kD * kVStride;
-constexpr int kBufBytes = kKBytes + kVBytes;
 constexpr float kRescaleSlack = 8.0f;    // log2 of the largest unrescaled growth
 constexpr int kMaxRanked = 64;           // sequences ordered by length when there are at most this many
 
@@ -79,12 +79,12 @@ struct TileLoader {
   uint4 k[kKU];
   uint32_t v[kVU][kVW];
 
-  // Tile keys [key0, key0 + 64).  Every load is issued unconditionally, so that the only wait for
-  // them is the one before store(); a block past the last one holding a key < n_keys is read as
-  // that last block (its keys are masked: scores by the causal mask, values zeroed in store()).
-  __device__ __forceinline__ void load(const char* kpool, const char* vpool, const int32_t* tab,
-                                       int64_t blk_stride, int64_t head_off, int key0, int n_keys,
-                                       int wave, int lane) {
+  // K or V of tile keys [key0, key0 + 64).  Every load is issued unconditionally, so that the only
+  // wait for them is the one before the matching store; a block past the last one holding a key
+  // < n_keys is read as that last block (its keys are masked: scores by the causal mask, values
+  // zeroed in store_v()).
+  __device__ __forceinline__ void load_k(const char* kpool, const int32_t* tab, int64_t blk_stride, int64_t head_off,
+                                         int key0, int n_keys, int wave, int lane) {
     const int jlast = (n_keys - 1) / BS;
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
@@ -96,6 +96,11 @@ struct TileLoader {
       k[u] = *reinterpret_cast<const uint4*>(kpool + phys * blk_stride + head_off +
                                              static_cast<int64_t>(key % BS) * kRowBytes + ch * 16);
     }
+  }
+
+  __device__ __forceinline__ void load_v(const char* vpool, const int32_t* tab, int64_t blk_stride, int64_t head_off,
+                                         int key0, int n_keys, int wave, int lane) {
+    const int jlast = (n_keys - 1) / BS;
 #pragma unroll
     for (int u = 0; u < kVU; ++u) {
       const int g16 = 2 * u + (wave >> 1);              // 16-key group of the tile
@@ -128,11 +133,8 @@ struct TileLoader {
     }
   }
 
-  // Widen to bf16 and write the tile to LDS.  Values of keys >= n_keys may hold any bits (even
-  // NaN, or another block's data): they are zeroed so that 0 * v stays 0.
-  __device__ __forceinline__ void store(char* buf, int key0, int n_keys, int wave, int lane) {
-    char* ks = buf;
-    char* vt = buf + kKBytes;
+  // K rows widened to bf16, [key][dim] with stride kKStride.
+  __device__ __forceinline__ void store_k(char* ks, int wave, int lane) const {
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
       const int id = u * kThreads + 64 * wave + lane;
@@ -148,6 +150,11 @@ struct TileLoader {
             make_uint4(fp8x2_lo(c.z), fp8x2_hi(c.z), fp8x2_lo(c.w), fp8x2_hi(c.w));
       }
     }
+  }
+
+  // V^T rows widened to bf16, [dim][key position] with stride kVStride.  Values of keys >= n_keys
+  // may hold any bits (even NaN, or another block's data): they are zeroed so that 0 * v stays 0.
+  __device__ __forceinline__ void store_v(char* vt, int key0, int n_keys, int wave, int lane) {
 #pragma unroll
     for (int u = 0; u < kVU; ++u) {
       const int g16 = 2 * u + (wave >> 1);
@@ -200,7 +207,7 @@ template <int KV, int BS, int G>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int out_bf16, int num_qtiles,
                                                               int xcd_remap) {
   constexpr int QT = kRows / G;      // queries per workgroup
-  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+  __shared__ __attribute__((aligned(16))) char smem[2 * (kKBytes + kVBytes)];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -270,15 +277,32 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   float l_run = 0.f;
   const float c2 = a.qk_scale;
 
-  TileLoader<KV, BS> ld;
-  ld.load(kpool, vpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
-  ld.store(smem, 0, n_keys, wave, lane);
+  // LDS: K and V^T of two tiles (double buffer).  Two register stages: the loads of tile t + 2 are
+  // issued while tile t is computed, and tile t + 1 (loaded one iteration earlier) is stored to LDS
+  // at the end of iteration t, so every load has two iterations to arrive.
+  char* const kbuf0 = smem;
+  char* const kbuf1 = smem + kKBytes;
+  char* const vbuf0 = smem + 2 * kKBytes;
+  char* const vbuf1 = smem + 2 * kKBytes + kVBytes;
+
+  TileLoader<KV, BS> la, lb;
+  la.load_k(kpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+  la.load_v(vpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+  la.store_k(kbuf0, wave, lane);
+  la.store_v(vbuf0, 0, n_keys, wave, lane);
+  la.load_k(kpool, tab, blk_stride, head_off, min(1, n_tiles - 1) * kKT, n_keys, wave, lane);
+  la.load_v(vpool, tab, blk_stride, head_off, min(1, n_tiles - 1) * kKT, n_keys, wave, lane);
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    char* buf = smem + (t & 1) * kBufBytes;
-    // the last iteration re-reads its own tile (unused), so that the load is unconditional
-    ld.load(kpool, vpool, tab, blk_stride, head_off, min(t + 1, n_tiles - 1) * kKT, n_keys, wave, lane);
+  // Iteration t: loads tile t + 2 into ld_ld, computes tile t, stores tile t + 1 from st_ld.  Loads
+  // past the last tile re-read it (unused), so that they are unconditional.
+  auto iteration = [&](TileLoader<KV, BS>& st_ld, TileLoader<KV, BS>& ld_ld, int t) {
+    const bool odd = t & 1;
+    const int t2 = min(t + 2, n_tiles - 1) * kKT;
+    ld_ld.load_k(kpool, tab, blk_stride, head_off, t2, n_keys, wave, lane);
+    ld_ld.load_v(vpool, tab, blk_stride, head_off, t2, n_keys, wave, lane);
+    const char* kb = odd ? kbuf1 : kbuf0;
+    const char* vb = odd ? vbuf1 : vbuf0;
 
     // ---- S^T = K Q^T for two 32-key halves ----
     f32x16 s[2];
@@ -286,7 +310,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
     for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-      const char* krow = buf + (sb * 32 + (lane & 31)) * kKStride + 16 * h;
+      const char* krow = kb + (sb * 32 + (lane & 31)) * kKStride + 16 * h;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 32 * c);
@@ -338,19 +362,31 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
       }
     l_run += lsum + shfl_xor(lsum, 32);
 
-    // ---- O^T += V^T P^T ----
+    // ---- O^T += V^T P^T, side by side with widening and storing the next tile ----
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const char* vrow = buf + kKBytes + (dt * 32 + (lane & 31)) * kVStride + 16 * h;
+      const char* vrow = vb + (dt * 32 + (lane & 31)) * kVStride + 16 * h;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + 32 * c);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], o[dt], 0, 0, 0);
       }
     }
-
-    if (t + 1 < n_tiles) ld.store(smem + ((t + 1) & 1) * kBufBytes, (t + 1) * kKT, n_keys, wave, lane);
+    st_ld.store_k(odd ? kbuf0 : kbuf1, wave, lane);
+    st_ld.store_v(odd ? vbuf0 : vbuf1, min(t + 1, n_tiles - 1) * kKT, n_keys, wave, lane);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read (V fragment)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU (widening)
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
+    }
     __syncthreads();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    iteration(la, lb, t);
+    if (t + 1 >= n_tiles) break;
+    iteration(lb, la, t + 1);
   }
 
   // ---- out[token][head][d] = O^T[d][row] / l ----
