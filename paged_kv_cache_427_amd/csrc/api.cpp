@@ -70,8 +70,6 @@ int64_t decode_max_parts(int32_t max_ctx, int32_t part) {
   return (static_cast<int64_t>(max_ctx) + part - 1) / part;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
 }  // namespace
 
 pa_status pa_fail(pa_status st, const char* msg) {
@@ -193,9 +191,9 @@ pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const vo
   if (!q || !k_pool || !v_pool || !tables || !lens || !out)
     return pa_fail(PA_ERR_INVALID, "pa_decode: null pointer");
   // stream positions (KV heads x 32-key units of all sequences) must fit in 31 bits
-  if (static_cast<int64_t>(pool->num_kv_heads) * num_seqs * ((static_cast<int64_t>(max_context_len) + 15) / 16) >=
+  if (static_cast<int64_t>(pool->num_kv_heads) * num_seqs * ((static_cast<int64_t>(max_context_len) + 31) / 32) >=
       (int64_t(1) << 31))
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 2^31 16-key units of K/V in one call");
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 2^31 32-key units of K/V in one call");
   const int32_t part = decode_partition(max_context_len, partition_size);
   const int64_t mp = decode_max_parts(max_context_len, part);
   if (mp > (int64_t(1) << 30)) return pa_fail(PA_ERR_INVALID, "pa_decode: too many partitions");
@@ -220,9 +218,7 @@ pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const vo
   a.part_tokens = part;
   a.max_parts = static_cast<int32_t>(mp);
   a.max_ctx = max_context_len;
-  char* w = static_cast<char*>(workspace);
-  a.ws_pref = reinterpret_cast<int32_t*>(w);
-  a.ws_part = reinterpret_cast<float*>(w + align256((static_cast<size_t>(num_seqs) + 1) * 4));
+  pa::decode_workspace_carve(a, workspace);
   a.out = out;
   return launch_status(pa::launch_decode(a, pool->dtype, q_dtype, out_dtype, pool->block_size,
                                          pool->head_dim, stream),

@@ -6,33 +6,36 @@
 // costs a little.  softmax(scale * q K^T) V is the textbook form of what the pages describe in words.
 //
 // Design (HBM-bound: at most 8 flop per byte of K/V, far below the MI355X ridge, so the goal is to
-// keep the vector ALUs out of the way of the loads):
-//  * a work item is one context partition of one KV head, for all G query heads of that group, so
-//    each K/V byte is read once; a persistent grid of workgroups (4 wave64s each, as many as are
-//    resident at once) loops over the items.  Items are numbered so that all work of one KV head
-//    lands on one XCD (initial dispatch is round-robin over the 8 XCDs): blocks shared by many
-//    sequences (a common prefix) are then re-read from that XCD's L2, not from HBM.
-//  * a wave takes 16-key units of the partition round-robin; the unit's table entry is a
-//    wave-uniform scalar load.  Both products of a unit run on 16x16 MFMA tiles fed straight from
-//    the loads, with no LDS staging:
-//      S^T[key][head] = K[key][:] . Q[head][:]     A = K rows (token-major tile), B = Q^T
+// keep HBM busy and the vector ALUs out of the way of the loads):
+//  * three launches: a one-workgroup plan kernel (per-sequence unit counts as a prefix sum, the
+//    share schedule and its table of start cursors), the stream kernel, and a merge kernel.
+//  * a unit is 32 keys of one (sequence, KV head) segment, for all G query heads of the group, so
+//    each K/V byte is read once.  The units of all segments form one stream per XCD (KV head h in
+//    stream h % 8; initial dispatch is round-robin over the 8 XCDs), so blocks shared by many
+//    sequences -- a common prefix -- are re-read from that XCD's L2, not from HBM.
+//  * a persistent grid of wave64s (as many as are resident) walks the streams; each wave takes one
+//    contiguous share of its stream, so every wave does the same number of units and the K/V of a
+//    segment is read in order.  The unit's physical blocks come from wave-uniform scalar reads of
+//    the block table: one lookup per block, prepared one unit ahead so they overlap the loads.
+//  * both products of a unit run on 16x16 MFMA tiles fed straight from the loads, no LDS staging:
+//      S^T[key][head] = K[key][:] . Q[head][:]       A = K rows (token-major tile), B = Q^T
 //      O^T[dim][head] += V^T[dim][key] P^T[key][head]   A = V^T rows (dim-major tile), B = P^T
-//    The G query heads occupy columns 0..G-1 of the 16 (the rest are zero).  The S^T accumulator
-//    layout -- lane l holds keys 4*(l/16)+r of the unit for head l%16 -- is, after rounding to bf16,
-//    exactly the B operand of the 16x16x16 P.V product, so the scores never cross lanes.
-//  * bf16 pools use v_mfma_f32_16x16x32_bf16 (S) and v_mfma_f32_16x16x16_bf16 (P.V); fp8 codes
-//    widen exactly to bf16 first (v_cvt_scalef32_pk_bf16_fp8, scales kept in fp32); fp32 pools use
-//    v_mfma_f32_16x16x4_f32.  The
-//    probabilities are rounded to bf16 for the bf16/fp8 products and the running sum uses the same
-//    rounded values; the fp32 path keeps fp32 probabilities.
+//    The G query heads occupy columns 0..G-1 of the 16.  The S^T accumulator layout -- lane l holds
+//    keys 4*(l/16)+r of each 16-key tile for head l%16 -- is, after rounding to bf16, exactly the B
+//    operand of the 16x16x32 P.V product over the unit's 32 keys, so the scores never cross lanes.
+//  * bf16 pools use v_mfma_f32_16x16x32_bf16 for both products; fp8 codes widen exactly to bf16
+//    first (v_cvt_scalef32_pk_bf16_fp8, scales kept in fp32); fp32 pools use
+//    v_mfma_f32_16x16x4_f32.  The probabilities are rounded to bf16 for the bf16/fp8 products and
+//    the running sum uses the same rounded values; the fp32 path keeps fp32 probabilities.
 //  * base-2 online softmax with one running max per head.  The max is raised only when a logit
 //    exceeds it by more than 2^8 (so every exp stays <= 256); that test is one wave-wide ballot, and
-//    only then are the lanes' maxima exchanged and the accumulators rescaled.  Each lane keeps a
-//    partial exp-sum of its own keys; lanes, then waves (through LDS), merge once per partition.
-//  * a ring of register stages keeps the next units' K/V in flight while one is consumed (2 for
-//    bf16, 4 for fp8), within a register budget that leaves 3 workgroups per CU.
-//  * a sequence with several partitions writes (max, sum, normalised partial) per partition and a
-//    second kernel merges them; a single-partition sequence writes its output directly.
+//    only then are the lanes' maxima exchanged and the accumulators rescaled.
+//  * one unit of K/V is in flight per wave while the previous one is consumed (three workgroups of
+//    four waves per CU for bf16/fp8).
+//  * a piece is a wave's run of units inside one partition of one segment.  A piece that is a whole
+//    segment writes the output directly; any other piece writes (max, sum, unnormalised partial
+//    output) to its own slot, and the merge kernel combines the pieces of each (sequence, head).
+
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -87,6 +90,13 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float x, bool bf
     static_cast<float*>(out)[i] = x;
 }
 
+// Integer inputs that no kernel of a decode launch writes while it runs (tables, lengths, the
+// plan), read through the constant address space: the compiler keeps uniform reads of them on the
+// scalar unit even where the kernel also stores or counts atomically, so they never wait behind the
+// K/V loads in flight.
+typedef const int32_t __attribute__((address_space(4)))* ro_i32;
+__device__ __forceinline__ ro_i32 ro(const int32_t* p) { return (ro_i32)p; }
+
 // Raw registers of one 32-key unit, as loaded by one lane (i = lane % 16, kg = lane / 16).
 //  k[t][c]: key 16t + i of the unit, 16 bytes at byte 64c + 16kg of its row
 //           (bf16: dims 32c+8kg..+8; fp8: dims 64c+16kg..+16; fp32: dims 16c+4kg..+4)
@@ -117,7 +127,7 @@ __device__ __forceinline__ void load_piece(uint32_t (&dst)[VW], const char* p) {
 struct SeqView {
   const char* kbase;       // K pool + this KV head's tile offset
   const char* vbase;
-  const int32_t* tab;      // this sequence's block table
+  ro_i32 tab;              // this sequence's block table
   int64_t blk_stride;      // bytes of one block of one pool (all KV heads)
   int nblk;                // valid table entries: ceil(L / BS)
 };
@@ -128,7 +138,7 @@ struct SeqView {
 template <int BS>
 struct UnitBlocks {
   static constexpr int N = kUnit / BS;
-  int64_t b[N];
+  int32_t b[N];   // physical block ids
 };
 
 template <int BS>
@@ -178,7 +188,6 @@ template <int KV, int D, int G>
 struct DecodeState {
   static constexpr int NQB = KV == kF32 ? D / 4 : D / 32;   // MFMAs per 16-key S^T tile
   typedef typename std::conditional<KV == kF32, float, bf16x8>::type QOp;
-  QOp qb[NQB];         // Q^T operand of each S^T MFMA (zero for columns >= G)
   f32x4 o[D / 16];     // O^T: lane holds dims 16t + 4kg + r for head lane % 16
   float m;             // running max (base-2 logits) of head lane % 16; equal across the 4 lane groups
   float l;             // this lane's partial exp-sum
@@ -190,7 +199,9 @@ struct DecodeState {
     l = 0.f;
   }
 
-  __device__ __forceinline__ void consume(UnitRegs<KV, D>& R, int U, int t1, int kg, int col,
+  // qb: the Q^T operand of each S^T MFMA (column i holds query head min(i, G - 1) of the group;
+  // columns >= G are computed and never used).
+  __device__ __forceinline__ void consume(UnitRegs<KV, D>& R, const QOp (&qb)[NQB], int U, int t1, int kg, int col,
                                           float qk_scale) {
     using R_t = UnitRegs<KV, D>;
     constexpr int KL = R_t::KL;
@@ -298,14 +309,52 @@ struct DecodeState {
 };
 
 // A length outside [0, max_ctx] is clamped so that table, workspace and output stay in bounds.
-__device__ __forceinline__ int clamped_len(const DecodeArgs& a, int seq) { return min(max(a.lens[seq], 0), a.max_ctx); }
+__device__ __forceinline__ int clamped_len(const DecodeArgs& a, int seq) { return min(max(ro(a.lens)[seq], 0), a.max_ctx); }
 
-// ---- work plan: units (16 keys) of every sequence, as a prefix sum --------------------------------
+// ---- work plan ---------------------------------------------------------------------------------
+// The units (32 keys) of every (KV head, sequence) segment form one stream per XCD, in the order
+// (head slot, sequence, unit).  Each wave of a stream takes one contiguous static share of
+// kStaticPct % of the stream / waves positions; the rest is handed out in shares of at least
+// kMinShare units from a counter to the waves that finish first.  (Measured on MI355X: any larger
+// dynamic part is slower -- each extra share costs the wave a cold start on a new segment's table
+// entries and Q and adds a partial record -- so the static part is the whole stream but the
+// remainder of the division, fewer positions than waves.)  Share v covers [start(v), start(v + 1)):
+//   start(v) = v * S0                       for v <  W0  (W0 = waves of the stream, or 0 if S0 = 0)
+//   start(v) = W0 * S0 + (v - W0) * S1      for v >= W0
+// All streams have the same shape (the same sequences, num_kv_heads / streams heads each), so one
+// table of share start cursors serves them all.
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanLds = 8192;        // prefix entries searched in LDS (larger batches search global memory)
+constexpr int kStaticPct = 100;       // part of a stream taken in static shares
+constexpr int kMinShare = 4;          // units per dynamic share, at least
+constexpr int kDynPerWave = 1;        // dynamic shares per wave of the stream, at most
+constexpr int kSharesPerWave = 1 + kDynPerWave;
+constexpr int kCtrStride = 32;        // ints between two counters (one per 128-byte line)
+constexpr int kSchedInts = kCtrStride * 10;
+// schedule header: [0] S0, [1] S1, [2] W0, [3] V; counter of stream x at [kCtrStride * (x + 1)]
 
-// One workgroup: pref[s] = sum over sequences s' < s of ceil(L_s' / 16).
+struct Sched {
+  int S0, S1, W0, V;
+  __device__ __forceinline__ int start(int v) const { return v < W0 ? v * S0 : W0 * S0 + (v - W0) * S1; }
+  __device__ __forceinline__ int share_of(int p) const { return p < W0 * S0 ? p / S0 : W0 + (p - W0 * S0) / S1; }
+};
+
+// Largest s with pref[s] <= r (then pref[s + 1] > r: sequence s holds unit r of its head slot).
+template <typename P>
+__device__ __forceinline__ int find_seq(const P& pref, int n, int r) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pref[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One workgroup: pref[s] = sum over sequences s' < s of ceil(L_s' / 32); the schedule header; the
+// start cursor (head slot, sequence, unit, units of the sequence) of every share; zeroed counters.
 __global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(DecodeArgs a) {
   __shared__ int csum[kPlanThreads];
+  __shared__ int spref[kPlanLds];
   const int n = a.num_seqs;
   const int tid = threadIdx.x;
   const int chunk = (n + kPlanThreads - 1) / kPlanThreads;
@@ -320,11 +369,48 @@ __global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(DecodeArgs a)
     csum[tid] += v;
     __syncthreads();
   }
+  const bool in_lds = n + 1 <= kPlanLds;
   int run = csum[tid] - local;
-  if (tid == 0) a.ws_pref[0] = 0;
+  if (tid == 0) {
+    a.ws_pref[0] = 0;
+    if (in_lds) spref[0] = 0;
+  }
   for (int s = s0; s < s1; ++s) {
     run += (clamped_len(a, s) + kUnit - 1) / kUnit;
     a.ws_pref[s + 1] = run;
+    if (in_lds) spref[s + 1] = run;
+  }
+  const int useq = csum[kPlanThreads - 1];
+  const int total = (a.num_kv_heads / a.streams) * useq;
+  const int W = a.stream_waves;
+  Sched sc;
+  sc.S0 = static_cast<int>(static_cast<int64_t>(total) * kStaticPct / 100 / W);
+  sc.W0 = sc.S0 > 0 ? W : 0;
+  const int rest = total - sc.W0 * sc.S0;
+  sc.S1 = max(kMinShare, (rest + kDynPerWave * W - 1) / (kDynPerWave * W));
+  sc.V = sc.W0 + (rest + sc.S1 - 1) / sc.S1;
+  if (tid == 0) {
+    a.ws_sched[0] = sc.S0;
+    a.ws_sched[1] = sc.S1;
+    a.ws_sched[2] = sc.W0;
+    a.ws_sched[3] = sc.V;
+  }
+  if (tid < 8) a.ws_sched[kCtrStride * (tid + 1)] = 0;
+  __syncthreads();   // the prefix written above is read back by other threads of this workgroup
+  for (int v = tid; v < sc.V; v += kPlanThreads) {
+    const int p = sc.start(v);
+    const int hh = p / useq, rem = p - hh * useq;
+    int seq, base, next;
+    if (in_lds) {
+      seq = find_seq(spref, n, rem);
+      base = spref[seq];
+      next = spref[seq + 1];
+    } else {
+      seq = find_seq(a.ws_pref, n, rem);
+      base = a.ws_pref[seq];
+      next = a.ws_pref[seq + 1];
+    }
+    *reinterpret_cast<int4*>(a.ws_share + 4 * v) = make_int4(hh, seq, rem - base, next - base);
   }
 }
 
@@ -334,24 +420,8 @@ struct Cursor {
   int hh, seq, j, nj;
 };
 
-// The cursor at stream position r (the sequence holding unit r % useq of KV head slot r / useq).
-__device__ __forceinline__ Cursor locate(const int32_t* pref, int n, int useq, int r) {
-  Cursor c;
-  c.hh = r / useq;
-  const int rem = r - c.hh * useq;
-  int lo = 0, hi = n - 1;                 // largest s with pref[s] <= rem; then pref[s + 1] > rem
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pref[mid] <= rem) lo = mid; else hi = mid - 1;
-  }
-  c.seq = lo;
-  c.j = rem - pref[lo];
-  c.nj = pref[lo + 1] - pref[lo];
-  return c;
-}
-
 // Next stream position (sequences without units are skipped).  Only called while a next position exists.
-__device__ __forceinline__ void advance(Cursor& c, const int32_t* pref, int n) {
+__device__ __forceinline__ void advance(Cursor& c, ro_i32 pref, int n) {
   if (++c.j < c.nj) return;
   c.j = 0;
   do {
@@ -369,24 +439,24 @@ __device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int seq, int kv
   SeqView sv;
   sv.kbase = static_cast<const char*>(a.k_pool) + static_cast<int64_t>(kvh) * TILE;
   sv.vbase = static_cast<const char*>(a.v_pool) + static_cast<int64_t>(kvh) * TILE;
-  sv.tab = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+  sv.tab = ro(a.tables) + static_cast<int64_t>(seq) * a.max_blocks;
   sv.blk_stride = static_cast<int64_t>(a.num_kv_heads) * TILE;
   sv.nblk = (clamped_len(a, seq) + BS - 1) / BS;
   return sv;
 }
 
-// Q^T operands of (seq, KV head): column i holds query head kvh*G + i (zeros for i >= G); the k-slots
-// of lane group kg follow the dims of its K loads.
+// Q^T operands of (seq, KV head): column i holds query head kvh*G + min(i, G - 1), so that every
+// lane loads a real row (the columns >= G are never used); the k-slots of lane group kg follow the
+// dims of its K loads.
 template <int KV, int D, int G, typename QArr>
 __device__ __forceinline__ void load_q(QArr& qb, const DecodeArgs& a, int seq, int kvh, int i, int kg) {
   using QT = typename std::conditional<KV == kF32, float, uint16_t>::type;
-  const bool live = i < G;
   const QT* qrow = static_cast<const QT*>(a.q) +
-                   (static_cast<int64_t>(seq) * a.num_q_heads + kvh * G + (live ? i : 0)) * D;
+                   (static_cast<int64_t>(seq) * a.num_q_heads + kvh * G + min(i, G - 1)) * D;
   if constexpr (KV == kF32) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const float4 w = live ? *reinterpret_cast<const float4*>(qrow + 16 * c + 4 * kg) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 w = *reinterpret_cast<const float4*>(qrow + 16 * c + 4 * kg);
       qb[4 * c] = w.x; qb[4 * c + 1] = w.y; qb[4 * c + 2] = w.z; qb[4 * c + 3] = w.w;
     }
   } else {
@@ -397,35 +467,26 @@ __device__ __forceinline__ void load_q(QArr& qb, const DecodeArgs& a, int seq, i
 #pragma unroll
       for (int h = 0; h < SUB; ++h) {
         const int d0 = DPC * c + (DPC / 4) * kg + 8 * h;
-        const uint4 w = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
-        qb[SUB * c + h] = __builtin_bit_cast(bf16x8, w);
+        qb[SUB * c + h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + d0));
       }
   }
 }
 
-// Streams and slots.  Stream x holds the KV heads h with h % streams == x, head slot hh = h / streams;
-// its positions are hh * useq + pref[seq] + j.  A piece is a maximal run of one wave's positions
-// inside one partition of one segment; it is written to slot
-//   (hh * num_seqs + seq) * max_parts + partition + (wave index in the stream)
-// which is unique: along a stream, later pieces have a larger (segment, partition) term and a wave
-// index at least as large.
-struct StreamGeo {
-  int x, nh, useq, wi;
-  int64_t share;
-};
-
-// Writes the piece [j0, j0 + np) of segment (c.hh, c.seq): the final output when the piece is the
-// whole segment, else its partial record.
+// Pieces and slots.  A piece is a maximal run of one share's positions inside one partition of one
+// segment; a piece that is not a whole segment is written to slot
+//   x * stream_slots + (hh * num_seqs + seq) * max_parts + partition + share
+// which is unique: along a stream both terms are non-decreasing from one piece to the next, and one
+// of them grows.
 template <int KV, int D, int G>
-__device__ __forceinline__ void finish_piece(const DecodeArgs& a, int out_bf16, const StreamGeo& geo,
-                                             DecodeState<KV, D, G>& st, const Cursor& c, int j0, int np, int PU,
+__device__ __forceinline__ void finish_piece(const DecodeArgs& a, int out_bf16, int x, int share,
+                                             DecodeState<KV, D, G>& st, const Cursor& c, int np, int PU,
                                              int i, int kg) {
   float l = st.l;
   l += shfl_xor(l, 16);
   l += shfl_xor(l, 32);
-  const int kvh = geo.x + a.streams * c.hh;
+  const int kvh = x + a.streams * c.hh;
   if (i >= G) return;
-  if (j0 == 0 && np == c.nj) {
+  if (c.j == 0 && np == c.nj) {
     const float inv = l > 0.f ? a.v_scale / l : 0.f;
     const int64_t base = (static_cast<int64_t>(c.seq) * a.num_q_heads + kvh * G + i) * D;
 #pragma unroll
@@ -440,8 +501,8 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs& a, int out_bf16, 
       }
     }
   } else {
-    const int64_t slot = geo.x * a.stream_slots +
-                         (static_cast<int64_t>(c.hh) * a.num_seqs + c.seq) * a.max_parts + j0 / PU + geo.wi;
+    const int64_t slot = x * a.stream_slots +
+                         (static_cast<int64_t>(c.hh) * a.num_seqs + c.seq) * a.max_parts + c.j / PU + share;
     float* rec = a.ws_part + (slot * G + i) * (D + 4);
     if (kg == 0) *reinterpret_cast<float4*>(rec) = make_float4(st.m, l, 0.f, 0.f);
 #pragma unroll
@@ -450,45 +511,90 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs& a, int out_bf16, 
   }
 }
 
-// Moves the load cursor to the next stream position and issues that unit's loads into R (at the
-// wave's last position it reloads that unit, unused); entering a new segment also loads the
-// segment's Q operands into qnext.
-template <int KV, int D, int BS, int G, typename QArr>
-__device__ __forceinline__ void load_step(const DecodeArgs& a, const StreamGeo& geo, UnitRegs<KV, D>& R, Cursor& lc,
-                                          SeqView& lv, int& lpos, int last, QArr& qnext, int i, int kg) {
-  if (lpos < last) {
-    ++lpos;
-    advance(lc, a.ws_pref, a.num_seqs);
-    if (lc.j == 0) {
-      const int kvh = geo.x + a.streams * lc.hh;
-      lv = seq_view<KV, D, BS>(a, lc.seq, kvh);
-      load_q<KV, D, G>(qnext, a, lc.seq, kvh, i, kg);
-    }
+// A stream position prepared for loading: its cursor, the view of its segment, its blocks, its
+// share (and the wave's following share), and whether it enters a segment or a share (its Q must be
+// loaded with it).  `live` is false once the wave has no position left: the position then stays on
+// the wave's last unit, which is loaded again (in bounds, unused).
+template <int BS>
+struct Pos {
+  Cursor c;
+  SeqView v;
+  UnitBlocks<BS> ub;
+  int pos, end, share, next;
+  bool enter, live;
+};
+
+// Asks the stream's counter for one more share: lane 0 adds 1 (device scope) and gets the old value.
+// The per-lane address keeps the add a single plain one (no wave-wide rewrite that would read the
+// answer at once).
+__device__ __forceinline__ int grab_share(int32_t* ctr, int lane) {
+  int got = 0;
+  if (lane == 0) {
+    int32_t __attribute__((address_space(1)))* p = (int32_t __attribute__((address_space(1)))*)ctr;
+    asm volatile("" : "+v"(p));
+    got = __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  const int U = lc.j * kUnit;
-  load_unit<KV, D, BS>(R, lv, unit_blocks<BS>(lv, U), i, kg);
+  return got;
+}
+
+// Points P at the first unit of share v (the plan table holds its start cursor).
+template <int KV, int D, int BS>
+__device__ __forceinline__ void enter_share(const DecodeArgs& a, int x, int total, const Sched& sc, Pos<BS>& P, int v) {
+  const ro_i32 e = ro(a.ws_share) + 4 * v;
+  P.c.hh = e[0];
+  P.c.seq = e[1];
+  P.c.j = e[2];
+  P.c.nj = e[3];
+  P.share = v;
+  P.pos = sc.start(v);
+  P.end = min(total, sc.start(v + 1));
+  P.v = seq_view<KV, D, BS>(a, P.c.seq, x + a.streams * P.c.hh);
+  P.enter = true;
+}
+
+// Moves P to the wave's next position -- the next unit of the share, else the first unit of the
+// wave's next share, which is asked for here -- and reads that position's block-table entries.  It
+// runs right after the loads of the current position are issued, so these dependent scalar reads
+// overlap the loads in flight instead of delaying the next issue.
+template <int KV, int D, int BS>
+__device__ __forceinline__ void prepare_next(const DecodeArgs& a, int x, int total, const Sched& sc, int32_t* ctr,
+                                             Pos<BS>& P, int lane) {
+  P.enter = false;
+  if (P.pos + 1 < P.end) {
+    ++P.pos;
+    advance(P.c, ro(a.ws_pref), a.num_seqs);
+    if (P.c.j == 0) {
+      P.v = seq_view<KV, D, BS>(a, P.c.seq, x + a.streams * P.c.hh);
+      P.enter = true;
+    }
+    P.ub = unit_blocks<BS>(P.v, P.c.j * kUnit);
+  } else if (P.next < sc.V) {
+    enter_share<KV, D, BS>(a, x, total, sc, P, P.next);
+    const int got = grab_share(ctr, lane);
+    P.ub = unit_blocks<BS>(P.v, P.c.j * kUnit);
+    __builtin_amdgcn_sched_barrier(0);
+    P.next = a.stream_waves + __builtin_amdgcn_readfirstlane(got);   // after the table reads are issued
+  } else {
+    P.live = false;
+  }
+}
+
+// Issues the loads of the prepared position P into R (and its segment's Q into qnext when P enters
+// a segment or a share: the only write of qnext, which the consumes of earlier units no longer need).
+template <int KV, int D, int BS, int G, typename QArr>
+__device__ __forceinline__ void issue(const DecodeArgs& a, int x, const Pos<BS>& P, UnitRegs<KV, D>& R, QArr& qnext,
+                                      int i, int kg) {
+  if (P.enter) load_q<KV, D, G>(qnext, a, P.c.seq, x + a.streams * P.c.hh, i, kg);
+  load_unit<KV, D, BS>(R, P.v, P.ub, i, kg);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Consumes the np units of one piece (keys from U0 on); R holds the first of them on entry and the
-// unit after the piece on exit: each consume is followed by the loads of the next stream position.
-template <int KV, int D, int BS, int G, typename QArr>
-__device__ __forceinline__ void run_piece(const DecodeArgs& a, const StreamGeo& geo, DecodeState<KV, D, G>& st,
-                                          UnitRegs<KV, D>& R, Cursor& lc, SeqView& lv, int& lpos, int last,
-                                          QArr& qnext, int U0, int L, int np, int i, int kg) {
-#pragma unroll 1
-  for (int q = 0; q < np; ++q) {
-    st.consume(R, U0 + kUnit * q, L, kg, i, a.qk_scale);
-    load_step<KV, D, BS, G>(a, geo, R, lc, lv, lpos, last, qnext, i, kg);
-  }
-}
-
-// Persistent grid of waves over the unit streams.  Every wave takes an equal contiguous share of its
-// stream (so the work is balanced to one unit) and runs one register ring across the segments of
-// its share, with the next segment's Q and table entries fetched while the current one is consumed:
-// no wave ever waits for a fresh start.  With streams == 8 the KV heads of stream x are served by
-// the workgroups on XCD x (initial dispatch is round-robin over the 8 XCDs), so blocks shared by many
-// sequences (a common prefix) are re-read from that XCD's L2, not from HBM.
+// Persistent grid of waves over the unit streams.  A wave starts on the share of its own index and
+// then takes the stream's next untaken share until none is left; one register ring runs across all
+// its shares and segments: each consume is followed by the loads of the next position, and the
+// position after that is prepared while those loads are in flight.  With streams == 8 the KV heads
+// of stream x are served by the workgroups on XCD x (initial dispatch is round-robin over the 8
+// XCDs), so blocks shared by many sequences (a common prefix) are re-read from that XCD's L2.
 template <int KV, int D, int BS, int G>
 __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_kernel(DecodeArgs a, int out_bf16) {
   using St = DecodeState<KV, D, G>;
@@ -496,55 +602,61 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15;         // row of an MFMA operand / column (head) of an accumulator
   const int kg = lane >> 4;        // k-group of an operand / row group of an accumulator
-  const int n = a.num_seqs;
-  const int32_t* pref = a.ws_pref;
-
-  StreamGeo geo;
-  geo.x = blockIdx.x % a.streams;
-  geo.nh = a.num_kv_heads / a.streams;
-  geo.useq = pref[n];
-  geo.wi = (blockIdx.x / a.streams) * kWaves + wave;
-  const int total = geo.nh * geo.useq;
-  geo.share = (static_cast<int64_t>(total) + a.stream_waves - 1) / a.stream_waves;
-  const int r0 = static_cast<int>(min(static_cast<int64_t>(total), geo.wi * geo.share));
-  const int r1 = static_cast<int>(min(static_cast<int64_t>(total), (geo.wi + 1) * geo.share));
-  if (r0 >= r1) return;
+  const int x = blockIdx.x % a.streams;
+  const int wi = (blockIdx.x / a.streams) * kWaves + wave;
+  Sched sc;
+  sc.S0 = ro(a.ws_sched)[0];
+  sc.S1 = ro(a.ws_sched)[1];
+  sc.W0 = ro(a.ws_sched)[2];
+  sc.V = ro(a.ws_sched)[3];
+  if (wi >= sc.V) return;
+  const int total = (a.num_kv_heads / a.streams) * ro(a.ws_pref)[a.num_seqs];
+  int32_t* ctr = a.ws_sched + kCtrStride * (x + 1);
   const int PU = a.part_tokens / kUnit;
 
   St st;
   typename St::QOp qnext[St::NQB];
-  Cursor cc = locate(pref, n, geo.useq, r0);            // consume cursor
-  Cursor lc = cc;                                      // load cursor
-  int lpos = r0;
-  SeqView lv = seq_view<KV, D, BS>(a, lc.seq, geo.x + a.streams * lc.hh);
-  load_q<KV, D, G>(st.qb, a, cc.seq, geo.x + a.streams * cc.hh, i, kg);
   UnitRegs<KV, D> R;
-  load_unit<KV, D, BS>(R, lv, unit_blocks<BS>(lv, lc.j * kUnit), i, kg);
+  Pos<BS> P;
+  P.live = true;
+  enter_share<KV, D, BS>(a, x, total, sc, P, wi);
+  const int got = grab_share(ctr, lane);
+  P.ub = unit_blocks<BS>(P.v, P.c.j * kUnit);
+  issue<KV, D, BS, G>(a, x, P, R, qnext, i, kg);
+  P.next = a.stream_waves + __builtin_amdgcn_readfirstlane(got);
+  Cursor cc = P.c;                      // the position whose unit R holds
+  int share = P.share, pos = P.pos, end = P.end;
+  prepare_next<KV, D, BS>(a, x, total, sc, ctr, P, lane);
 
 #pragma unroll 1
-  for (int p = r0; p < r1;) {
-    // the piece: the rest of this partition of this segment, within the wave's share
-    const int np = min(min(r1 - p, cc.nj - cc.j), PU - cc.j % PU);
-    const int L = clamped_len(a, cc.seq);
+  for (;;) {
+    // the piece: the rest of this partition of this segment, within the share
+    const Cursor c0 = cc;
+    const int share0 = share, end0 = end;
+    const int np = min(min(end0 - pos, c0.nj - c0.j), PU - c0.j % PU);
+    const int L = clamped_len(a, c0.seq);
+    bool more = true;
     st.reset();
-    run_piece<KV, D, BS, G>(a, geo, st, R, lc, lv, lpos, r1 - 1, qnext, cc.j * kUnit, L, np, i, kg);
-    finish_piece<KV, D, G>(a, out_bf16, geo, st, cc, cc.j, np, PU, i, kg);
-    p += np;
-    if (p < r1) {
-      const bool new_seg = cc.j + np == cc.nj;
 #pragma unroll 1
-      for (int k = 0; k < np; ++k) advance(cc, pref, n);
-      if (new_seg) {
-#pragma unroll
-        for (int c = 0; c < St::NQB; ++c) st.qb[c] = qnext[c];
-      }
+    for (int q = 0; q < np; ++q) {
+      st.consume(R, qnext, (c0.j + q) * kUnit, L, kg, i, a.qk_scale);
+      more = P.live;
+      issue<KV, D, BS, G>(a, x, P, R, qnext, i, kg);
+      cc = P.c;
+      share = P.share;
+      pos = P.pos;
+      end = P.end;
+      prepare_next<KV, D, BS>(a, x, total, sc, ctr, P, lane);
     }
+    finish_piece<KV, D, G>(a, out_bf16, x, share0, st, c0, np, PU, i, kg);
+    if (!more) break;   // the last issue was a reload: every share of the wave is done
   }
 }
 
 // Merge of the partial records of every (sequence, query head) whose segment was split into
-// pieces: out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M) * v_scale, M = max_p m_p.  Segments
-// served by one piece were written by the stream kernel; empty sequences (L = 0) get zeros here.
+// pieces: out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M) * v_scale, M = max_p m_p, in one pass
+// with a running maximum.  Segments served by one piece were written by the stream kernel; empty
+// sequences (L = 0) get zeros here.
 template <int D>
 __global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_bf16) {
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -552,7 +664,7 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_b
   const int seq = blockIdx.x / a.num_q_heads;
   const int kvh = h / G, g = h % G;
   const int d = threadIdx.x;
-  const int32_t* pref = a.ws_pref;
+  const ro_i32 pref = ro(a.ws_pref);
   const int n = a.num_seqs;
   const int nj = pref[seq + 1] - pref[seq];
   const int64_t oi = (static_cast<int64_t>(seq) * a.num_q_heads + h) * D + d;
@@ -561,29 +673,27 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_b
     return;
   }
   const int x = kvh % a.streams, hh = kvh / a.streams;
-  const int useq = pref[n];
-  const int64_t total = static_cast<int64_t>(a.num_kv_heads / a.streams) * useq;
-  const int64_t share = (total + a.stream_waves - 1) / a.stream_waves;
-  const int64_t S = static_cast<int64_t>(hh) * useq + pref[seq];
+  Sched sc;
+  sc.S0 = ro(a.ws_sched)[0];
+  sc.S1 = ro(a.ws_sched)[1];
+  sc.W0 = ro(a.ws_sched)[2];
+  const int P0 = hh * pref[n] + pref[seq];   // stream position of the segment's first unit
   const int PU = a.part_tokens / kUnit;
   const int nparts = (nj + PU - 1) / PU;
-  if (nparts == 1 && S / share == (S + nj - 1) / share) return;
+  if (nparts == 1 && sc.share_of(P0) == sc.share_of(P0 + nj - 1)) return;
   const int64_t seg = (static_cast<int64_t>(hh) * n + seq) * a.max_parts + x * a.stream_slots;
-  float mm = -INFINITY;
+  float mm = -INFINITY, lsum = 0.f, o = 0.f;
   for (int k = 0; k < nparts; ++k) {
-    const int64_t u0 = S + static_cast<int64_t>(k) * PU, u1 = S + min((k + 1) * PU, nj) - 1;
-    for (int64_t w = u0 / share; w <= u1 / share; ++w)
-      mm = fmaxf(mm, a.ws_part[((seg + k + w) * G + g) * (D + 4)]);
-  }
-  const float ms = mm == -INFINITY ? 0.f : mm;
-  float lsum = 0.f, o = 0.f;
-  for (int k = 0; k < nparts; ++k) {
-    const int64_t u0 = S + static_cast<int64_t>(k) * PU, u1 = S + min((k + 1) * PU, nj) - 1;
-    for (int64_t w = u0 / share; w <= u1 / share; ++w) {
-      const float* rec = a.ws_part + ((seg + k + w) * G + g) * (D + 4);
-      const float f = __builtin_amdgcn_exp2f(rec[0] - ms);
-      lsum += rec[1] * f;
-      o += rec[4 + d] * f;
+    const int v0 = sc.share_of(P0 + k * PU), v1 = sc.share_of(P0 + min((k + 1) * PU, nj) - 1);
+#pragma unroll 4
+    for (int v = v0; v <= v1; ++v) {
+      const float* rec = a.ws_part + ((seg + k + v) * G + g) * (D + 4);
+      const float m = rec[0], l = rec[1], y = rec[4 + d];
+      const float mn = fmaxf(mm, m);
+      const float fo = __builtin_amdgcn_exp2f(mm - mn), fn = __builtin_amdgcn_exp2f(m - mn);
+      lsum = lsum * fo + l * fn;
+      o = o * fo + y * fn;
+      mm = mn;
     }
   }
   store_out(a.out, oi, lsum > 0.f ? o / lsum * a.v_scale : 0.f, out_bf16 != 0);
@@ -609,7 +719,8 @@ int launch_one(const DecodeArgs& a0, int out_bf16, hipStream_t s) {
   const int64_t wgs = static_cast<int64_t>(device_cus()) * Pipe<KV, D>::kOcc / 8 * 8;   // resident, multiple of 8
   a.streams = a.num_kv_heads % 8 == 0 ? 8 : 1;
   a.stream_waves = static_cast<int32_t>(wgs / a.streams * kWaves);
-  a.stream_slots = static_cast<int64_t>(a.num_kv_heads / a.streams) * a.num_seqs * a.max_parts + a.stream_waves;
+  a.max_shares = kSharesPerWave * a.stream_waves;   // bounds the plan's share count V
+  a.stream_slots = static_cast<int64_t>(a.num_kv_heads / a.streams) * a.num_seqs * a.max_parts + a.max_shares;
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return static_cast<int>(e);
@@ -656,12 +767,27 @@ int pick_dim(const DecodeArgs& a, int bs, int d, int out_bf16, hipStream_t s) {
 
 int decode_max_waves() { return device_cus() * kMaxOcc * kWaves; }
 
+static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace layout: share plan (pref, schedule header with the counters, share table), then the
+// partial records.  Every share count is bounded by kSharesPerWave per wave of the launch.
 size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t max_parts,
                               int64_t waves) {
-  const int64_t pref = ((num_seqs + 1) * 4 + 255) / 256 * 256;
+  const int64_t plan = align256((num_seqs + 1) * 4) + align256(kSchedInts * 4) + align256(16 * kSharesPerWave * waves);
   const int64_t g = num_q_heads < 8 ? num_q_heads : 8;   // G <= 8 and G <= num_q_heads
-  const int64_t records = num_q_heads * num_seqs * max_parts + waves * g;
-  return static_cast<size_t>(pref + records * (head_dim + 4) * 4);
+  const int64_t records = num_q_heads * num_seqs * max_parts + kSharesPerWave * waves * g;
+  return static_cast<size_t>(plan + records * (head_dim + 4) * 4);
+}
+
+void decode_workspace_carve(DecodeArgs& a, void* workspace) {
+  char* p = static_cast<char*>(workspace);
+  a.ws_pref = reinterpret_cast<int32_t*>(p);
+  p += align256((static_cast<int64_t>(a.num_seqs) + 1) * 4);
+  a.ws_sched = reinterpret_cast<int32_t*>(p);
+  p += align256(kSchedInts * 4);
+  a.ws_share = reinterpret_cast<int32_t*>(p);
+  p += align256(static_cast<int64_t>(16) * kSharesPerWave * decode_max_waves());
+  a.ws_part = reinterpret_cast<float*>(p);
 }
 
 int launch_decode(const DecodeArgs& a, int kv_dtype, int q_dtype, int out_dtype, int block_size,

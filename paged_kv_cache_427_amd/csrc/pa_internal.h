@@ -58,8 +58,11 @@ struct DecodeArgs {
   int32_t max_ctx;       // bound on every context length (lengths are clamped to it on the device)
   int32_t streams;       // unit streams: 8 (one per XCD; KV head h in stream h % 8) or 1
   int32_t stream_waves;  // waves per stream
+  int32_t max_shares;    // bound on the shares of one stream
   int64_t stream_slots;  // partial-record slots per stream
-  int32_t* ws_pref;      // [num_seqs + 1] units (16 keys) of sequences before s, for one KV head
+  int32_t* ws_pref;      // [num_seqs + 1] units (32 keys) of sequences before s, for one KV head
+  int32_t* ws_sched;     // share size, share count, one share counter per stream
+  int32_t* ws_share;     // [max_shares][4] start cursor of each share: head slot, sequence, unit, units
   float* ws_part;        // [streams * stream_slots][G][head_dim + 4]: max, sum, -, -, unnormalised o
   void* out;
 };
@@ -69,6 +72,8 @@ size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t hea
                               int64_t waves);
 // Waves of one decode launch on the current device (an upper bound for any dtype).
 int decode_max_waves();
+// Sets the workspace pointers of `a` (num_seqs set) inside a workspace of decode_workspace_bytes().
+void decode_workspace_carve(DecodeArgs& a, void* workspace);
 
 struct PrefillArgs {
   const void* q;
