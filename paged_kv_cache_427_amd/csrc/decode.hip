@@ -20,9 +20,10 @@
 //  * both products of a unit run on 16x16 MFMA tiles fed straight from the loads, no LDS staging:
 //      S^T[key][head] = K[key][:] . Q[head][:]       A = K rows (token-major tile), B = Q^T
 //      O^T[dim][head] += V^T[dim][key] P^T[key][head]   A = V^T rows (dim-major tile), B = P^T
-//    The G query heads occupy columns 0..G-1 of the 16.  The S^T accumulator layout -- lane l holds
-//    keys 4*(l/16)+r of each 16-key tile for head l%16 -- is, after rounding to bf16, exactly the B
-//    operand of the 16x16x32 P.V product over the unit's 32 keys, so the scores never cross lanes.
+//    The G query heads occupy columns 0..G-1 of the 16.  The keys of a unit are ordered inside its
+//    two S^T tiles so that lane l holds keys 8*(l/16)..+7 for head l%16; after rounding to bf16 that
+//    is exactly the B operand of the 16x16x32 P.V product over the unit's 32 keys, so the scores
+//    never cross lanes, and the matching V^T operand is 8 consecutive keys of one dim-major V row.
 //  * bf16 pools use v_mfma_f32_16x16x32_bf16 for both products; fp8 codes widen exactly to bf16
 //    first (v_cvt_scalef32_pk_bf16_fp8, scales kept in fp32); fp32 pools use
 //    v_mfma_f32_16x16x4_f32.  The probabilities are rounded to bf16 for the bf16/fp8 products and
@@ -97,29 +98,36 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float x, bool bf
 typedef const int32_t __attribute__((address_space(4)))* ro_i32;
 __device__ __forceinline__ ro_i32 ro(const int32_t* p) { return (ro_i32)p; }
 
+// Key order inside a unit.  Row i of the unit's S^T tile t is key 8*(i/4) + 4t + i%4, so the
+// accumulator rows 4kg..4kg+3 of both tiles -- what lane group kg holds -- are keys 8kg..8kg+7: the
+// probabilities of a lane are 8 consecutive keys, and so is its slice of the P.V operand, one
+// contiguous piece of a dim-major V row.
+__device__ __forceinline__ int tile_row_key(int t, int i) { return 8 * (i >> 2) + 4 * t + (i & 3); }
+
 // Raw registers of one 32-key unit, as loaded by one lane (i = lane % 16, kg = lane / 16).
-//  k[t][c]: key 16t + i of the unit, 16 bytes at byte 64c + 16kg of its row
+//  k[t][c]: key tile_row_key(t, i) of the unit, 16 bytes at byte 64c + 16kg of its row
 //           (bf16: dims 32c+8kg..+8; fp8: dims 64c+16kg..+16; fp32: dims 16c+4kg..+4)
-//  v[d][p]: dim 16d + i, keys 16p + 4kg .. +4 of the unit (VW dwords)
+//  v[d]:    dim 16d + i, keys 8kg .. 8kg+7 of the unit (VW dwords)
 template <int KV, int D>
 struct UnitRegs {
   static constexpr int E = Elem<KV>::kBytes;
   static constexpr int KL = D * E / 64;   // 16-byte K loads per 16-key tile
-  static constexpr int VW = E;            // dwords per 4-key V piece
+  static constexpr int VW = 2 * E;        // dwords of 8 keys of one V row
   uint4 k[2][KL];
-  uint32_t v[D / 16][2][VW];
+  uint32_t v[D / 16][VW];
 };
 
 template <int VW>
 __device__ __forceinline__ void load_piece(uint32_t (&dst)[VW], const char* p) {
-  if constexpr (VW == 1) {
-    dst[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else if constexpr (VW == 2) {
+  if constexpr (VW == 2) {
     const uint2 w = *reinterpret_cast<const uint2*>(p);
     dst[0] = w.x; dst[1] = w.y;
   } else {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
+#pragma unroll
+    for (int h = 0; h < VW / 4; ++h) {
+      const uint4 w = *reinterpret_cast<const uint4*>(p + 16 * h);
+      dst[4 * h] = w.x; dst[4 * h + 1] = w.y; dst[4 * h + 2] = w.z; dst[4 * h + 3] = w.w;
+    }
   }
 }
 
@@ -141,6 +149,16 @@ struct UnitBlocks {
   int32_t b[N];   // physical block ids
 };
 
+// ub.b[q] for a per-lane q, as selects of wave-uniform values (the compiler must not turn the
+// selects back into an indexed read, which would keep the block ids in scratch memory).
+template <int N>
+__device__ __forceinline__ int32_t pick_block(const int32_t (&b)[N], int q) {
+  int32_t r = __builtin_amdgcn_readfirstlane(b[0]);
+#pragma unroll
+  for (int k = 1; k < N; ++k) r = q == k ? __builtin_amdgcn_readfirstlane(b[k]) : r;
+  return r;
+}
+
 template <int BS>
 __device__ __forceinline__ UnitBlocks<BS> unit_blocks(const SeqView& sv, int U) {
   const int j0 = U / BS;
@@ -158,30 +176,15 @@ __device__ __forceinline__ void load_unit(UnitRegs<KV, D>& R, const SeqView& sv,
   constexpr int E = R_t::E, KL = R_t::KL, VW = R_t::VW;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const char* krow;                                   // key 16t + i of the unit
-    if constexpr (BS == 8) {
-      krow = sv.kbase + ((i >> 3) ? ub.b[2 * t + 1] : ub.b[2 * t]) * sv.blk_stride + (i & 7) * (D * E);
-    } else if constexpr (BS == 16) {
-      krow = sv.kbase + ub.b[t] * sv.blk_stride + i * (D * E);
-    } else {
-      krow = sv.kbase + ub.b[0] * sv.blk_stride + (16 * t + i) * (D * E);
-    }
+    const int key = tile_row_key(t, i);                 // the unit's key in row i of tile t
+    const char* krow = sv.kbase + static_cast<int64_t>(pick_block(ub.b, key / BS)) * sv.blk_stride + (key % BS) * (D * E);
 #pragma unroll
     for (int c = 0; c < KL; ++c) R.k[t][c] = *reinterpret_cast<const uint4*>(krow + 64 * c + 16 * kg);
   }
+  const int key0 = 8 * kg;                              // keys 8kg .. 8kg+7: one block, consecutive
+  const char* vrow = sv.vbase + static_cast<int64_t>(pick_block(ub.b, key0 / BS)) * sv.blk_stride + (key0 % BS) * E;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const char* vrow;                                   // keys 16p + 4kg .. +4 of the unit
-    if constexpr (BS == 8) {
-      vrow = sv.vbase + ((kg >> 1) ? ub.b[2 * p + 1] : ub.b[2 * p]) * sv.blk_stride + (4 * (kg & 1)) * E;
-    } else if constexpr (BS == 16) {
-      vrow = sv.vbase + ub.b[p] * sv.blk_stride + (4 * kg) * E;
-    } else {
-      vrow = sv.vbase + ub.b[0] * sv.blk_stride + (16 * p + 4 * kg) * E;
-    }
-#pragma unroll
-    for (int d = 0; d < D / 16; ++d) load_piece<VW>(R.v[d][p], vrow + (16 * d + i) * BS * E);
-  }
+  for (int d = 0; d < D / 16; ++d) load_piece<VW>(R.v[d], vrow + (16 * d + i) * BS * E);
 }
 
 template <int KV, int D, int G>
@@ -205,7 +208,7 @@ struct DecodeState {
                                           float qk_scale) {
     using R_t = UnitRegs<KV, D>;
     constexpr int KL = R_t::KL;
-    // ---- S^T of the unit's two 16-key tiles: lane holds keys 16t + 4kg + r for head col ----
+    // ---- S^T of the unit's two 16-key tiles: lane holds keys 8kg + 4t + r for head col ----
     f32x4 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -232,7 +235,7 @@ struct DecodeState {
       }
     }
     // ---- base-2 logits; keys at or past the context end are masked (last unit only) ----
-    float x[8];   // x[4t + r]: key 16t + 4kg + r of the unit
+    float x[8];   // x[e]: key 8kg + e of the unit (e = 4t + r)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -242,24 +245,22 @@ struct DecodeState {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (U + 16 * t + 4 * kg + r >= t1) x[4 * t + r] = -INFINITY;
+          if (U + 8 * kg + 4 * t + r >= t1) x[4 * t + r] = -INFINITY;
       // masked keys may hold any bits (even NaN): zero their values so that 0 * v stays 0
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int e = 0; e < 8; ++e) {
+        if (U + 8 * kg + e < t1) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (U + 16 * p + 4 * kg + e < t1) continue;
-#pragma unroll
-          for (int d = 0; d < D / 16; ++d) {
-            if constexpr (KV == kF32) {
-              R.v[d][p][e] = 0u;
-            } else if constexpr (KV == kBF16) {
-              R.v[d][p][e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-            } else {
-              R.v[d][p][0] &= ~(0xffu << (8 * e));
-            }
+        for (int d = 0; d < D / 16; ++d) {
+          if constexpr (KV == kF32) {
+            R.v[d][e] = 0u;
+          } else if constexpr (KV == kBF16) {
+            R.v[d][e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          } else {
+            R.v[d][e / 4] &= ~(0xffu << (8 * (e % 4)));
           }
         }
+      }
     }
     // ---- running max: raised only when a logit exceeds it by more than the slack ----
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -278,14 +279,14 @@ struct DecodeState {
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - ms);   // 0 for masked keys
-    // ---- O^T += V^T P^T: k-slot e of lane group kg is key 16(e/4) + 4kg + e%4 ----
+    // ---- O^T += V^T P^T: k-slot e of lane group kg is key 8kg + e ----
     if constexpr (KV == kF32) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) l += p[e];
 #pragma unroll
       for (int d = 0; d < D / 16; ++d)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[d] = mma_s(__uint_as_float(R.v[d][e / 4][e % 4]), p[e], o[d]);
+        for (int e = 0; e < 8; ++e) o[d] = mma_s(__uint_as_float(R.v[d][e]), p[e], o[d]);
     } else {
       bf16x8 pb;
 #pragma unroll
@@ -297,10 +298,10 @@ struct DecodeState {
       for (int d = 0; d < D / 16; ++d) {
         bf16x8 va;
         if constexpr (KV == kBF16) {
-          va = as_bf16x8(R.v[d][0][0], R.v[d][0][1], R.v[d][1][0], R.v[d][1][1]);
+          va = as_bf16x8(R.v[d][0], R.v[d][1], R.v[d][2], R.v[d][3]);
         } else {
-          va = as_bf16x8(fp8x2_to_bf16x2<false>(R.v[d][0][0]), fp8x2_to_bf16x2<true>(R.v[d][0][0]),
-                         fp8x2_to_bf16x2<false>(R.v[d][1][0]), fp8x2_to_bf16x2<true>(R.v[d][1][0]));
+          va = as_bf16x8(fp8x2_to_bf16x2<false>(R.v[d][0]), fp8x2_to_bf16x2<true>(R.v[d][0]),
+                         fp8x2_to_bf16x2<false>(R.v[d][1]), fp8x2_to_bf16x2<true>(R.v[d][1]));
         }
         o[d] = mma_s(va, pb, o[d]);
       }
