@@ -181,7 +181,7 @@ def main():
     cfg = {"workload": args.config, "num_seqs": len(wl.decode_seqs) or len(wl.prefill_seqs),
            "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
            "block_size": wl.block_size, "pool_blocks": wl.num_blocks, "kv_dtype": wl.kv_dtype,
-           "partition": si.dec_partition or 512}
+           "partition": si.dec_partition or 0}
     tab = si.dec_tables.cpu().numpy() if si.dec_tables is not None else None
     if tab is not None:
         uniq, logical, other = decode_bytes(wl, tab)

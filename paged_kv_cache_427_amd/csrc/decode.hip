@@ -655,11 +655,19 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
 }
 
 // Merge of the partial records of every (sequence, query head) whose segment was split into
-// pieces: out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M) * v_scale, M = max_p m_p, in one pass
-// with a running maximum.  Segments served by one piece were written by the stream kernel; empty
-// sequences (L = 0) get zeros here.
+// pieces: out = sum_r o_r 2^(m_r - M) / sum_r l_r 2^(m_r - M) * v_scale, M = max_r m_r.  Segments
+// served by one piece were written by the stream kernel; empty sequences (L = 0) get zeros here.
+// The records of partition k are those of the shares v0(k)..v1(k) that overlap it.  The workgroup
+// lists them in LDS (a scan of per-partition counts), reads every (m, l) at once, and then each
+// thread (one output dim) sums its dim over the records with many loads in flight.
+constexpr int kMergeMaxRec = 1024;
+
 template <int D>
 __global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_bf16) {
+  __shared__ int64_t rec_s[kMergeMaxRec];   // record offsets (floats into ws_part)
+  __shared__ float w_s[kMergeMaxRec];       // 2^(m_r - M)
+  __shared__ int scan_s[D];
+  __shared__ float red_s[D];
   const int G = a.num_q_heads / a.num_kv_heads;
   const int h = blockIdx.x % a.num_q_heads;
   const int seq = blockIdx.x / a.num_q_heads;
@@ -683,12 +691,71 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_b
   const int nparts = (nj + PU - 1) / PU;
   if (nparts == 1 && sc.share_of(P0) == sc.share_of(P0 + nj - 1)) return;
   const int64_t seg = (static_cast<int64_t>(hh) * n + seq) * a.max_parts + x * a.stream_slots;
+  auto rec_of = [&](int k, int v) { return ((seg + k + v) * G + g) * (D + 4); };
+
+  // ---- list the records: thread t owns partitions [t * ch, (t + 1) * ch) ----
+  const int ch = (nparts + D - 1) / D;
+  const int k0 = min(d * ch, nparts), k1 = min(k0 + ch, nparts);
+  int cnt = 0;
+  for (int k = k0; k < k1; ++k)
+    cnt += sc.share_of(P0 + min((k + 1) * PU, nj) - 1) - sc.share_of(P0 + k * PU) + 1;
+  scan_s[d] = cnt;
+  __syncthreads();
+  for (int off = 1; off < D; off *= 2) {
+    const int v = d >= off ? scan_s[d - off] : 0;
+    __syncthreads();
+    scan_s[d] += v;
+    __syncthreads();
+  }
+  const int R = scan_s[D - 1];
+  if (R <= kMergeMaxRec) {
+    int r = scan_s[d] - cnt;
+    for (int k = k0; k < k1; ++k) {
+      const int v0 = sc.share_of(P0 + k * PU), v1 = sc.share_of(P0 + min((k + 1) * PU, nj) - 1);
+      for (int v = v0; v <= v1; ++v) rec_s[r++] = rec_of(k, v);
+    }
+    __syncthreads();
+    // ---- maximum and weighted sum of the partial sums ----
+    float mm = -INFINITY;
+    for (int q = d; q < R; q += D) {
+      const float m = a.ws_part[rec_s[q]];
+      w_s[q] = m;
+      mm = fmaxf(mm, m);
+    }
+    red_s[d] = mm;
+    __syncthreads();
+    for (int off = D / 2; off > 0; off /= 2) {
+      if (d < off) red_s[d] = fmaxf(red_s[d], red_s[d + off]);
+      __syncthreads();
+    }
+    const float M = red_s[0];
+    __syncthreads();
+    float ls = 0.f;
+    for (int q = d; q < R; q += D) {
+      const float w = __builtin_amdgcn_exp2f(w_s[q] - M);
+      w_s[q] = w;
+      ls += a.ws_part[rec_s[q] + 1] * w;
+    }
+    red_s[d] = ls;
+    __syncthreads();
+    for (int off = D / 2; off > 0; off /= 2) {
+      if (d < off) red_s[d] += red_s[d + off];
+      __syncthreads();
+    }
+    const float lsum = red_s[0];
+    // ---- this thread's output dim ----
+    float o = 0.f;
+#pragma unroll 8
+    for (int q = 0; q < R; ++q) o += a.ws_part[rec_s[q] + 4 + d] * w_s[q];
+    store_out(a.out, oi, lsum > 0.f ? o / lsum * a.v_scale : 0.f, out_bf16 != 0);
+    return;
+  }
+  // more records than the LDS list holds: one pass with a running maximum
   float mm = -INFINITY, lsum = 0.f, o = 0.f;
   for (int k = 0; k < nparts; ++k) {
     const int v0 = sc.share_of(P0 + k * PU), v1 = sc.share_of(P0 + min((k + 1) * PU, nj) - 1);
-#pragma unroll 4
     for (int v = v0; v <= v1; ++v) {
-      const float* rec = a.ws_part + ((seg + k + v) * G + g) * (D + 4);
+      const float* rec = a.ws_part + rec_of(k, v);
       const float m = rec[0], l = rec[1], y = rec[4 + d];
       const float mn = fmaxf(mm, m);
       const float fo = __builtin_amdgcn_exp2f(mm - mn), fn = __builtin_amdgcn_exp2f(m - mn);
