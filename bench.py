@@ -9,7 +9,7 @@ already resident in HBM.  The default workload is the shared-prefix decode (256 
 head_dim 128, bf16, 16-token blocks, one copy-on-write per sequence).
 
 Prints one JSON line.  `value` is the decode's unique KV bytes per step (each physical block once)
-divided by the step time, in GB/s.  `roofline` prices the decode kernels (partition + merge),
+divided by the step time, in GB/s.  `roofline` prices the decode launch (plan, stream and merge kernels),
 timed with HIP events on the launch stream, against the 8 TB/s HBM peak.  `cpu_baseline` is the
 fp64 CPU oracle timed on a bounded sample of the same workload on this host's cores.
 """
@@ -191,7 +191,7 @@ def main():
         res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": measured_traffic(args.config, args.block_size),
-                           "kernel": "pa_decode (partition kernel + merge kernel)",
+                           "kernel": "pa_decode (plan + stream + merge kernels)",
                            "algorithmic_bytes_per_launch": int(uniq + other)}
         res["decode_logical_kv_GBps"] = round(logical / (ms_decode * 1e-3) / 1e9, 1)
         cfg["mean_context"] = round(float(np.mean(wl.decode_lens)), 1)
