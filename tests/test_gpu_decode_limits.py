@@ -1,0 +1,109 @@
+"""GPU parity of pa_decode at the edges of its work plan: more sequences than the plan kernel ranks
+in LDS (8192), and more pieces per (sequence, head) than the merge kernel lists in LDS (1024), each
+against the fp64 oracle on sampled or all outputs (bf16 tolerance 2e-2)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gather_seq, ref_decode
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+
+
+def _say(*a):
+    print("[gpu-test]", *a, flush=True)
+
+
+def _pools(gen, num_blocks, hkv, b, d):
+    k = torch.randn((num_blocks, hkv, b, d), generator=gen).to(torch.bfloat16)
+    v = torch.randn((num_blocks, hkv, d, b), generator=gen).to(torch.bfloat16)
+    return k, v
+
+
+def _tables(rng, lens, b, num_blocks):
+    """Every sequence gets distinct physical blocks, in a seeded random order."""
+    need = [-(-int(L) // b) for L in lens]
+    perm = rng.permutation(num_blocks)
+    tabs = np.zeros((len(lens), max(max(need), 1)), dtype=np.int32)
+    at = 0
+    for s, n in enumerate(need):
+        tabs[s, :n] = perm[at:at + n]
+        at += n
+    return tabs
+
+
+def _oracle_rows(kpool, vpool, tabs, lens, q, scale, seqs):
+    """fp64 oracle outputs of the sequences `seqs` (their blocks only, through their tables)."""
+    out = {}
+    for s in seqs:
+        L = int(lens[s])
+        nblk = -(-L // kpool.shape[2])
+        blocks = torch.as_tensor(tabs[s, :nblk].astype(np.int64))
+        ks = kpool.index_select(0, blocks).double().numpy()
+        vs = vpool.index_select(0, blocks).double().numpy()
+        k = gather_seq(ks, list(range(nblk)), L, "k")
+        v = gather_seq(vs, list(range(nblk)), L, "v")
+        out[s] = ref_decode(q[s:s + 1].double().numpy(), [(k, v)], scale)[0]
+    return out
+
+
+def _decode(q, kpool, vpool, tabs, lens, scale, max_ctx, partition):
+    from paged_kv_cache_427_amd.ops import pa_decode, make_pool_desc
+    from paged_kv_cache_427_amd._lib import PA_BF16
+    num_blocks, hkv, b, d = kpool.shape
+    pool = make_pool_desc(num_blocks, b, hkv, d, PA_BF16)
+    dev = torch.device("cuda")
+    out = torch.full(q.shape, 3.0, dtype=torch.bfloat16, device=dev)
+    pa_decode(q.to(dev), kpool.to(dev), vpool.to(dev), pool, torch.as_tensor(tabs).to(dev),
+              torch.as_tensor(np.asarray(lens, np.int32)).to(dev), scale, out, max_ctx, partition)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def test_more_sequences_than_the_plan_ranks_in_lds():
+    """9000 short sequences (some empty): the plan kernel searches its prefix in global memory."""
+    rng = np.random.Generator(np.random.PCG64(4271))
+    gen = torch.Generator().manual_seed(4271)
+    n, hq, hkv, b, d = 9000, 16, 8, 16, 64
+    lens = rng.integers(1, 41, size=n).astype(np.int32)
+    lens[[5, 4000, 8999]] = 0
+    need = sum(-(-int(L) // b) for L in lens)
+    num_blocks = need + 64
+    kpool, vpool = _pools(gen, num_blocks, hkv, b, d)
+    tabs = _tables(rng, lens, b, num_blocks)
+    q = torch.randn((n, hq, d), generator=gen).to(torch.bfloat16)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    _say("decode", n, "sequences, blocks", num_blocks)
+    got = _decode(q, kpool, vpool, tabs, lens, scale, 40, 0)
+    for s in (5, 4000, 8999):
+        assert np.count_nonzero(got[s]) == 0
+    sample = [0, 1, 8191, 8192, 8193, 8998] + rng.choice(n, size=40, replace=False).tolist()
+    sample = [s for s in sample if lens[s] > 0]
+    ref = _oracle_rows(kpool, vpool, tabs, lens, q, scale, sample)
+    err = max(float(np.max(np.abs(got[s] - ref[s]))) for s in sample)
+    _say("max err", err)
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("partition", [32, 512])
+def test_more_pieces_than_the_merge_lists_in_lds(partition):
+    """Two long contexts cut every 32 tokens: over 1024 pieces per (sequence, head), merged by the
+    merge kernel's one-pass fallback (and, for comparison, the same contexts cut every 512)."""
+    rng = np.random.Generator(np.random.PCG64(4272))
+    gen = torch.Generator().manual_seed(4272)
+    hq, hkv, b, d = 2, 1, 16, 128
+    lens = np.array([36000, 33001], dtype=np.int32)
+    need = sum(-(-int(L) // b) for L in lens)
+    num_blocks = need + 16
+    kpool, vpool = _pools(gen, num_blocks, hkv, b, d)
+    tabs = _tables(rng, lens, b, num_blocks)
+    q = torch.randn((2, hq, d), generator=gen).to(torch.bfloat16)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    _say("decode, 2 long contexts, partition", partition)
+    got = _decode(q, kpool, vpool, tabs, lens, scale, 36000, partition)
+    ref = _oracle_rows(kpool, vpool, tabs, lens, q, scale, [0, 1])
+    err = max(float(np.max(np.abs(got[s] - ref[s]))) for s in (0, 1))
+    _say("max err", err)
+    assert err <= TOL_BF16
