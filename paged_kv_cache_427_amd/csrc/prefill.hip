@@ -12,9 +12,10 @@
 //    the G query heads that share the KV head, so one K/V tile in LDS serves every head of the group;
 //    each wave owns 32 rows;
 //  * key tiles of 64 positions are gathered through the block table and stored in LDS as bf16 (fp8
-//    e4m3 codes convert exactly; scales stay in fp32), double-buffered in LDS and in registers: the
-//    loads of tile t + 2 are issued while tile t is computed, so each has two iterations to arrive
-//    (the kernel is bound by that latency, not by its MFMAs, when a load has only one).  Every load instruction of a wave reads
+//    e4m3 codes convert exactly; scales stay in fp32), double-buffered in LDS with one register
+//    stage: iteration t stores tile t + 1 and then issues the loads of tile t + 2 before computing
+//    tile t, so each load has about one iteration to arrive, and the loop body is not unrolled, so
+//    the accumulators keep their registers from tile to tile.  Every load instruction of a wave reads
 //    inside one pool block, so the table entries are wave-uniform scalar loads, and every load is
 //    issued unconditionally, so that the only wait for them is the one before the LDS store.  K
 //    tiles are stored [key][dim]; the V pool's dim-major tiles give [dim][key] rows directly, so V
@@ -285,24 +286,29 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   char* const vbuf0 = smem + 2 * kKBytes;
   char* const vbuf1 = smem + 2 * kKBytes + kVBytes;
 
-  TileLoader<KV, BS> la, lb;
-  la.load_k(kpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
-  la.load_v(vpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
-  la.store_k(kbuf0, wave, lane);
-  la.store_v(vbuf0, 0, n_keys, wave, lane);
-  la.load_k(kpool, tab, blk_stride, head_off, min(1, n_tiles - 1) * kKT, n_keys, wave, lane);
-  la.load_v(vpool, tab, blk_stride, head_off, min(1, n_tiles - 1) * kKT, n_keys, wave, lane);
+  TileLoader<KV, BS> ld;
+  ld.load_k(kpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+  ld.load_v(vpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+  ld.store_k(kbuf0, wave, lane);
+  ld.store_v(vbuf0, 0, n_keys, wave, lane);
+  ld.load_k(kpool, tab, blk_stride, head_off, min(1, n_tiles - 1) * kKT, n_keys, wave, lane);
+  ld.load_v(vpool, tab, blk_stride, head_off, min(1, n_tiles - 1) * kKT, n_keys, wave, lane);
   __syncthreads();
 
-  // Iteration t: loads tile t + 2 into ld_ld, computes tile t, stores tile t + 1 from st_ld.  Loads
-  // past the last tile re-read it (unused), so that they are unconditional.
-  auto iteration = [&](TileLoader<KV, BS>& st_ld, TileLoader<KV, BS>& ld_ld, int t) {
+  // Iteration t: stores tile t + 1 (loaded during iteration t - 1) into the other LDS buffer, issues
+  // the loads of tile t + 2 into the same registers, then computes tile t.  One register stage, so
+  // the loop body is not unrolled and the accumulators keep their registers from one tile to the
+  // next.  Loads past the last tile re-read it (unused), so that they are unconditional.
+#pragma unroll 1
+  for (int t = 0; t < n_tiles; ++t) {
     const bool odd = t & 1;
-    const int t2 = min(t + 2, n_tiles - 1) * kKT;
-    ld_ld.load_k(kpool, tab, blk_stride, head_off, t2, n_keys, wave, lane);
-    ld_ld.load_v(vpool, tab, blk_stride, head_off, t2, n_keys, wave, lane);
     const char* kb = odd ? kbuf1 : kbuf0;
     const char* vb = odd ? vbuf1 : vbuf0;
+    ld.store_k(odd ? kbuf0 : kbuf1, wave, lane);
+    ld.store_v(odd ? vbuf0 : vbuf1, min(t + 1, n_tiles - 1) * kKT, n_keys, wave, lane);
+    const int t2 = min(t + 2, n_tiles - 1) * kKT;
+    ld.load_k(kpool, tab, blk_stride, head_off, t2, n_keys, wave, lane);
+    ld.load_v(vpool, tab, blk_stride, head_off, t2, n_keys, wave, lane);
 
     // ---- S^T = K Q^T for two 32-key halves ----
     f32x16 s[2];
@@ -362,7 +368,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
       }
     l_run += lsum + shfl_xor(lsum, 32);
 
-    // ---- O^T += V^T P^T, side by side with widening and storing the next tile ----
+    // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const char* vrow = vb + (dt * 32 + (lane & 31)) * kVStride + 16 * h;
@@ -372,21 +378,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], o[dt], 0, 0, 0);
       }
     }
-    st_ld.store_k(odd ? kbuf0 : kbuf1, wave, lane);
-    st_ld.store_v(odd ? vbuf0 : vbuf1, min(t + 1, n_tiles - 1) * kKT, n_keys, wave, lane);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read (V fragment)
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU (widening)
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
-    }
     __syncthreads();
-  };
-  for (int t = 0; t < n_tiles; t += 2) {
-    iteration(la, lb, t);
-    if (t + 1 >= n_tiles) break;
-    iteration(lb, la, t + 1);
   }
 
   // ---- out[token][head][d] = O^T[d][row] / l ----
