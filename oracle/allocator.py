@@ -12,12 +12,23 @@ What the pages fix:
     [day28] §四 4.2 and §六 items 3-4).
   * running out of blocks is still possible ([day28] FAQ Q3).
 
+Prefix caching ([ch7] 7.1 「三个关键机制」 and its vLLM parameter list: requests with the same
+system-prompt prefix point at the same physical blocks under a reference count, only the differing
+suffixes get blocks of their own; [day28] §七: requests sharing a cached system prompt skip its
+prefill; [day28] FAQ Q5: that pays when the shared prefix is long and stable).
+
 Readings taken where the pages are silent:
   * free list: a FIFO queue whose initial order is given; freed blocks join its tail in table order.
   * slot of logical position p: table[p // b] * b + p % b.
   * append is all-or-nothing: if the free list cannot cover every block it needs, nothing changes.
+  * prefix cache (when enabled): only full blocks are cached.  A block's key is (the entry id of the
+    block before it, or 0 for the first, and its b token ids); entry ids are never reused, so a key
+    names one exact token prefix.  A new sequence takes the longest run of cached blocks matching
+    its prompt, but always leaves at least one prompt token to compute.  A cached block whose count
+    falls to zero is not freed but kept, least recently released first, and is reclaimed (its entry
+    dropped) only when the free list is empty.
 """
-from collections import deque
+from collections import OrderedDict, deque
 from typing import Dict, List, Optional, Sequence, Tuple
 
 
@@ -42,6 +53,89 @@ class RefAllocator:
         self.ref: List[int] = [0] * num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
+        self.caching = False
+        self.entries: Dict[Tuple[int, Tuple[int, ...]], int] = {}   # key -> entry id
+        self.entry_block: Dict[int, int] = {}                        # entry id -> block
+        self.entry_key: Dict[int, Tuple[int, Tuple[int, ...]]] = {}
+        self.block_entry: List[int] = [0] * num_blocks               # 0: the block is not cached
+        self.evictable: "OrderedDict[int, None]" = OrderedDict()     # cached, count 0, oldest first
+        self.next_entry = 1
+
+    # -- block supply -------------------------------------------------------------------------
+    def enable_prefix_cache(self) -> None:
+        self.caching = True
+
+    def available(self) -> int:
+        """Blocks an append can take: free ones, then cached ones nobody points at."""
+        return len(self.free) + len(self.evictable)
+
+    def _take(self) -> int:
+        if self.free:
+            return self.free.popleft()
+        blk, _ = self.evictable.popitem(last=False)      # least recently released cached block
+        eid = self.block_entry[blk]
+        del self.entries[self.entry_key.pop(eid)]
+        del self.entry_block[eid]
+        self.block_entry[blk] = 0
+        return blk
+
+    def _release(self, blk: int) -> None:
+        self.ref[blk] -= 1
+        if self.ref[blk] == 0:
+            if self.block_entry[blk]:
+                self.evictable[blk] = None
+            else:
+                self.free.append(blk)
+
+    # -- prefix cache -------------------------------------------------------------------------
+    def add_seq_prefix(self, sid: int, tokens: Sequence[int]) -> int:
+        """New sequence whose prompt is `tokens`: its table starts with the longest run of cached
+        full blocks matching the prompt (leaving at least one token).  Returns the tokens covered."""
+        self.add_seq(sid)
+        if not self.caching:
+            return 0
+        b = self.block_size
+        parent = 0
+        table = self.tables[sid]
+        while (len(table) + 1) * b <= len(tokens) - 1:
+            j = len(table)
+            eid = self.entries.get((parent, tuple(int(x) for x in tokens[j * b:(j + 1) * b])))
+            if eid is None:
+                break
+            blk = self.entry_block[eid]
+            if self.ref[blk] == 0:
+                del self.evictable[blk]
+            self.ref[blk] += 1
+            table.append(blk)
+            parent = eid
+        self.lens[sid] = len(table) * b
+        return self.lens[sid]
+
+    def cache_seq(self, sid: int, tokens: Sequence[int]) -> None:
+        """Register the full blocks of `sid` that hold tokens[0 : len(tokens)] (their K/V written)."""
+        if sid not in self.tables:
+            raise AllocError(f"unknown sequence {sid}")
+        if len(tokens) > self.lens[sid]:
+            raise AllocError("more tokens than the sequence holds")
+        if not self.caching:
+            return
+        b = self.block_size
+        parent = 0
+        table = self.tables[sid]
+        for j in range(len(tokens) // b):
+            key = (parent, tuple(int(x) for x in tokens[j * b:(j + 1) * b]))
+            eid = self.entries.get(key)
+            blk = table[j]
+            if eid is None:
+                if self.block_entry[blk]:
+                    raise AllocError(f"block {blk} is cached under other tokens")
+                eid = self.next_entry
+                self.next_entry += 1
+                self.entries[key] = eid
+                self.entry_key[eid] = key
+                self.entry_block[eid] = blk
+                self.block_entry[blk] = eid
+            parent = eid
 
     # -- sequence lifecycle -------------------------------------------------------------------
     def add_seq(self, sid: int) -> None:
@@ -66,9 +160,7 @@ class RefAllocator:
         if sid not in self.tables:
             raise AllocError(f"unknown sequence {sid}")
         for blk in self.tables[sid]:
-            self.ref[blk] -= 1
-            if self.ref[blk] == 0:
-                self.free.append(blk)
+            self._release(blk)
         del self.tables[sid]
         del self.lens[sid]
 
@@ -94,9 +186,9 @@ class RefAllocator:
             raise AllocError(f"unknown sequence {sid}")
         if n < 0:
             raise AllocError("negative token count")
-        if self.blocks_needed(sid, n) > len(self.free):
+        if self.blocks_needed(sid, n) > self.available():
             raise OutOfBlocks(f"sequence {sid}: need {self.blocks_needed(sid, n)} blocks, "
-                              f"{len(self.free)} free")
+                              f"{self.available()} available")
         b = self.block_size
         table = self.tables[sid]
         slots: List[int] = []
@@ -106,13 +198,13 @@ class RefAllocator:
             logical = p // b
             if p % b == 0:
                 # first token of a new logical block: take the head of the free list
-                blk = self.free.popleft()
+                blk = self._take()
                 self.ref[blk] = 1
                 table.append(blk)
             elif self.ref[table[logical]] > 1:
                 # writing into a block someone else also points at: copy it first
                 old = table[logical]
-                new = self.free.popleft()
+                new = self._take()
                 self.ref[old] -= 1
                 self.ref[new] = 1
                 table[logical] = new
@@ -134,6 +226,12 @@ class RefAllocator:
     def num_free(self) -> int:
         return len(self.free)
 
+    def num_cached(self) -> int:
+        return len(self.entries)
+
+    def evictable_list(self) -> List[int]:
+        return list(self.evictable)
+
     def free_list(self) -> List[int]:
         return list(self.free)
 
@@ -152,5 +250,15 @@ class RefAllocator:
         free = set(self.free)
         assert len(free) == len(self.free), "duplicate block on the free list"
         used = {i for i, c in enumerate(count) if c > 0}
+        idle = set(self.evictable)
         assert not (free & used), "a referenced block is on the free list"
-        assert free | used == set(range(self.num_blocks)), "a block is neither free nor referenced"
+        assert not (idle & used) and not (idle & free), "an evictable block is in use or free"
+        assert free | used | idle == set(range(self.num_blocks)), "a block is neither free nor referenced"
+        # cache: every entry names one block and back; evictable blocks are exactly the cached ones
+        # nobody points at
+        assert len(self.entries) == len(self.entry_block) == len(self.entry_key)
+        for key, eid in self.entries.items():
+            assert self.entry_key[eid] == key and self.block_entry[self.entry_block[eid]] == eid
+        cached = {blk for blk in range(self.num_blocks) if self.block_entry[blk]}
+        assert cached == set(self.entry_block.values())
+        assert idle == {blk for blk in cached if self.ref[blk] == 0}
