@@ -238,6 +238,36 @@ pa_status pa_alloc_stats(const pa_allocator* a, int32_t* num_free, int32_t* num_
 /* The free list in queue order into host int32 out[cap]; *n_out = its length. */
 pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n_out);
 
+/* ---------------------------------------------------------------------------------------------
+ * Prefix cache.  [ch7] 7.1 「三个关键机制」 and its vLLM parameter list (requests with the same
+ * system prompt share its physical blocks under a reference count); [day28] §七 (a request whose
+ * prompt starts with a cached prefix skips that prefill); [day28] FAQ Q5 (it pays when the prefix
+ * is long and stable).  Off until enabled; while off, the calls below change nothing.
+ *   - only full blocks are cached, each under the key (the entry id of the block before it, 0 for
+ *     the first, and its block_size token ids); entry ids are never reused, so a key names one
+ *     exact token prefix;
+ *   - a cached block whose count drops to zero is kept ("evictable", least recently released
+ *     first) and reclaimed, entry dropped, only once the free list is empty: appends and OOM
+ *     checks count free + evictable blocks, and a failed append restores the cache too.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_alloc_enable_prefix_cache(pa_allocator* a);
+/* New sequence with prompt host int32 tokens[n_tokens]: its table starts with the longest run of
+ * cached blocks matching the prompt, leaving at least one prompt token uncovered (its K/V are
+ * already in the pool); *n_cached_out = the tokens covered (a multiple of block_size, also the
+ * sequence length).  The caller appends and computes only tokens[*n_cached_out:].  PA_ERR_INVALID
+ * if the id exists or the prompt pointer is null with n_tokens > 0. */
+pa_status pa_alloc_add_seq_prefix(pa_allocator* a, int64_t seq_id, const int32_t* tokens,
+                                  int32_t n_tokens, int32_t* n_cached_out);
+/* Register the full blocks of seq_id holding tokens[0:n_tokens] (host int32), whose K/V the caller
+ * has written.  Blocks whose key is cached already keep the existing entry.  PA_ERR_INVALID if the
+ * sequence is unknown, n_tokens exceeds its length, or one of its blocks is cached under other
+ * tokens (entries registered before the error stay). */
+pa_status pa_alloc_cache_seq(pa_allocator* a, int64_t seq_id, const int32_t* tokens, int64_t n_tokens);
+/* Number of cache entries and of evictable blocks (either pointer may be NULL). */
+pa_status pa_alloc_cache_stats(const pa_allocator* a, int32_t* num_cached, int32_t* num_evictable);
+/* The evictable blocks, least recently released first, into host int32 out[cap]; *n_out = count. */
+pa_status pa_alloc_evictable_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,11 @@ _PROTOS = {
     "pa_alloc_refcount": (c_int32, [c_void_p, c_int32, _I32P]),
     "pa_alloc_stats": (c_int32, [c_void_p, _I32P, _I32P, _I64P]),
     "pa_alloc_free_list": (c_int32, [c_void_p, _I32P, c_int32, _I32P]),
+    "pa_alloc_enable_prefix_cache": (c_int32, [c_void_p]),
+    "pa_alloc_add_seq_prefix": (c_int32, [c_void_p, c_int64, _I32P, c_int32, _I32P]),
+    "pa_alloc_cache_seq": (c_int32, [c_void_p, c_int64, _I32P, c_int64]),
+    "pa_alloc_cache_stats": (c_int32, [c_void_p, _I32P, _I32P]),
+    "pa_alloc_evictable_list": (c_int32, [c_void_p, _I32P, c_int32, _I32P]),
 }
 
 EXPORTED = tuple(_PROTOS)

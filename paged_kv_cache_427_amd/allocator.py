@@ -19,7 +19,8 @@ def _i64p(a: np.ndarray):
 
 
 class BlockAllocator:
-    """Block tables, on-demand blocks, refcounted sharing (fork) and copy-on-write (append)."""
+    """Block tables, on-demand blocks, refcounted sharing (fork), copy-on-write (append) and an
+    optional prefix cache of full blocks keyed by their token prefix."""
 
     def __init__(self, num_blocks: int, block_size: int, free_order: Sequence[int] = None):
         self.num_blocks = int(num_blocks)
@@ -109,4 +110,42 @@ class BlockAllocator:
         n = ctypes.c_int32(0)
         buf = np.empty(max(self.num_blocks, 1), dtype=np.int32)
         check(lib().pa_alloc_free_list(self._h, _i32p(buf), self.num_blocks, ctypes.byref(n)))
+        return buf[:n.value].tolist()
+
+    # -- prefix cache ---------------------------------------------------------------------------
+    def enable_prefix_cache(self) -> None:
+        check(lib().pa_alloc_enable_prefix_cache(self._h))
+
+    def add_seq_prefix(self, sid: int, tokens: Sequence[int]) -> int:
+        """New sequence whose table starts with the cached blocks matching `tokens` (at least one
+        token left over); returns the number of prompt tokens those blocks already hold."""
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        buf = tok if tok.size else np.zeros(1, np.int32)
+        check(lib().pa_alloc_add_seq_prefix(self._h, int(sid), _i32p(buf), int(tok.size), ctypes.byref(n)))
+        return n.value
+
+    def cache_seq(self, sid: int, tokens: Sequence[int]) -> None:
+        """Register the full blocks of `sid` holding tokens[:len(tokens)] (their K/V written)."""
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        buf = tok if tok.size else np.zeros(1, np.int32)
+        check(lib().pa_alloc_cache_seq(self._h, int(sid), _i32p(buf), int(tok.size)))
+
+    def cache_stats(self) -> Tuple[int, int]:
+        """(cache entries, evictable blocks)."""
+        c, e = ctypes.c_int32(0), ctypes.c_int32(0)
+        check(lib().pa_alloc_cache_stats(self._h, ctypes.byref(c), ctypes.byref(e)))
+        return c.value, e.value
+
+    def num_cached(self) -> int:
+        return self.cache_stats()[0]
+
+    def available(self) -> int:
+        """Blocks an append can take: free plus evictable."""
+        return self.num_free() + self.cache_stats()[1]
+
+    def evictable_list(self) -> List[int]:
+        n = ctypes.c_int32(0)
+        buf = np.empty(max(self.num_blocks, 1), dtype=np.int32)
+        check(lib().pa_alloc_evictable_list(self._h, _i32p(buf), self.num_blocks, ctypes.byref(n)))
         return buf[:n.value].tolist()

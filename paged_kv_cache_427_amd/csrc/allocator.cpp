@@ -12,9 +12,19 @@
 // Readings where the pages are silent: the free list is a FIFO queue with a caller-given initial
 // order; freed blocks join its tail in table order; the slot of position p is
 // table[p / b] * b + p % b; an append that cannot get every block it needs changes nothing.
+//
+// Prefix cache (7.1 again, and its vLLM parameter list: requests with the same system-prompt
+// prefix share its physical blocks, only the differing suffixes get blocks of their own; Day 28 §七:
+// requests sharing a cached prompt skip its prefill; FAQ Q5: worth it when the prefix is long and
+// stable).  Readings: only full blocks are cached, under the key (entry id of the block before, or 0,
+// and the block's token ids); entry ids are never reused, so a key names one exact token prefix.  A
+// new sequence attaches the longest matching run of cached blocks but leaves at least one prompt
+// token to compute.  A cached block whose count falls to zero is kept, and is reclaimed (its entry
+// dropped), least recently released first, only when the free list is empty.
 #include <cstdint>
 #include <cstring>
 #include <deque>
+#include <list>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -32,18 +42,86 @@ struct pa_allocator {
     int64_t len = 0;
   };
   std::unordered_map<int64_t, Seq> seqs;
+
+  // prefix cache
+  struct Key {
+    int64_t parent;
+    std::vector<int32_t> tokens;
+    bool operator==(const Key& o) const { return parent == o.parent && tokens == o.tokens; }
+  };
+  struct KeyHash {
+    size_t operator()(const Key& k) const {
+      uint64_t h = 1469598103934665603ull ^ static_cast<uint64_t>(k.parent);   // FNV-1a over the ids
+      for (int32_t t : k.tokens) h = (h ^ static_cast<uint32_t>(t)) * 1099511628211ull;
+      return static_cast<size_t>(h);
+    }
+  };
+  struct Entry {
+    int32_t block;
+    Key key;
+  };
+  bool caching = false;
+  std::unordered_map<Key, int64_t, KeyHash> entries;   // key -> entry id
+  std::unordered_map<int64_t, Entry> entry;            // entry id -> block and key
+  std::vector<int64_t> block_entry;                    // 0: the block is not cached
+  std::list<int32_t> evictable;                        // cached blocks with count 0, oldest first
+  std::vector<std::list<int32_t>::iterator> evict_pos;
+  int64_t next_entry = 1;
 };
 
 namespace {
+
+// A block taken by an append: from the free-list head, or reclaimed from the cache.
+struct Take {
+  int32_t block;
+  bool reclaimed;
+  int64_t eid;                      // the dropped cache entry (reclaimed blocks)
+  pa_allocator::Key key;
+};
 
 // Undo record of one append: enough to restore the state exactly.
 struct AppendUndo {
   int64_t seq_id;
   int64_t old_len;
   size_t old_table_size;
-  std::vector<int32_t> popped;                         // blocks taken from the free-list head, in order
+  std::vector<Take> taken;                             // in order
   std::vector<std::pair<int32_t, int32_t>> cow;        // (logical index, old block)
 };
+
+int64_t available(const pa_allocator* a) {
+  return static_cast<int64_t>(a->free_list.size()) + static_cast<int64_t>(a->evictable.size());
+}
+
+// The next block for an append: the free-list head, else the least recently released cached block
+// nobody points at (its cache entry is dropped).  The caller has checked that one exists.
+int32_t take_block(pa_allocator* a, AppendUndo* undo) {
+  if (!a->free_list.empty()) {
+    const int32_t blk = a->free_list.front();
+    a->free_list.pop_front();
+    if (undo) undo->taken.push_back(Take{blk, false, 0, {}});
+    return blk;
+  }
+  const int32_t blk = a->evictable.front();
+  a->evictable.pop_front();
+  const int64_t eid = a->block_entry[blk];
+  auto it = a->entry.find(eid);
+  if (undo) undo->taken.push_back(Take{blk, true, eid, it->second.key});
+  a->entries.erase(it->second.key);
+  a->entry.erase(it);
+  a->block_entry[blk] = 0;
+  return blk;
+}
+
+// One reference to `blk` dropped: at zero a cached block is kept (newest at the back), any other
+// block joins the free-list tail.
+void release_block(pa_allocator* a, int32_t blk) {
+  if (--a->ref[blk] != 0) return;
+  if (a->block_entry[blk] != 0) {
+    a->evict_pos[blk] = a->evictable.insert(a->evictable.end(), blk);
+  } else {
+    a->free_list.push_back(blk);
+  }
+}
 
 int32_t blocks_needed(const pa_allocator* a, const pa_allocator::Seq& s, int32_t n) {
   const int64_t b = a->block_size;
@@ -67,24 +145,18 @@ void do_append(pa_allocator* a, int64_t seq_id, pa_allocator::Seq& s, int32_t n,
     const int64_t p = s.len;
     const int64_t logical = p / b;
     if (p % b == 0) {
-      const int32_t blk = a->free_list.front();
-      a->free_list.pop_front();
+      const int32_t blk = take_block(a, undo);
       a->ref[blk] = 1;
       s.table.push_back(blk);
-      if (undo) undo->popped.push_back(blk);
     } else if (a->ref[s.table[logical]] > 1) {
       const int32_t old = s.table[logical];
-      const int32_t fresh = a->free_list.front();
-      a->free_list.pop_front();
+      const int32_t fresh = take_block(a, undo);
       a->ref[old] -= 1;
       a->ref[fresh] = 1;
       s.table[logical] = fresh;
       cow_out.push_back(old);
       cow_out.push_back(fresh);
-      if (undo) {
-        undo->popped.push_back(fresh);
-        undo->cow.emplace_back(static_cast<int32_t>(logical), old);
-      }
+      if (undo) undo->cow.emplace_back(static_cast<int32_t>(logical), old);
     }
     slots[i] = static_cast<int64_t>(s.table[logical]) * b + p % b;
     s.len = p + 1;
@@ -103,7 +175,16 @@ void undo_append(pa_allocator* a, const AppendUndo& u) {
     a->ref[s.table.back()] = 0;
     s.table.pop_back();
   }
-  for (auto it = u.popped.rbegin(); it != u.popped.rend(); ++it) a->free_list.push_front(*it);
+  for (auto it = u.taken.rbegin(); it != u.taken.rend(); ++it) {
+    if (!it->reclaimed) {
+      a->free_list.push_front(it->block);
+      continue;
+    }
+    a->entries.emplace(it->key, it->eid);
+    a->entry.emplace(it->eid, pa_allocator::Entry{it->block, it->key});
+    a->block_entry[it->block] = it->eid;
+    a->evict_pos[it->block] = a->evictable.insert(a->evictable.begin(), it->block);
+  }
   s.len = u.old_len;
 }
 
@@ -130,6 +211,8 @@ pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t*
   a->num_blocks = num_blocks;
   a->block_size = block_size;
   a->ref.assign(num_blocks, 0);
+  a->block_entry.assign(num_blocks, 0);
+  a->evict_pos.resize(num_blocks);
   for (int32_t i = 0; i < num_blocks; ++i) a->free_list.push_back(order ? order[i] : i);
   *out = a;
   return pa_ok();
@@ -174,8 +257,7 @@ pa_status pa_alloc_append(pa_allocator* a, int64_t id, int32_t n, int64_t* slots
   if (n > 0 && !slots) return pa_fail(PA_ERR_INVALID, "pa_alloc_append: slots_out is null");
   pa_allocator::Seq& s = it->second;
   const int32_t need = blocks_needed(a, s, n);
-  if (need > static_cast<int32_t>(a->free_list.size()))
-    return pa_fail(PA_ERR_OOM, "pa_alloc_append: not enough free blocks");
+  if (need > available(a)) return pa_fail(PA_ERR_OOM, "pa_alloc_append: not enough free blocks");
   const int64_t b = a->block_size;
   const bool cow = n > 0 && s.len % b != 0 && a->ref[s.table[s.len / b]] > 1;
   if (cow && (cow_cap < 1 || !cow_pairs))
@@ -208,7 +290,7 @@ pa_status pa_alloc_append_batch(pa_allocator* a, const int64_t* ids, const int32
   for (int32_t i = 0; i < m; ++i) {
     pa_allocator::Seq& s = a->seqs[ids[i]];
     const int32_t need = blocks_needed(a, s, ns[i]);
-    if (need > static_cast<int32_t>(a->free_list.size())) {
+    if (need > available(a)) {
       for (auto it = undo.rbegin(); it != undo.rend(); ++it) undo_append(a, *it);
       return pa_fail(PA_ERR_OOM, "pa_alloc_append_batch: not enough free blocks");
     }
@@ -230,11 +312,89 @@ pa_status pa_alloc_free_seq(pa_allocator* a, int64_t id) {
   if (!a) return pa_fail(PA_ERR_INVALID, "allocator is null");
   auto it = a->seqs.find(id);
   if (it == a->seqs.end()) return pa_fail(PA_ERR_INVALID, "pa_alloc_free_seq: unknown sequence");
-  for (int32_t blk : it->second.table) {
-    a->ref[blk] -= 1;
-    if (a->ref[blk] == 0) a->free_list.push_back(blk);
-  }
+  for (int32_t blk : it->second.table) release_block(a, blk);
   a->seqs.erase(it);
+  return pa_ok();
+}
+
+pa_status pa_alloc_enable_prefix_cache(pa_allocator* a) {
+  if (!a) return pa_fail(PA_ERR_INVALID, "allocator is null");
+  a->caching = true;
+  return pa_ok();
+}
+
+pa_status pa_alloc_add_seq_prefix(pa_allocator* a, int64_t id, const int32_t* tokens, int32_t n_tokens,
+                                  int32_t* n_cached) {
+  if (!a || !n_cached) return pa_fail(PA_ERR_INVALID, "pa_alloc_add_seq_prefix: null argument");
+  *n_cached = 0;
+  if (n_tokens < 0 || (n_tokens > 0 && !tokens))
+    return pa_fail(PA_ERR_INVALID, "pa_alloc_add_seq_prefix: bad prompt");
+  if (a->seqs.count(id)) return pa_fail(PA_ERR_INVALID, "pa_alloc_add_seq_prefix: sequence exists");
+  pa_allocator::Seq& s = a->seqs.emplace(id, pa_allocator::Seq()).first->second;
+  if (!a->caching) return pa_ok();
+  const int64_t b = a->block_size;
+  pa_allocator::Key key{0, {}};
+  while ((static_cast<int64_t>(s.table.size()) + 1) * b <= static_cast<int64_t>(n_tokens) - 1) {
+    const int64_t j = static_cast<int64_t>(s.table.size());
+    key.tokens.assign(tokens + j * b, tokens + (j + 1) * b);
+    auto it = a->entries.find(key);
+    if (it == a->entries.end()) break;
+    const int32_t blk = a->entry[it->second].block;
+    if (a->ref[blk] == 0) a->evictable.erase(a->evict_pos[blk]);
+    a->ref[blk] += 1;
+    s.table.push_back(blk);
+    key.parent = it->second;
+  }
+  s.len = static_cast<int64_t>(s.table.size()) * b;
+  *n_cached = static_cast<int32_t>(s.len);
+  return pa_ok();
+}
+
+pa_status pa_alloc_cache_seq(pa_allocator* a, int64_t id, const int32_t* tokens, int64_t n_tokens) {
+  if (!a) return pa_fail(PA_ERR_INVALID, "allocator is null");
+  auto it = a->seqs.find(id);
+  if (it == a->seqs.end()) return pa_fail(PA_ERR_INVALID, "pa_alloc_cache_seq: unknown sequence");
+  if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return pa_fail(PA_ERR_INVALID, "pa_alloc_cache_seq: bad tokens");
+  if (n_tokens > it->second.len)
+    return pa_fail(PA_ERR_INVALID, "pa_alloc_cache_seq: more tokens than the sequence holds");
+  if (!a->caching) return pa_ok();
+  const int64_t b = a->block_size;
+  const auto& table = it->second.table;
+  pa_allocator::Key key{0, {}};
+  for (int64_t j = 0; j < n_tokens / b; ++j) {
+    key.tokens.assign(tokens + j * b, tokens + (j + 1) * b);
+    auto e = a->entries.find(key);
+    int64_t eid;
+    if (e != a->entries.end()) {
+      eid = e->second;
+    } else {
+      const int32_t blk = table[j];
+      if (a->block_entry[blk] != 0)
+        return pa_fail(PA_ERR_INVALID, "pa_alloc_cache_seq: a block is cached under other tokens");
+      eid = a->next_entry++;
+      a->entries.emplace(key, eid);
+      a->entry.emplace(eid, pa_allocator::Entry{blk, key});
+      a->block_entry[blk] = eid;
+    }
+    key.parent = eid;
+  }
+  return pa_ok();
+}
+
+pa_status pa_alloc_cache_stats(const pa_allocator* a, int32_t* num_cached, int32_t* num_evictable) {
+  if (!a) return pa_fail(PA_ERR_INVALID, "allocator is null");
+  if (num_cached) *num_cached = static_cast<int32_t>(a->entries.size());
+  if (num_evictable) *num_evictable = static_cast<int32_t>(a->evictable.size());
+  return pa_ok();
+}
+
+pa_status pa_alloc_evictable_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n_out) {
+  if (!a || !n_out) return pa_fail(PA_ERR_INVALID, "null argument");
+  *n_out = static_cast<int32_t>(a->evictable.size());
+  if (*n_out > cap) return pa_fail(PA_ERR_INVALID, "evictable list longer than cap");
+  if (*n_out > 0 && !out) return pa_fail(PA_ERR_INVALID, "out is null");
+  int32_t i = 0;
+  for (int32_t blk : a->evictable) out[i++] = blk;
   return pa_ok();
 }
 

@@ -1,5 +1,7 @@
 """Host-side tests of libpa (no GPU): exported symbols, the C++ allocator against the oracle's
-RefAllocator (bit-exact slots, tables, copy pairs, free order, counts), argument validation."""
+RefAllocator (bit-exact slots, tables, copy pairs, free order, counts, prefix-cache hits and eviction
+order), argument validation."""
+import copy
 import ctypes
 import os
 import re
@@ -25,7 +27,7 @@ def _header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _header_functions()
-    assert len(names) == 23
+    assert len(names) == 28
     handle = lib()
     for n in names:
         assert hasattr(handle, n), n
@@ -97,6 +99,154 @@ def test_cpp_allocator_matches_reference(ops, b, nblocks, seed):
             assert isinstance(ref_exc, AllocError) and e.status == PA_ERR_INVALID
         _same_state(c, r, list(r.tables))
     c.close()
+
+
+# ---- prefix cache: differential against the oracle -------------------------------------------
+
+_PROMPTS = [[7] * 40, [7] * 24 + [9] * 16, [1, 2, 3, 4] * 10, [7] * 8 + [5] * 3]
+
+_pop = st.one_of(
+    st.tuples(st.just("prefix"), st.integers(0, 5), st.integers(0, 3), st.integers(0, 40)),
+    st.tuples(st.just("fork"), st.integers(0, 5), st.integers(0, 5)),
+    st.tuples(st.just("append"), st.integers(0, 5), st.integers(0, 20)),
+    st.tuples(st.just("batch"), st.lists(st.tuples(st.integers(0, 5), st.integers(0, 12)), max_size=3)),
+    st.tuples(st.just("cache"), st.integers(0, 5), st.integers(0, 60)),
+    st.tuples(st.just("free"), st.integers(0, 5)),
+)
+
+
+def _same_cache(c: BlockAllocator, r: RefAllocator):
+    assert c.evictable_list() == r.evictable_list()
+    assert c.num_cached() == r.num_cached()
+    assert c.available() == r.available()
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(_pop, max_size=50), st.sampled_from([4, 8]), st.integers(3, 24), st.integers(0, 2**31))
+def test_cpp_prefix_cache_matches_reference(ops, b, nblocks, seed):
+    order = np.random.default_rng(seed).permutation(nblocks).astype(np.int32)
+    c, r = _both(nblocks, b, order)
+    c.enable_prefix_cache()
+    r.enable_prefix_cache()
+    content = {}                      # sid -> the token ids the sequence holds
+    nxt = [1000]
+
+    def fresh(n):
+        nxt[0] += n
+        return list(range(nxt[0] - n, nxt[0]))
+
+    for op in ops:
+        if op[0] == "prefix":
+            # a new request: attach its cached prefix, then take slots for the rest of its prompt
+            prompt = _PROMPTS[op[2]][:op[3]]
+            try:
+                n_r = r.add_seq_prefix(op[1], prompt)
+            except AllocError:
+                with pytest.raises(PaError):
+                    c.add_seq_prefix(op[1], prompt)
+                continue
+            assert c.add_seq_prefix(op[1], prompt) == n_r
+            content[op[1]] = list(prompt[:n_r])
+            op = ("append", op[1], len(prompt) - n_r, prompt[n_r:])
+        ref_exc, out_r, out_c = None, None, None
+        snap = copy.deepcopy(r) if op[0] == "batch" else None
+        try:
+            if op[0] == "fork":
+                r.fork(op[1], op[2])
+            elif op[0] == "append":
+                out_r = r.append(op[1], op[2])
+            elif op[0] == "batch":
+                ids = [sid for sid, _ in op[1]]
+                if len(set(ids)) != len(ids) or any(sid not in r.tables for sid in ids):
+                    raise AllocError("repeated or unknown sequence")   # checked before any append
+                out_r = [r.append(sid, n) for sid, n in op[1]]
+            elif op[0] == "cache":
+                if op[1] not in content:
+                    raise AllocError("unknown")
+                r.cache_seq(op[1], content[op[1]][:op[2]])
+            else:
+                r.free_seq(op[1])
+        except (AllocError, RefOOM) as e:
+            ref_exc = e
+            if snap is not None:
+                r = snap
+        try:
+            if op[0] == "fork":
+                c.fork(op[1], op[2])
+            elif op[0] == "append":
+                out_c = c.append(op[1], op[2])
+            elif op[0] == "batch":
+                out_c = c.append_batch([sid for sid, _ in op[1]], [n for _, n in op[1]])
+            elif op[0] == "cache":
+                c.cache_seq(op[1], content.get(op[1], [0] * op[2])[:op[2]])
+            else:
+                c.free_seq(op[1])
+            assert ref_exc is None, f"C++ accepted {op} that the reference refused: {ref_exc}"
+        except OutOfBlocks:
+            assert isinstance(ref_exc, RefOOM)
+        except PaError as e:
+            assert isinstance(ref_exc, AllocError) and e.status == PA_ERR_INVALID
+        if ref_exc is None:
+            if op[0] == "fork":
+                content[op[2]] = list(content[op[1]])
+            elif op[0] == "append":
+                assert out_c[0].tolist() == out_r[0]
+                assert [tuple(x) for x in out_c[1].tolist()] == out_r[1]
+                content[op[1]] = content[op[1]] + (list(op[3]) if len(op) > 3 else fresh(op[2]))
+            elif op[0] == "batch":
+                assert out_c[0].tolist() == [x for sl, _ in out_r for x in sl]
+                assert [tuple(x) for x in out_c[1].tolist()] == [p for _, cw in out_r for p in cw]
+                for sid, n in op[1]:
+                    content[sid] = content[sid] + fresh(n)
+            elif op[0] == "free":
+                del content[op[1]]
+        _same_state(c, r, list(r.tables))
+        _same_cache(c, r)
+        r.check_invariants()
+    c.close()
+
+
+def test_cpp_prefix_cache_shared_prompt():
+    """Ten requests behind one 1000-token system prompt share its 62 full blocks; each computes
+    only its own tail."""
+    b = 16
+    c = BlockAllocator(200, b)
+    c.enable_prefix_cache()
+    system = list(range(1000))
+    c.add_seq(0)
+    c.append(0, 1000)
+    c.cache_seq(0, system)
+    assert c.num_cached() == 62
+    free0 = c.num_free()
+    for s in range(1, 11):
+        prompt = system + [5000 + s] * 20
+        assert c.add_seq_prefix(s, prompt) == 992
+        c.append(s, len(prompt) - 992)
+    assert c.num_free() == free0 - 10 * 2        # 1020 - 992 = 28 tokens: two blocks each
+    assert all(c.table(s)[:62] == c.table(0)[:62] for s in range(1, 11))
+    assert c.refcount(c.table(0)[0]) == 11
+    c.free_seq(0)
+    for s in range(1, 11):
+        c.free_seq(s)
+    assert c.cache_stats() == (62, 62)
+    assert c.available() == 200
+
+
+def test_cpp_prefix_cache_errors():
+    c = BlockAllocator(8, 4)
+    with pytest.raises(PaError):
+        c.cache_seq(3, [1, 2, 3, 4])              # unknown sequence
+    c.enable_prefix_cache()
+    c.add_seq(1)
+    c.append(1, 4)
+    with pytest.raises(PaError):
+        c.cache_seq(1, [1, 2, 3, 4, 5])           # more tokens than the sequence holds
+    c.cache_seq(1, [1, 2, 3, 4])
+    with pytest.raises(PaError):
+        c.cache_seq(1, [4, 3, 2, 1])              # its block is cached under other tokens
+    with pytest.raises(PaError):
+        c.add_seq_prefix(1, [1, 2, 3])            # id exists
+    assert lib().pa_alloc_add_seq_prefix(c._h, 9, None, 3, ctypes.byref(ctypes.c_int32())) == PA_ERR_INVALID
 
 
 def test_cow_pairs_and_fill_tables():
