@@ -248,7 +248,10 @@ pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap, i
  *     exact token prefix;
  *   - a cached block whose count drops to zero is kept ("evictable", least recently released
  *     first) and reclaimed, entry dropped, only once the free list is empty: appends and OOM
- *     checks count free + evictable blocks, and a failed append restores the cache too.
+ *     checks count free + evictable blocks, and a failed append restores the cache too;
+ *   - pa_alloc_free_seq queues a sequence's cached blocks from its table's last block to its
+ *     first, so under pressure a cached prompt loses its deepest blocks first and the rest still
+ *     matches (a lookup always starts at a prompt's first block).
  * ------------------------------------------------------------------------------------------- */
 pa_status pa_alloc_enable_prefix_cache(pa_allocator* a);
 /* New sequence with prompt host int32 tokens[n_tokens]: its table starts with the longest run of

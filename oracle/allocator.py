@@ -26,7 +26,9 @@ Readings taken where the pages are silent:
     names one exact token prefix.  A new sequence takes the longest run of cached blocks matching
     its prompt, but always leaves at least one prompt token to compute.  A cached block whose count
     falls to zero is not freed but kept, least recently released first, and is reclaimed (its entry
-    dropped) only when the free list is empty.
+    dropped) only when the free list is empty.  The cached blocks one release leaves unreferenced
+    are queued from the table's last block to its first, so a chain loses its deepest blocks first
+    and its head stays matchable.
 """
 from collections import OrderedDict, deque
 from typing import Dict, List, Optional, Sequence, Tuple
@@ -79,13 +81,17 @@ class RefAllocator:
         self.block_entry[blk] = 0
         return blk
 
-    def _release(self, blk: int) -> None:
-        self.ref[blk] -= 1
-        if self.ref[blk] == 0:
-            if self.block_entry[blk]:
-                self.evictable[blk] = None
-            else:
+    def _release(self, table: Sequence[int]) -> None:
+        """Drop one reference to each block of a table.  Blocks left unreferenced join the free list
+        in table order, or, when cached, the evictable list from the table's last block to its first:
+        a lookup walks a chain from its first block, so the deepest blocks should go first."""
+        for blk in table:
+            self.ref[blk] -= 1
+            if self.ref[blk] == 0 and not self.block_entry[blk]:
                 self.free.append(blk)
+        for blk in reversed(table):
+            if self.ref[blk] == 0 and self.block_entry[blk]:
+                self.evictable[blk] = None
 
     # -- prefix cache -------------------------------------------------------------------------
     def add_seq_prefix(self, sid: int, tokens: Sequence[int]) -> int:
@@ -159,8 +165,7 @@ class RefAllocator:
         """Drop the sequence; blocks whose count reaches zero go back to the tail of the free list."""
         if sid not in self.tables:
             raise AllocError(f"unknown sequence {sid}")
-        for blk in self.tables[sid]:
-            self._release(blk)
+        self._release(self.tables[sid])
         del self.tables[sid]
         del self.lens[sid]
 

@@ -20,7 +20,8 @@
 // and the block's token ids); entry ids are never reused, so a key names one exact token prefix.  A
 // new sequence attaches the longest matching run of cached blocks but leaves at least one prompt
 // token to compute.  A cached block whose count falls to zero is kept, and is reclaimed (its entry
-// dropped), least recently released first, only when the free list is empty.
+// dropped), least recently released first, only when the free list is empty; one release queues
+// its cached blocks from the table's end, so chains shrink from their deepest block.
 #include <cstdint>
 #include <cstring>
 #include <deque>
@@ -112,15 +113,16 @@ int32_t take_block(pa_allocator* a, AppendUndo* undo) {
   return blk;
 }
 
-// One reference to `blk` dropped: at zero a cached block is kept (newest at the back), any other
-// block joins the free-list tail.
-void release_block(pa_allocator* a, int32_t blk) {
-  if (--a->ref[blk] != 0) return;
-  if (a->block_entry[blk] != 0) {
-    a->evict_pos[blk] = a->evictable.insert(a->evictable.end(), blk);
-  } else {
-    a->free_list.push_back(blk);
-  }
+// One reference to each block of a table dropped.  Unreferenced blocks join the free-list tail in
+// table order; unreferenced cached blocks are kept, queued (newest at the back) from the table's
+// last block to its first, so that a chain loses its deepest blocks first and its head, where every
+// lookup starts, stays matchable.
+void release_table(pa_allocator* a, const std::vector<int32_t>& table) {
+  for (int32_t blk : table)
+    if (--a->ref[blk] == 0 && a->block_entry[blk] == 0) a->free_list.push_back(blk);
+  for (auto it = table.rbegin(); it != table.rend(); ++it)
+    if (a->ref[*it] == 0 && a->block_entry[*it] != 0)
+      a->evict_pos[*it] = a->evictable.insert(a->evictable.end(), *it);
 }
 
 int32_t blocks_needed(const pa_allocator* a, const pa_allocator::Seq& s, int32_t n) {
@@ -312,7 +314,7 @@ pa_status pa_alloc_free_seq(pa_allocator* a, int64_t id) {
   if (!a) return pa_fail(PA_ERR_INVALID, "allocator is null");
   auto it = a->seqs.find(id);
   if (it == a->seqs.end()) return pa_fail(PA_ERR_INVALID, "pa_alloc_free_seq: unknown sequence");
-  for (int32_t blk : it->second.table) release_block(a, blk);
+  release_table(a, it->second.table);
   a->seqs.erase(it);
   return pa_ok();
 }

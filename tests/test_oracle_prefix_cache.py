@@ -79,12 +79,31 @@ def test_eviction_takes_the_least_recently_released_first():
     first, second = a.table(1)[:2], a.table(2)[:2]
     a.free_seq(1)
     a.free_seq(2)
-    assert a.evictable_list() == first + second and a.num_free() == 2
+    # each release queues its cached blocks deepest first
+    assert a.evictable_list() == first[::-1] + second[::-1] and a.num_free() == 2
     a.add_seq(3)
     a.append(3, 12)                          # 3 blocks: the 2 free ones, then the oldest cached one
-    assert a.table(3)[2] == first[0]
-    assert a.add_seq_prefix(4, p1) == 0      # p1's first block is gone, so nothing matches
+    assert a.table(3)[2] == first[1]
+    assert a.add_seq_prefix(4, p1) == 4      # p1 keeps its first block, so its head still matches
     assert a.add_seq_prefix(5, p2) == 8      # p2's blocks are intact
+    a.check_invariants()
+
+
+def test_eviction_order_keeps_the_longest_matchable_head():
+    """Under pressure a chain shrinks from its end: after k evictions the first (n - k) blocks of an
+    n-block prompt still match."""
+    b = 4
+    a = RefAllocator(10, b)
+    a.enable_prefix_cache()
+    p = _prompt(33, 9)                       # 8 full blocks + 1 partial
+    _serve(a, 1, p)
+    a.free_seq(1)                            # 8 cached idle, 2 free (the partial block and one unused)
+    for k in range(1, 7):
+        a.add_seq(100 + k)
+        a.append(100 + k, 4 if k > 1 else 12) # takes the 2 free blocks, then one cached block a time
+        assert a.num_cached() == 8 - k
+        assert a.add_seq_prefix(200 + k, p) == 4 * (8 - k)
+        a.free_seq(200 + k)
     a.check_invariants()
 
 
