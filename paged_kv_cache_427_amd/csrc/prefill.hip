@@ -12,14 +12,17 @@
 //    the G query heads that share the KV head, so one K/V tile in LDS serves every head of the group;
 //    each wave owns 32 rows;
 //  * key tiles of 64 positions are gathered through the block table and stored in LDS as bf16 (fp8
-//    e4m3 codes convert exactly; scales stay in fp32), double-buffered in LDS with one register
-//    stage: iteration t stores tile t + 1 and then issues the loads of tile t + 2 before computing
-//    tile t, so each load has about one iteration to arrive, and the loop body is not unrolled, so
-//    the accumulators keep their registers from tile to tile.  Every load instruction of a wave reads
-//    inside one pool block, so the table entries are wave-uniform scalar loads, and every load is
-//    issued unconditionally, so that the only wait for them is the one before the LDS store.  K
-//    tiles are stored [key][dim]; the V pool's dim-major tiles give [dim][key] rows directly, so V
-//    needs no transposition, only a fixed permutation of the keys inside each 16-key group;
+//    e4m3 codes convert exactly; scales stay in fp32), two K and two V^T buffers, one register stage
+//    each for K and V, loads issued about one iteration before their LDS store;
+//  * software pipeline: step t issues the score MFMAs of tile t + 1 beside the exponentials of tile
+//    t, then the O MFMAs of tile t beside the LDS stores and loads of later tiles, so each MFMA
+//    phase has independent vector work beside it; two steps per trip let the two score arrays
+//    trade roles without register copies;
+//  * every load instruction of a wave reads inside one pool block, so the table entries are
+//    wave-uniform scalar loads, and every load is issued unconditionally, so that the only wait for
+//    them is the one before the LDS store.  K tiles are stored [key][dim]; the V pool's dim-major
+//    tiles give [dim][key] rows directly, so V needs no transposition, only a fixed permutation of
+//    the keys inside each 16-key group;
 //  * scores are formed transposed, S^T = K Q^T (A = K rows from LDS, B = Q held in registers), so the
 //    fp32 result layout (each lane owns one query row and 16 keys) becomes, after bf16 rounding,
 //    exactly the B operand of O^T = V^T P^T; softmax statistics need one cross-half lane exchange;
@@ -41,6 +44,9 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// A plain vector type for 16-byte register stages: copies of the uint4 struct go through memcpy,
+// which can leave the loader's array in scratch memory.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;          // head_dim
 constexpr int kKT = 64;          // keys per tile
@@ -77,7 +83,7 @@ struct TileLoader {
   static constexpr int kKU = kKT * kCPR / kThreads;     // K chunks per thread (fp8 2, bf16 4)
   static constexpr int kVU = 4 * kD / kThreads;         // V pieces per thread (2)
   static constexpr int kVW = 16 * kE / 4;               // dwords of one 16-key piece (fp8 4, bf16 8)
-  uint4 k[kKU];
+  u32x4 k[kKU];
   uint32_t v[kVU][kVW];
 
   // K or V of tile keys [key0, key0 + 64).  Every load is issued unconditionally, so that the only
@@ -94,7 +100,7 @@ struct TileLoader {
       const int key = key0 + (u * kThreads + 64 * wave + lane) / kCPR;
       const int ch = lane % kCPR;
       const int64_t phys = tab[min(kw / BS, jlast)];
-      k[u] = *reinterpret_cast<const uint4*>(kpool + phys * blk_stride + head_off +
+      k[u] = *reinterpret_cast<const u32x4*>(kpool + phys * blk_stride + head_off +
                                              static_cast<int64_t>(key % BS) * kRowBytes + ch * 16);
     }
   }
@@ -143,9 +149,9 @@ struct TileLoader {
       const int ch = id % kCPR;
       char* dst = ks + key * kKStride;
       if constexpr (kE == 2) {
-        *reinterpret_cast<uint4*>(dst + ch * 16) = k[u];
+        *reinterpret_cast<u32x4*>(dst + ch * 16) = k[u];
       } else {
-        const uint4 c = k[u];
+        const u32x4 c = k[u];
         *reinterpret_cast<uint4*>(dst + ch * 32) = make_uint4(fp8x2_lo(c.x), fp8x2_hi(c.x), fp8x2_lo(c.y), fp8x2_hi(c.y));
         *reinterpret_cast<uint4*>(dst + ch * 32 + 16) =
             make_uint4(fp8x2_lo(c.z), fp8x2_hi(c.z), fp8x2_lo(c.w), fp8x2_hi(c.w));
@@ -278,40 +284,16 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   float l_run = 0.f;
   const float c2 = a.qk_scale;
 
-  // LDS: K and V^T of two tiles (double buffer).  Two register stages: the loads of tile t + 2 are
-  // issued while tile t is computed, and tile t + 1 (loaded one iteration earlier) is stored to LDS
-  // at the end of iteration t, so every load has two iterations to arrive.
+  // LDS: two K buffers and two V^T buffers.  Tile t's K sits in kbuf[t & 1], its V^T in vbuf[t & 1].
   char* const kbuf0 = smem;
   char* const kbuf1 = smem + kKBytes;
   char* const vbuf0 = smem + 2 * kKBytes;
   char* const vbuf1 = smem + 2 * kKBytes + kVBytes;
-
+  const int last = n_tiles - 1;
   TileLoader<KV, BS> ld;
-  ld.load_k(kpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
-  ld.load_v(vpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
-  ld.store_k(kbuf0, wave, lane);
-  ld.store_v(vbuf0, 0, n_keys, wave, lane);
-  ld.load_k(kpool, tab, blk_stride, head_off, min(1, n_tiles - 1) * kKT, n_keys, wave, lane);
-  ld.load_v(vpool, tab, blk_stride, head_off, min(1, n_tiles - 1) * kKT, n_keys, wave, lane);
-  __syncthreads();
 
-  // Iteration t: stores tile t + 1 (loaded during iteration t - 1) into the other LDS buffer, issues
-  // the loads of tile t + 2 into the same registers, then computes tile t.  One register stage, so
-  // the loop body is not unrolled and the accumulators keep their registers from one tile to the
-  // next.  Loads past the last tile re-read it (unused), so that they are unconditional.
-#pragma unroll 1
-  for (int t = 0; t < n_tiles; ++t) {
-    const bool odd = t & 1;
-    const char* kb = odd ? kbuf1 : kbuf0;
-    const char* vb = odd ? vbuf1 : vbuf0;
-    ld.store_k(odd ? kbuf0 : kbuf1, wave, lane);
-    ld.store_v(odd ? vbuf0 : vbuf1, min(t + 1, n_tiles - 1) * kKT, n_keys, wave, lane);
-    const int t2 = min(t + 2, n_tiles - 1) * kKT;
-    ld.load_k(kpool, tab, blk_stride, head_off, t2, n_keys, wave, lane);
-    ld.load_v(vpool, tab, blk_stride, head_off, t2, n_keys, wave, lane);
-
-    // ---- S^T = K Q^T for two 32-key halves ----
-    f32x16 s[2];
+  // S^T = K Q^T of the tile whose K rows are in kb, as two 32-key halves.
+  auto scores = [&](const char* kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
@@ -323,8 +305,20 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
         s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[c], s[sb], 0, 0, 0);
       }
     }
+  };
 
-    // ---- causal mask (tiles crossing the diagonal only), running max of the raw scores ----
+  // Software pipeline.  On entry to step t: sc = S(t); K(t + 1) and V(t) are in LDS; the registers
+  // hold V(t + 1) and K(t + 2) (loaded, or in flight).  Step t
+  //   1. masks tile t (tiles crossing the diagonal only), takes its max, rescales if needed;
+  //   2. issues the MFMAs of S(t + 1) into sn beside the exponentials of tile t, then stores V(t + 1)
+  //      into vbuf[(t + 1) & 1] and issues the loads of V(t + 2);
+  //   3. issues O += V(t) P(t) beside the store of K(t + 2) into kbuf[t & 1] (K(t) is done) and the
+  //      loads of K(t + 3);
+  //   4. waits at the barrier, after which every buffer written in 2 and 3 is visible and every
+  //      buffer read in 2 and 3 may be overwritten.
+  // Tiles past the last one are read as the last one (their results are unused).
+  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
+    const bool odd = t & 1;
     const int key_base = t * kKT;
     if (key_base + kKT - 1 > P + q0) {
 #pragma unroll
@@ -332,14 +326,14 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key_base + sb * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-          s[sb][r] = key <= qpos ? s[sb][r] : -INFINITY;
+          sc[sb][r] = key <= qpos ? sc[sb][r] : -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[sb][r]);
     mx = fmaxf(mx, shfl_xor(mx, 32)) * c2;     // base-2 logit units (c2 > 0)
     // rescale only when the max moved by more than the slack (wave-uniform decision)
     const bool grow = mx > m_run + kRescaleSlack;
@@ -355,31 +349,57 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
     }
     const float nm = m_run == -INFINITY ? 0.f : -m_run;
 
-    // ---- P^T = 2^(c2 S^T - m) as bf16 B operands; row sums ----
+    scores(odd ? kbuf0 : kbuf1, sn);
     bf16x8 pb[4];
     float lsum = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c / 2][8 * (c % 2) + e], c2, nm));
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c / 2][8 * (c % 2) + e], c2, nm));
         lsum += p;
         pb[c][e] = static_cast<__bf16>(p);
       }
     l_run += lsum + shfl_xor(lsum, 32);
+    ld.store_v(odd ? vbuf0 : vbuf1, min(t + 1, last) * kKT, n_keys, wave, lane);
+    ld.load_v(vpool, tab, blk_stride, head_off, min(t + 2, last) * kKT, n_keys, wave, lane);
 
-    // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const char* vrow = vb + (dt * 32 + (lane & 31)) * kVStride + 16 * h;
+      const char* vrow = (odd ? vbuf1 : vbuf0) + (dt * 32 + (lane & 31)) * kVStride + 16 * h;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + 32 * c);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], o[dt], 0, 0, 0);
       }
     }
+    ld.store_k(odd ? kbuf1 : kbuf0, wave, lane);
+    ld.load_k(kpool, tab, blk_stride, head_off, min(t + 3, last) * kKT, n_keys, wave, lane);
     __syncthreads();
+  };
+
+  // Prologue: K(0), V(0) to LDS; S(0); K(1) to LDS; V(1) and K(2) left in registers.
+  ld.load_k(kpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+  ld.load_v(vpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+  ld.store_k(kbuf0, wave, lane);
+  ld.store_v(vbuf0, 0, n_keys, wave, lane);
+  ld.load_k(kpool, tab, blk_stride, head_off, min(1, last) * kKT, n_keys, wave, lane);
+  ld.load_v(vpool, tab, blk_stride, head_off, min(1, last) * kKT, n_keys, wave, lane);
+  __syncthreads();
+  f32x16 sa[2], sb2[2];
+  scores(kbuf0, sa);
+  ld.store_k(kbuf1, wave, lane);
+  ld.load_k(kpool, tab, blk_stride, head_off, min(2, last) * kKT, n_keys, wave, lane);
+  __syncthreads();
+
+  // Two steps per trip so that the score arrays trade roles without register copies.
+  int t = 0;
+#pragma unroll 1
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, sa, sb2);
+    step(t + 1, sb2, sa);
   }
+  if (t < n_tiles) step(t, sa, sb2);
 
   // ---- out[token][head][d] = O^T[d][row] / l ----
   if (!row_ok) return;
