@@ -312,6 +312,15 @@ def main():
         fl = prefill_flops(wl)
         res["prefill_tflops"] = round(fl / (ms_prefill * 1e-3) / 1e12, 1)
         res["prefill_mfma_frac"] = round(fl / (ms_prefill * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+    if len(si.host_cow):
+        # copy-on-write copies: each pair reads and writes one whole block, K and V, all KV heads
+        blk = 2 * wl.num_kv_heads * wl.block_size * wl.head_dim * elem_bytes(wl.kv_dtype)
+        moved = 2 * len(si.host_cow) * blk
+        res["copy_roofline"] = {"bound": "hbm", "achieved": round(moved / (ms_copy * 1e-3) / 1e9, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(moved / (ms_copy * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "kernel": "pa_copy_blocks", "pairs": int(len(si.host_cow)),
+                                "algorithmic_bytes_per_launch": int(moved)}
     res["kernel_ms"] = {"copy_blocks": round(ms_copy, 4), "cache_write": round(ms_write, 4),
                         "prefill": round(ms_prefill, 4), "decode": round(ms_decode, 4)}
     res["config"] = cfg

@@ -25,7 +25,8 @@ from typing import List, Optional, Tuple
 import numpy as np
 import torch
 
-CONFIG_NAMES = ("tiny_fp32", "llama7b_bf16", "shared_prefix_bf16", "gqa_long_bf16", "mixed_fp8")
+CONFIG_NAMES = ("tiny_fp32", "llama7b_bf16", "shared_prefix_bf16", "gqa_long_bf16", "mixed_fp8",
+                "fork_storm_bf16")
 SEED_BASE = 4270
 
 _ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
@@ -158,6 +159,7 @@ def make_workload(name: str, size: str = "full", device="cpu", block_size: Optio
         "shared_prefix_bf16": _shared_prefix_bf16,
         "gqa_long_bf16": _gqa_long_bf16,
         "mixed_fp8": _mixed_fp8,
+        "fork_storm_bf16": _fork_storm_bf16,
     }[name]
     return builder(name, size, rng, gen, device, block_size)
 
@@ -278,6 +280,53 @@ def _shared_prefix_bf16(name, size, rng, gen, device, block_size):
         history=history, step=step, post=post, k_tok=k.to(torch.bfloat16), v_tok=v.to(torch.bfloat16),
         decode_seqs=list(range(bsz)), decode_lens=np.asarray(lens, np.int32), q_decode=q,
         notes=f"{prefix}-token prefix shared by all {bsz} sequences; one CoW per sequence in the step")
+
+
+def _fork_storm_bf16(name, size, rng, gen, device, block_size):
+    """Beam search / parallel sampling (the Day 28 page, §六 question 3: candidate branches share
+    their prompt's blocks): every request is forked into W branches that share all its blocks, then
+    each branch writes its next token.  All but the last writer of a request copy the shared tail
+    block, so one step carries (W - 1) copies per request before the decode of all branches."""
+    b = block_size or 16
+    hq = hkv = 32
+    d = 128
+    if size == "full":
+        n_req, width, lo, hi = 128, 8, 512, 2048
+    else:
+        n_req, width, lo, hi = 3, 4, 20, 90
+    lens = []
+    for _ in range(n_req):
+        while True:
+            L = int(rng.integers(lo, hi, endpoint=True))
+            if L % b != 0:      # a partly filled tail block, so the branches' writes copy it
+                break
+        lens.append(L)
+    needed = sum(_ceil_div(L, b) + width - 1 for L in lens)
+    nb = _pool_blocks(needed)
+    free_order = rng.permutation(nb).astype(np.int32)
+    sc = _Script()
+    for r, L in enumerate(lens):
+        sc.add(r * width)
+        sc.append(r * width, L)
+        for j in range(1, width):
+            sc.fork(r * width, r * width + j)
+    history = sc.take()
+    seqs = [r * width + j for r in range(n_req) for j in range(width)]
+    for sid in seqs:
+        sc.append(sid, 1)
+    step = sc.take()
+    t = sc.next_tok
+    bsz = len(seqs)
+    q = _q(gen, device, bsz, hq, d, "bf16")
+    k, v = _draw_tokens(gen, device, t, hkv, d, "bf16")
+    return Workload(
+        name=name, size=size, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=b,
+        kv_dtype="bf16", act_dtype="bf16", num_blocks=nb, free_order=free_order,
+        scale=_fp32(1.0 / math.sqrt(d)), k_scale=1.0, v_scale=1.0,
+        history=history, step=step, post=[], k_tok=k.to(torch.bfloat16), v_tok=v.to(torch.bfloat16),
+        decode_seqs=seqs, decode_lens=np.asarray([lens[s // width] for s in seqs], np.int32), q_decode=q,
+        notes=f"{n_req} requests x {width} branches sharing every prompt block; "
+              f"{n_req * (width - 1)} copy-on-write copies in the step")
 
 
 def _mixed_fp8(name, size, rng, gen, device, block_size):

@@ -15,7 +15,7 @@ from synth import make_workload, poison_code
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
-SMALL = ["tiny_fp32", "llama7b_bf16", "shared_prefix_bf16", "gqa_long_bf16", "mixed_fp8"]
+SMALL = ["tiny_fp32", "llama7b_bf16", "shared_prefix_bf16", "gqa_long_bf16", "mixed_fp8", "fork_storm_bf16"]
 
 
 def _engine():
@@ -197,7 +197,7 @@ def test_prefill_variants(kv, hq, hkv, b):
 
 # ---- full-size workloads: sampled outputs against the pool-free dense oracle ---------------------
 
-FULL = ["llama7b_bf16", "shared_prefix_bf16", "gqa_long_bf16", "mixed_fp8"]
+FULL = ["llama7b_bf16", "shared_prefix_bf16", "gqa_long_bf16", "mixed_fp8", "fork_storm_bf16"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -208,7 +208,9 @@ def test_full_size_sampled(name):
     eng.build_history()
     si = eng.prepare_step()
     if len(si.host_cow):
-        k_before = eng.k_pool[torch.as_tensor(si.host_cow[:4, 0].astype(np.int64), device="cuda")].clone()
+        src_all = torch.as_tensor(si.host_cow[:, 0].astype(np.int64), device="cuda")
+        k_before = eng.k_pool[src_all].clone()
+        v_before = eng.v_pool[src_all].clone()
     eng.run_step(si)
     torch.cuda.synchronize()
     lg = logical_view(wl)
@@ -226,18 +228,20 @@ def test_full_size_sampled(name):
         _say(name, "decode sampled max err", worst)
         assert worst <= tol
     if len(si.host_cow):
-        # the copy holds the source block's rows; the old block is untouched by the step's write
-        cow = si.host_cow[:4]
+        # every copy holds its source block's rows below the new token; sources the step did not
+        # write to are untouched (bit patterns: unused rows hold the NaN poison)
+        cow = si.host_cow
         src = torch.as_tensor(cow[:, 0].astype(np.int64), device="cuda")
         dst = torch.as_tensor(cow[:, 1].astype(np.int64), device="cuda")
-        # compare bit patterns: unused rows hold the NaN poison
-        assert torch.equal(eng.k_pool[src].view(torch.int16), k_before.view(torch.int16))
         b = wl.block_size
+        bits = torch.int16 if wl.kv_dtype == "bf16" else torch.uint8
+        slot_in = {int(x) // b: int(x) for x in si.host_slots}    # the step token written to each block
         for i in range(len(cow)):
-            s = int(si.host_slots[i])
-            assert s // b == int(cow[i, 1])
-            off = s % b
-            assert torch.equal(eng.k_pool[dst[i], :, :off].view(torch.int16), k_before[i, :, :off].view(torch.int16))
+            off = slot_in[int(cow[i, 1])] % b
+            assert torch.equal(eng.k_pool[dst[i], :, :off].view(bits), k_before[i, :, :off].view(bits))
+            assert torch.equal(eng.v_pool[dst[i], :, :, :off].view(bits), v_before[i, :, :, :off].view(bits))
+            if int(cow[i, 0]) not in slot_in:
+                assert torch.equal(eng.k_pool[src[i]].view(bits), k_before[i].view(bits))
     # sampled step tokens: the slot holds exactly the token's row (fp8: its quantised codes)
     from oracle import e4m3_quantise
     s0, _ = wl.step_token_range()

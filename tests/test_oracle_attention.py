@@ -122,7 +122,8 @@ def test_tiny_workload_against_pure_python_loops():
 
 # ---- paged == dense, permutation invariance, shared prefix -------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "llama7b_bf16", "shared_prefix_bf16", "mixed_fp8"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama7b_bf16", "shared_prefix_bf16", "mixed_fp8",
+                                  "fork_storm_bf16"])
 def test_paged_equals_dense(name):
     wl = make_workload(name, "small")
     res = run_paged(wl)
@@ -136,6 +137,24 @@ def test_paged_equals_dense(name):
         rows = [0, c // 2, c - 1]
         got = res.prefill_out[start:start + c][rows]
         assert np.array_equal(got, dense_prefill(wl, si, rows, heads, lg))
+
+
+def test_fork_storm_copies_all_but_the_last_writer():
+    """Beam branches share all their prompt's blocks (the Day 28 page, §六 question 3); each branch's
+    write into the shared tail copies it first, except the last writer, which finds the block
+    private again and keeps it (§六 item 4)."""
+    wl = make_workload("fork_storm_bf16", "small")
+    res = run_paged(wl)
+    n_req, width = 3, 4
+    assert len(wl.decode_seqs) == n_req * width
+    assert len(res.step_cow) == n_req * (width - 1)
+    for r in range(n_req):
+        tabs = [res.tables[r * width + j] for j in range(width)]
+        assert all(t[:-1] == tabs[0][:-1] for t in tabs)
+        assert len({t[-1] for t in tabs}) == width
+        pairs = res.step_cow[r * (width - 1):(r + 1) * (width - 1)]
+        assert {int(a) for a, _ in pairs} == {tabs[-1][-1]}
+        assert [int(b) for _, b in pairs] == [t[-1] for t in tabs[:-1]]
 
 
 def test_result_independent_of_physical_block_order():
