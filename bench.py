@@ -8,7 +8,8 @@ already resident in HBM.  The default workload is the shared-prefix decode (256 
 512-token shared prefix plus a private suffix of 512..2560 tokens, 40 query = 40 KV heads,
 head_dim 128, bf16, 16-token blocks, one copy-on-write per sequence).  `--config prefix_cache_bf16`
 instead times 64 prompts behind one shared 1000-token system prompt, prefilled through the prefix
-cache and, for comparison, in full without it.
+cache and, for comparison, in full without it; `--config swap_llama7b_bf16` times the swap of every
+sequence of the Llama-7B-shaped decode workload to pinned host memory and back.
 
 Prints one JSON line.  `value` is the decode's unique KV bytes per step (each physical block once)
 divided by the step time, in GB/s.  `roofline` prices the decode launch (plan, stream and merge kernels),
@@ -220,6 +221,89 @@ def prefix_cpu_baseline(b, pc, budget_s: float):
                       f"fp64 NumPy, {spent:.1f} s"}
 
 
+HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def swap_bench(args, dev):
+    """Swap-out of every sequence of the Llama-7B-shaped decode workload to a pinned host pool and
+    swap-in back (pa_alloc_move_seq on the host, one pa_swap_blocks launch per direction), timed per
+    direction with HIP events; a plain DMA copy of the same bytes is timed beside it."""
+    from paged_kv_cache_427_amd.engine import PagedKVEngine
+    from paged_kv_cache_427_amd.allocator import BlockAllocator, move_seq
+    from paged_kv_cache_427_amd.ops import make_pool_desc, pa_swap_blocks
+    from paged_kv_cache_427_amd._lib import PA_BF16
+    wl = make_workload("llama7b_bf16", "full", device=dev)
+    eng = PagedKVEngine(wl, device=dev, poison=poison_code(wl.kv_dtype))
+    eng.build_history()
+    si = eng.prepare_step()
+    eng.run_step(si)
+    torch.cuda.synchronize()
+    ref_out = si.dec_out.clone()
+    sids = list(wl.decode_seqs)
+    n_host = sum(len(eng.alloc.table(s)) for s in sids)
+    hk = torch.empty((n_host,) + tuple(eng.k_pool.shape[1:]), dtype=eng.k_pool.dtype, pin_memory=True)
+    hv = torch.empty((n_host,) + tuple(eng.v_pool.shape[1:]), dtype=eng.v_pool.dtype, pin_memory=True)
+    hpool = make_pool_desc(n_host, wl.block_size, wl.num_kv_heads, wl.head_dim, PA_BF16)
+    host = BlockAllocator(n_host, wl.block_size)
+    blk = 2 * wl.num_kv_heads * wl.block_size * wl.head_dim * elem_bytes(wl.kv_dtype)
+    stream = torch.cuda.current_stream()
+    t_out, t_in = [], []
+    for i in range(args.warmup + args.steps):
+        p_out = np.concatenate([move_seq(eng.alloc, host, s) for s in sids])
+        pt = torch.as_tensor(p_out, device=dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        pa_swap_blocks(hk, hv, hpool, eng.k_pool, eng.v_pool, eng.pool, pt)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        p_in = np.concatenate([move_seq(host, eng.alloc, s) for s in sids])
+        pt = torch.as_tensor(p_in, device=dev)
+        e[2].record(stream)
+        pa_swap_blocks(eng.k_pool, eng.v_pool, eng.pool, hk, hv, hpool, pt)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            t_out.append(e[0].elapsed_time(e[1]))
+            t_in.append(e[2].elapsed_time(e[3]))
+    # the sequences now live in other device blocks; decode must give the same bits as before
+    mb = si.dec_tables.shape[1]
+    si.dec_tables = torch.as_tensor(eng.alloc.fill_tables(sids, mb), device=dev)
+    eng.decode_step(si)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(si.dec_out.view(torch.int16), ref_out.view(torch.int16)))
+    nbytes = len(p_out) * blk
+    ms_out, ms_in = float(np.mean(t_out)), float(np.mean(t_in))
+    # DMA reference: one contiguous copy of the same bytes each way
+    dbuf = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    hbuf = torch.empty(nbytes // 2, dtype=torch.int16, pin_memory=True)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record(stream)
+    hbuf.copy_(dbuf, non_blocking=True)
+    e[1].record(stream)
+    dbuf.copy_(hbuf, non_blocking=True)
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    dma_out, dma_in = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+    gbs_out, gbs_in = nbytes / (ms_out * 1e-3) / 1e9, nbytes / (ms_in * 1e-3) / 1e9
+    return {"metric": "swap of a whole decode batch between HBM and pinned host memory: GB/s per direction",
+            "value": round(min(gbs_out, gbs_in), 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_out + ms_in, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (the Llama-7B-shaped decode workload's K/V)",
+            "swap_out": {"GBps": round(gbs_out, 2), "ms": round(ms_out, 4)},
+            "swap_in": {"GBps": round(gbs_in, 2), "ms": round(ms_in, 4)},
+            "dma_copy_same_bytes": {"out_GBps": round(nbytes / (dma_out * 1e-3) / 1e9, 2),
+                                    "in_GBps": round(nbytes / (dma_in * 1e-3) / 1e9, 2)},
+            "decode_identical_after_round_trip": same,
+            "roofline": {"bound": "pcie", "achieved": round(min(gbs_out, gbs_in), 2), "peak": HOST_LINK_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(min(gbs_out, gbs_in) / HOST_LINK_PEAK_GBS, 4),
+                         "traffic": None, "kernel": "pa_swap_blocks (copy_blocks_kernel over the host link)",
+                         "algorithmic_bytes_per_launch": int(nbytes)},
+            "config": {"workload": "swap_llama7b_bf16", "sequences": len(sids), "blocks": int(len(p_out)),
+                       "block_bytes": blk, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+                       "head_dim": wl.head_dim, "block_size": wl.block_size}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +330,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.config == "prefix_cache_bf16":
         print(json.dumps(prefix_cache_bench(args, dev)), flush=True)
+        return
+    if args.config == "swap_llama7b_bf16":
+        print(json.dumps(swap_bench(args, dev)), flush=True)
         return
     t_setup = time.time()
     wl = make_workload(args.config, "full", device=dev, block_size=args.block_size)

@@ -113,6 +113,26 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool, c
                          int32_t num_pairs, pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * pa_swap_blocks -- whole-block copies from one pool to another of the same block format: the
+ * data movement of a swap-out (device pool -> pinned host pool) or swap-in (host -> device) of a
+ * preempted sequence ([day28] §六 question 4).
+ *
+ *   dst_*  destination K and V pools and their descriptor
+ *   src_*  source K and V pools and their descriptor (num_blocks may differ; block_size,
+ *          num_kv_heads, head_dim, dtype and the fp8 scales must be equal: codes move unchanged)
+ *   pairs  int32 [num_pairs][2] = (source block, destination block), as pa_alloc_move_seq
+ *          returns them, in device or pinned host memory.  Destinations must be distinct.
+ * Each pool pointer must be device memory or pinned host memory (hipHostMalloc), which the kernel
+ * reaches over the host link; anything else (pageable memory, unknown pointers) is refused with
+ * PA_ERR_INVALID before any launch.  Block ids are not checked (out of range is undefined
+ * behaviour).  One kernel launch on the stream, asynchronous like every call here: the pools and
+ * the pairs must stay allocated, and unchanged, until it completes.  num_pairs == 0 is a no-op.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const pa_pool_desc* dst_pool,
+                         const void* src_k_pool, const void* src_v_pool, const pa_pool_desc* src_pool,
+                         const int32_t* pairs, int32_t num_pairs, pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for these sizes, on the
  * current device (the size depends on its compute-unit count).
  *   partition_size 0 means the library's choice (the same choice pa_decode makes for 0).
@@ -266,6 +286,20 @@ pa_status pa_alloc_add_seq_prefix(pa_allocator* a, int64_t seq_id, const int32_t
  * sequence is unknown, n_tokens exceeds its length, or one of its blocks is cached under other
  * tokens (entries registered before the error stay). */
 pa_status pa_alloc_cache_seq(pa_allocator* a, int64_t seq_id, const int32_t* tokens, int64_t n_tokens);
+/* ---------------------------------------------------------------------------------------------
+ * Swap of a preempted sequence between two pools of one block format, each with its own allocator
+ * (say the device pool and a pinned host pool).  [day28] §六 question 4 (preemption swaps a
+ * request's KV cache to CPU memory; paging makes that a copy of the blocks its table lists) and
+ * FAQ Q3 (memory can still run out).  Every block of the sequence's table gets a block from dst's
+ * supply (free list, then idle cached blocks), in table order; the sequence keeps its length and
+ * id and is then freed in src like a finished one (a block it shared keeps its other references).
+ * The (src block, dst block) pairs go to host int32 pairs_out[cap][2], *n_pairs_out = their count
+ * (= the table length); run pa_swap_blocks on them before the freed src blocks are reused.
+ * PA_ERR_OOM (both states unchanged) if dst cannot supply every block; PA_ERR_INVALID if the id is
+ * unknown in src or exists in dst, the block sizes differ, src == dst, or cap is too small.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_alloc_move_seq(pa_allocator* src, pa_allocator* dst, int64_t seq_id, int32_t* pairs_out,
+                            int32_t cap, int32_t* n_pairs_out);
 /* Number of cache entries and of evictable blocks (either pointer may be NULL). */
 pa_status pa_alloc_cache_stats(const pa_allocator* a, int32_t* num_cached, int32_t* num_evictable);
 /* The evictable blocks, least recently released first, into host int32 out[cap]; *n_out = count. */

@@ -19,9 +19,11 @@ from .sizes import kv_bytes_per_token, kv_cache_bytes  # noqa: F401
 from .codecs import (  # noqa: F401
     bf16_bits_to_f64, f32_bits_to_f64, e4m3_decode, e4m3_encode, e4m3_quantise, decode_pool,
 )
-from .allocator import RefAllocator, AllocError, OutOfBlocks  # noqa: F401
+from .allocator import RefAllocator, AllocError, OutOfBlocks, move_seq  # noqa: F401
 from .logical import LogicalSeqs  # noqa: F401
-from .cache import slot_of, pool_shape, ref_cache_write, ref_copy_blocks, gather_seq  # noqa: F401
+from .cache import (  # noqa: F401
+    slot_of, pool_shape, ref_cache_write, ref_copy_blocks, ref_move_blocks, gather_seq,
+)
 from .attention import (  # noqa: F401
     attend, ref_decode, ref_decode_split, partition_stats, merge_partitions, ref_prefill,
 )

@@ -267,3 +267,35 @@ class RefAllocator:
         cached = {blk for blk in range(self.num_blocks) if self.block_entry[blk]}
         assert cached == set(self.entry_block.values())
         assert idle == {blk for blk in cached if self.ref[blk] == 0}
+
+
+def move_seq(src: RefAllocator, dst: RefAllocator, sid) -> List[Tuple[int, int]]:
+    """Move sequence `sid` from the pool `src` manages to the pool `dst` manages: swap-out (device
+    to host) or swap-in (host to device) of a preempted request ([day28] §六 question 4: preemption
+    swaps a request's KV cache out to CPU memory, which paging makes a matter of copying the blocks
+    its table lists; FAQ Q3: memory can still run out under paging).
+
+    Reading: every block of the table gets a fresh block from dst's supply (free list, then idle
+    cached blocks), in table order, and the sequence keeps its length; then the sequence is freed in
+    src like any finished one, so a block it shared with another sequence stays in src with one
+    reference less.  All-or-nothing: OutOfBlocks, with both states unchanged, when dst cannot supply
+    every block.  Returns the (src block, dst block) pairs whose content must be copied."""
+    if src.block_size != dst.block_size:
+        raise AllocError("the two pools have different block sizes")
+    if sid not in src.tables:
+        raise AllocError(f"unknown sequence {sid}")
+    if sid in dst.tables:
+        raise AllocError(f"sequence {sid} exists in the destination")
+    table = src.tables[sid]
+    if len(table) > dst.available():
+        raise OutOfBlocks(f"sequence {sid}: need {len(table)} blocks, {dst.available()} available")
+    dst.add_seq(sid)
+    pairs = []
+    for blk in table:
+        nb = dst._take()
+        dst.ref[nb] = 1
+        dst.tables[sid].append(nb)
+        pairs.append((blk, nb))
+    dst.lens[sid] = src.lens[sid]
+    src.free_seq(sid)
+    return pairs

@@ -77,6 +77,13 @@ def ref_copy_blocks(pool: np.ndarray, pairs: Sequence) -> None:
         pool[int(dst)] = pool[int(src)].copy()
 
 
+def ref_move_blocks(dst_pool: np.ndarray, src_pool: np.ndarray, pairs: Sequence) -> None:
+    """Swap: block d of dst_pool receives block s of src_pool, for each (s, d) pair ([day28] §六
+    question 4).  The two pools hold blocks of one format; stored codes move unchanged."""
+    for src, dst in pairs:
+        dst_pool[int(dst)] = src_pool[int(src)].copy()
+
+
 def gather_seq(pool_vals: np.ndarray, table: Sequence[int], length: int, which: str = "k") -> np.ndarray:
     """Contiguous [length, Hkv, D] K (which="k") or V (which="v") of a sequence, rebuilt through its
     block table ([day28] §三 3.1: the kernel reaches scattered K/V by indirection through the table)."""

@@ -39,6 +39,8 @@ _PROTOS = {
     "pa_cache_write": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_void_p, c_void_p, c_void_p,
                                  POINTER(PoolDesc), c_void_p]),
     "pa_copy_blocks": (c_int32, [c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_int32, c_void_p]),
+    "pa_swap_blocks": (c_int32, [c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_void_p, POINTER(PoolDesc),
+                                 c_void_p, c_int32, c_void_p]),
     "pa_decode_workspace_size": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_size_t)]),
     "pa_decode": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_int32,
                             c_void_p, c_int32, c_int32, c_float, c_int32, c_int32, c_void_p, c_size_t,
@@ -65,6 +67,7 @@ _PROTOS = {
     "pa_alloc_add_seq_prefix": (c_int32, [c_void_p, c_int64, _I32P, c_int32, _I32P]),
     "pa_alloc_cache_seq": (c_int32, [c_void_p, c_int64, _I32P, c_int64]),
     "pa_alloc_cache_stats": (c_int32, [c_void_p, _I32P, _I32P]),
+    "pa_alloc_move_seq": (c_int32, [c_void_p, c_void_p, c_int64, _I32P, c_int32, _I32P]),
     "pa_alloc_evictable_list": (c_int32, [c_void_p, _I32P, c_int32, _I32P]),
 }
 

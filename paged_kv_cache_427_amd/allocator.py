@@ -149,3 +149,13 @@ class BlockAllocator:
         buf = np.empty(max(self.num_blocks, 1), dtype=np.int32)
         check(lib().pa_alloc_evictable_list(self._h, _i32p(buf), self.num_blocks, ctypes.byref(n)))
         return buf[:n.value].tolist()
+
+
+def move_seq(src: BlockAllocator, dst: BlockAllocator, sid: int) -> np.ndarray:
+    """Move a sequence between two pools' allocators (swap-out or swap-in); returns the int32 [n, 2]
+    (source block, destination block) pairs to copy with pa_swap_blocks."""
+    n = ctypes.c_int32(0)
+    cap = max(src.num_blocks, 1)
+    buf = np.empty((cap, 2), dtype=np.int32)
+    check(lib().pa_alloc_move_seq(src._h, dst._h, int(sid), _i32p(buf), cap, ctypes.byref(n)))
+    return buf[:n.value].copy()

@@ -383,6 +383,37 @@ pa_status pa_alloc_cache_seq(pa_allocator* a, int64_t id, const int32_t* tokens,
   return pa_ok();
 }
 
+pa_status pa_alloc_move_seq(pa_allocator* src, pa_allocator* dst, int64_t id, int32_t* pairs, int32_t cap,
+                            int32_t* n_pairs) {
+  if (!src || !dst || !n_pairs) return pa_fail(PA_ERR_INVALID, "pa_alloc_move_seq: null argument");
+  *n_pairs = 0;
+  if (src == dst) return pa_fail(PA_ERR_INVALID, "pa_alloc_move_seq: source and destination are one allocator");
+  if (src->block_size != dst->block_size)
+    return pa_fail(PA_ERR_INVALID, "pa_alloc_move_seq: the pools have different block sizes");
+  auto it = src->seqs.find(id);
+  if (it == src->seqs.end()) return pa_fail(PA_ERR_INVALID, "pa_alloc_move_seq: unknown sequence");
+  if (dst->seqs.count(id)) return pa_fail(PA_ERR_INVALID, "pa_alloc_move_seq: sequence exists in the destination");
+  const std::vector<int32_t>& table = it->second.table;
+  const int64_t n = static_cast<int64_t>(table.size());
+  if (n > cap || (n > 0 && !pairs)) return pa_fail(PA_ERR_INVALID, "pa_alloc_move_seq: pairs_out too small");
+  if (n > available(dst)) return pa_fail(PA_ERR_OOM, "pa_alloc_move_seq: not enough blocks in the destination");
+  pa_allocator::Seq moved;
+  moved.len = it->second.len;
+  moved.table.reserve(table.size());
+  for (size_t j = 0; j < table.size(); ++j) {
+    const int32_t blk = take_block(dst, nullptr);
+    dst->ref[blk] = 1;
+    moved.table.push_back(blk);
+    pairs[2 * j] = table[j];
+    pairs[2 * j + 1] = blk;
+  }
+  dst->seqs.emplace(id, std::move(moved));
+  release_table(src, it->second.table);
+  src->seqs.erase(it);
+  *n_pairs = static_cast<int32_t>(n);
+  return pa_ok();
+}
+
 pa_status pa_alloc_cache_stats(const pa_allocator* a, int32_t* num_cached, int32_t* num_evictable) {
   if (!a) return pa_fail(PA_ERR_INVALID, "allocator is null");
   if (num_cached) *num_cached = static_cast<int32_t>(a->entries.size());

@@ -138,13 +138,79 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool, c
   if (num_pairs == 0) return pa_ok();
   if (!k_pool || !v_pool || !pairs) return pa_fail(PA_ERR_INVALID, "pa_copy_blocks: null pointer");
   pa::CopyBlocksArgs a{};
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
+  a.src_k = k_pool;
+  a.src_v = v_pool;
+  a.dst_k = k_pool;
+  a.dst_v = v_pool;
   a.block_bytes = static_cast<int64_t>(pool->num_kv_heads) * pool->block_size * pool->head_dim *
                   elem_bytes(pool->dtype);
   a.pairs = pairs;
   a.num_pairs = num_pairs;
   return launch_status(pa::launch_copy_blocks(a, stream), "pa_copy_blocks");
+}
+
+namespace {
+
+// The address through which kernels reach a pool: device (or managed) memory as it is; pinned host
+// memory through its device mapping.  Pageable host memory and unknown pointers are refused, so
+// that a swap never makes the device touch memory it cannot reach.
+bool device_reachable(const void* p, const void** out) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();   // not sticky: clear it so the next launch check does not see it
+    return false;
+  }
+  switch (attr.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+    case hipMemoryTypeUnified:
+      *out = p;
+      return true;
+    case hipMemoryTypeHost:
+      if (!attr.devicePointer || !attr.hostPointer) return false;
+      *out = static_cast<const char*>(attr.devicePointer) +
+             (static_cast<const char*>(p) - static_cast<const char*>(attr.hostPointer));
+      return true;
+    default:
+      return false;
+  }
+}
+
+bool same_format(const pa_pool_desc* a, const pa_pool_desc* b) {
+  return a->block_size == b->block_size && a->num_kv_heads == b->num_kv_heads && a->head_dim == b->head_dim &&
+         a->dtype == b->dtype && a->k_scale == b->k_scale && a->v_scale == b->v_scale;
+}
+
+}  // namespace
+
+pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const pa_pool_desc* dst_pool, const void* src_k_pool,
+                         const void* src_v_pool, const pa_pool_desc* src_pool, const int32_t* pairs,
+                         int32_t num_pairs, pa_stream stream) {
+  pa_status st = check_pool(dst_pool, "pa_swap_blocks");
+  if (st != PA_OK) return st;
+  st = check_pool(src_pool, "pa_swap_blocks");
+  if (st != PA_OK) return st;
+  if (!same_format(dst_pool, src_pool))
+    return pa_fail(PA_ERR_INVALID, "pa_swap_blocks: the pools differ in block format or scales");
+  if (num_pairs < 0) return pa_fail(PA_ERR_INVALID, "pa_swap_blocks: negative num_pairs");
+  if (num_pairs == 0) return pa_ok();
+  if (!dst_k_pool || !dst_v_pool || !src_k_pool || !src_v_pool || !pairs)
+    return pa_fail(PA_ERR_INVALID, "pa_swap_blocks: null pointer");
+  pa::CopyBlocksArgs a{};
+  const void* dk = nullptr;
+  const void* dv = nullptr;
+  const void* pp = nullptr;
+  if (!device_reachable(src_k_pool, &a.src_k) || !device_reachable(src_v_pool, &a.src_v) ||
+      !device_reachable(dst_k_pool, &dk) || !device_reachable(dst_v_pool, &dv) || !device_reachable(pairs, &pp))
+    return pa_fail(PA_ERR_INVALID,
+                   "pa_swap_blocks: a pool or the pairs are neither device memory nor pinned host memory");
+  a.dst_k = const_cast<void*>(dk);
+  a.dst_v = const_cast<void*>(dv);
+  a.pairs = static_cast<const int32_t*>(pp);
+  a.block_bytes = static_cast<int64_t>(src_pool->num_kv_heads) * src_pool->block_size * src_pool->head_dim *
+                  elem_bytes(src_pool->dtype);
+  a.num_pairs = num_pairs;
+  return launch_status(pa::launch_copy_blocks(a, stream), "pa_swap_blocks");
 }
 
 pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,

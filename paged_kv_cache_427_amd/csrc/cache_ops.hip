@@ -144,14 +144,16 @@ __global__ void __launch_bounds__(kThreads) cache_write_v_kernel(CacheWriteArgs 
   }
 }
 
-// grid (num_pairs, 2 pools, splits): each workgroup copies a share of one block of one pool.
+// grid (num_pairs, 2 pools, splits): each workgroup copies a share of one block of one pool (K for
+// blockIdx.y == 0, V for 1).
 __global__ void __launch_bounds__(kThreads) copy_blocks_kernel(CopyBlocksArgs a) {
   const int pair = blockIdx.x;
   const int32_t src = a.pairs[2 * pair];
   const int32_t dst = a.pairs[2 * pair + 1];
-  char* base = static_cast<char*>(blockIdx.y ? a.v_pool : a.k_pool);
-  const uint4* s = reinterpret_cast<const uint4*>(base + static_cast<int64_t>(src) * a.block_bytes);
-  uint4* d = reinterpret_cast<uint4*>(base + static_cast<int64_t>(dst) * a.block_bytes);
+  const char* sbase = static_cast<const char*>(blockIdx.y ? a.src_v : a.src_k);
+  char* dbase = static_cast<char*>(blockIdx.y ? a.dst_v : a.dst_k);
+  const uint4* s = reinterpret_cast<const uint4*>(sbase + static_cast<int64_t>(src) * a.block_bytes);
+  uint4* d = reinterpret_cast<uint4*>(dbase + static_cast<int64_t>(dst) * a.block_bytes);
   const int64_t n16 = a.block_bytes / 16;
   for (int64_t i = static_cast<int64_t>(blockIdx.z) * kThreads + threadIdx.x; i < n16;
        i += static_cast<int64_t>(gridDim.z) * kThreads)

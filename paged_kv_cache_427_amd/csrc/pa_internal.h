@@ -32,9 +32,13 @@ struct CacheWriteArgs {
   float v_inv_scale;
 };
 
+// Whole-block copies from (src_k, src_v) to (dst_k, dst_v); the same pools for copy-on-write,
+// different ones (device and pinned host memory) for swaps.
 struct CopyBlocksArgs {
-  void* k_pool;
-  void* v_pool;
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
   int64_t block_bytes;  // bytes of one block of one pool (all KV heads)
   const int32_t* pairs;
   int32_t num_pairs;

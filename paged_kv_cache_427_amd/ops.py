@@ -74,6 +74,27 @@ def pa_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc, p
                                _dev(pairs, "pairs"), n, _stream(stream)))
 
 
+def pa_swap_blocks(dst_k_pool: torch.Tensor, dst_v_pool: torch.Tensor, dst_pool: PoolDesc,
+                   src_k_pool: torch.Tensor, src_v_pool: torch.Tensor, src_pool: PoolDesc, pairs: torch.Tensor,
+                   stream=None) -> None:
+    """Copy whole blocks between two pools (device memory or pinned host memory): block pairs[i, 1]
+    of the destination receives block pairs[i, 0] of the source."""
+    if pairs.dtype != torch.int32:
+        raise TypeError("pairs must be int32")
+    n = int(pairs.shape[0]) if pairs.numel() else 0
+    if n == 0:
+        return
+    for t, name in ((dst_k_pool, "dst_k_pool"), (dst_v_pool, "dst_v_pool"), (src_k_pool, "src_k_pool"),
+                    (src_v_pool, "src_v_pool"), (pairs, "pairs")):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a device tensor or pinned host memory")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    check(lib().pa_swap_blocks(dst_k_pool.data_ptr(), dst_v_pool.data_ptr(), ctypes.byref(dst_pool),
+                               src_k_pool.data_ptr(), src_v_pool.data_ptr(), ctypes.byref(src_pool),
+                               pairs.data_ptr(), n, _stream(stream)))
+
+
 def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
                              partition_size: int = 0) -> int:
     out = ctypes.c_size_t(0)
