@@ -304,6 +304,20 @@ def swap_bench(args, dev):
                        "head_dim": wl.head_dim, "block_size": wl.block_size}}
 
 
+def copy_probe(args, dev, res) -> None:
+    """After timing, one device copy of a known size: the kernel that calibrates byte counters."""
+    if args.copy_probe_gib <= 0:
+        return
+    n = int(args.copy_probe_gib * 2**30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    res["copy_probe_bytes"] = {"read": n * 4, "write": n * 4}
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,11 +342,10 @@ def main():
     from paged_kv_cache_427_amd.engine import PagedKVEngine
 
     dev = torch.device("cuda:0")
-    if args.config == "prefix_cache_bf16":
-        print(json.dumps(prefix_cache_bench(args, dev)), flush=True)
-        return
-    if args.config == "swap_llama7b_bf16":
-        print(json.dumps(swap_bench(args, dev)), flush=True)
+    if args.config in ("prefix_cache_bf16", "swap_llama7b_bf16"):
+        res = (prefix_cache_bench if args.config == "prefix_cache_bf16" else swap_bench)(args, dev)
+        copy_probe(args, dev, res)
+        print(json.dumps(res), flush=True)
         return
     t_setup = time.time()
     wl = make_workload(args.config, "full", device=dev, block_size=args.block_size)
@@ -411,15 +424,7 @@ def main():
     res["kernel_ms"] = {"copy_blocks": round(ms_copy, 4), "cache_write": round(ms_write, 4),
                         "prefill": round(ms_prefill, 4), "decode": round(ms_decode, 4)}
     res["config"] = cfg
-    if args.copy_probe_gib > 0:
-        n = int(args.copy_probe_gib * 2**30) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        res["copy_probe_bytes"] = {"read": n * 4, "write": n * 4}
-        del src, dst
+    copy_probe(args, dev, res)
     if not args.no_cpu_baseline and wl.decode_seqs:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
