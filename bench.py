@@ -9,7 +9,9 @@ already resident in HBM.  The default workload is the shared-prefix decode (256 
 head_dim 128, bf16, 16-token blocks, one copy-on-write per sequence).  `--config prefix_cache_bf16`
 instead times 64 prompts behind one shared 1000-token system prompt, prefilled through the prefix
 cache and, for comparison, in full without it; `--config swap_llama7b_bf16` times the swap of every
-sequence of the Llama-7B-shaped decode workload to pinned host memory and back.
+sequence of the Llama-7B-shaped decode workload to pinned host memory and back;
+`--config llama7b_32layer_bf16` runs that workload's step for all 32 layers of the model, eager and
+as one HIP graph.
 
 Prints one JSON line.  `value` is the decode's unique KV bytes per step (each physical block once)
 divided by the step time, in GB/s.  `roofline` prices the decode launch (plan, stream and merge kernels),
@@ -304,6 +306,70 @@ def swap_bench(args, dev):
                        "head_dim": wl.head_dim, "block_size": wl.block_size}}
 
 
+def layers_bench(args, dev, num_layers: int = 32):
+    """The Llama-7B-shaped decode step for all 32 layers of the model: one allocator and table, per-
+    layer pools (46 GB), one copy launch, then per layer the cache write and the decode.  Timed eager
+    and replayed as one HIP graph."""
+    from synth import layer_rows
+    from paged_kv_cache_427_amd.layers import LayeredEngine
+    wl = make_workload("llama7b_bf16", "full", device=dev)
+    eng = LayeredEngine(wl, num_layers, layer_rows, device=dev, poison=poison_code(wl.kv_dtype))
+    eng.build_history()
+    si = eng.prepare_step()
+    eng.prepare_layers(si)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, e0.elapsed_time(e1) / args.steps
+
+    wall_e, gpu_e = timed(lambda: eng.run_layers(si))
+    eager = si.out_layers.clone()
+    g = eng.capture(si)
+    wall_g, gpu_g = timed(g.replay)
+    same = bool(torch.equal(si.out_layers.view(torch.int16), eager.view(torch.int16)))
+    # one layer's decode alone, for the kernel roofline
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        eng.k_pool, eng.v_pool = eng.k_layers[num_layers // 2], eng.v_layers[num_layers // 2]
+        eng.decode_step(si)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms_dec = ev[0].elapsed_time(ev[1]) / args.steps
+    tab = si.dec_tables.cpu().numpy()
+    uniq, logical, other = decode_bytes(wl, tab)
+    ms = max(wall_g, gpu_g)
+    achieved = (uniq + other) / (ms_dec * 1e-3) / 1e9
+    return {"metric": "paged decode KV-read GB/s (% of MI355X HBM peak); decode tokens/s per layer",
+            "value": round(num_layers * uniq / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (the Llama-7B-shaped decode workload; layer l's rows rotated by l along head_dim)",
+            "decode_tokens_per_s_all_layers": round(len(wl.decode_lens) / (ms * 1e-3), 1),
+            "eager": {"ms_per_step_wall": round(wall_e, 4), "ms_per_step_gpu": round(gpu_e, 4)},
+            "graph": {"ms_per_step_wall": round(wall_g, 4), "ms_per_step_gpu": round(gpu_g, 4),
+                      "identical_to_eager": same},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "pa_decode of one layer (plan + stream + merge kernels)",
+                         "algorithmic_bytes_per_launch": int(uniq + other)},
+            "config": {"workload": "llama7b_32layer_bf16", "layers": num_layers, "num_seqs": len(wl.decode_seqs),
+                       "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                       "block_size": wl.block_size, "pool_blocks": wl.num_blocks,
+                       "pool_GB_all_layers": round(2 * eng.k_layers.numel() * eng.k_layers.element_size() / 1e9, 2)}}
+
+
 def copy_probe(args, dev, res) -> None:
     """After timing, one device copy of a known size: the kernel that calibrates byte counters."""
     if args.copy_probe_gib <= 0:
@@ -342,8 +408,10 @@ def main():
     from paged_kv_cache_427_amd.engine import PagedKVEngine
 
     dev = torch.device("cuda:0")
-    if args.config in ("prefix_cache_bf16", "swap_llama7b_bf16"):
-        res = (prefix_cache_bench if args.config == "prefix_cache_bf16" else swap_bench)(args, dev)
+    modes = {"prefix_cache_bf16": prefix_cache_bench, "swap_llama7b_bf16": swap_bench,
+             "llama7b_32layer_bf16": layers_bench}
+    if args.config in modes:
+        res = modes[args.config](args, dev)
         copy_probe(args, dev, res)
         print(json.dumps(res), flush=True)
         return

@@ -113,6 +113,20 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool, c
                          int32_t num_pairs, pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * pa_copy_blocks_layers -- the copy-on-write copies of one step for every layer of a model, in one
+ * launch.  A block id names the same block in every layer's pools ([ch7] 7.1: the KV cache holds
+ * K and V of every layer; one block table serves them all).
+ *
+ *   k_pools, v_pools    layer 0's K and V pools; layer l's start l * layer_stride_bytes later
+ *                       (a multiple of 16, at least one layer's pool size when num_layers > 1)
+ *   num_layers          1 .. 32767
+ *   pool, pairs, n      as pa_copy_blocks (pool describes one layer)
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_copy_blocks_layers(void* k_pools, void* v_pools, int64_t layer_stride_bytes, int32_t num_layers,
+                                const pa_pool_desc* pool, const int32_t* pairs, int32_t num_pairs,
+                                pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
  * pa_swap_blocks -- whole-block copies from one pool to another of the same block format: the
  * data movement of a swap-out (device pool -> pinned host pool) or swap-in (host -> device) of a
  * preempted sequence ([day28] §六 question 4).

@@ -39,6 +39,8 @@ _PROTOS = {
     "pa_cache_write": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_void_p, c_void_p, c_void_p,
                                  POINTER(PoolDesc), c_void_p]),
     "pa_copy_blocks": (c_int32, [c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_int32, c_void_p]),
+    "pa_copy_blocks_layers": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, POINTER(PoolDesc), c_void_p,
+                                        c_int32, c_void_p]),
     "pa_swap_blocks": (c_int32, [c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_void_p, POINTER(PoolDesc),
                                  c_void_p, c_int32, c_void_p]),
     "pa_decode_workspace_size": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_size_t)]),

@@ -146,7 +146,38 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool, c
                   elem_bytes(pool->dtype);
   a.pairs = pairs;
   a.num_pairs = num_pairs;
+  a.num_layers = 1;
+  a.layer_stride = 0;
   return launch_status(pa::launch_copy_blocks(a, stream), "pa_copy_blocks");
+}
+
+pa_status pa_copy_blocks_layers(void* k_pools, void* v_pools, int64_t layer_stride_bytes, int32_t num_layers,
+                                const pa_pool_desc* pool, const int32_t* pairs, int32_t num_pairs,
+                                pa_stream stream) {
+  pa_status st = check_pool(pool, "pa_copy_blocks_layers");
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return pa_fail(PA_ERR_INVALID, "pa_copy_blocks_layers: negative num_pairs");
+  if (num_layers < 1 || num_layers > 32767)
+    return pa_fail(PA_ERR_INVALID, "pa_copy_blocks_layers: num_layers must be in 1..32767");
+  const int64_t block_bytes = static_cast<int64_t>(pool->num_kv_heads) * pool->block_size * pool->head_dim *
+                              elem_bytes(pool->dtype);
+  if (num_layers > 1 && layer_stride_bytes < block_bytes * pool->num_blocks)
+    return pa_fail(PA_ERR_INVALID, "pa_copy_blocks_layers: layer_stride_bytes is smaller than one layer's pool");
+  if (layer_stride_bytes % 16 != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_copy_blocks_layers: layer_stride_bytes must be a multiple of 16");
+  if (num_pairs == 0) return pa_ok();
+  if (!k_pools || !v_pools || !pairs) return pa_fail(PA_ERR_INVALID, "pa_copy_blocks_layers: null pointer");
+  pa::CopyBlocksArgs a{};
+  a.src_k = k_pools;
+  a.src_v = v_pools;
+  a.dst_k = k_pools;
+  a.dst_v = v_pools;
+  a.block_bytes = block_bytes;
+  a.pairs = pairs;
+  a.num_pairs = num_pairs;
+  a.num_layers = num_layers;
+  a.layer_stride = layer_stride_bytes;
+  return launch_status(pa::launch_copy_blocks(a, stream), "pa_copy_blocks_layers");
 }
 
 namespace {
@@ -210,6 +241,8 @@ pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const pa_pool_desc*
   a.block_bytes = static_cast<int64_t>(src_pool->num_kv_heads) * src_pool->block_size * src_pool->head_dim *
                   elem_bytes(src_pool->dtype);
   a.num_pairs = num_pairs;
+  a.num_layers = 1;
+  a.layer_stride = 0;
   return launch_status(pa::launch_copy_blocks(a, stream), "pa_swap_blocks");
 }
 

@@ -144,14 +144,15 @@ __global__ void __launch_bounds__(kThreads) cache_write_v_kernel(CacheWriteArgs 
   }
 }
 
-// grid (num_pairs, 2 pools, splits): each workgroup copies a share of one block of one pool (K for
-// blockIdx.y == 0, V for 1).
+// grid (num_pairs, 2 pools x layers, splits): each workgroup copies a share of one block of one pool
+// of one layer (blockIdx.y = 2 * layer + (0 for K, 1 for V)).
 __global__ void __launch_bounds__(kThreads) copy_blocks_kernel(CopyBlocksArgs a) {
   const int pair = blockIdx.x;
   const int32_t src = a.pairs[2 * pair];
   const int32_t dst = a.pairs[2 * pair + 1];
-  const char* sbase = static_cast<const char*>(blockIdx.y ? a.src_v : a.src_k);
-  char* dbase = static_cast<char*>(blockIdx.y ? a.dst_v : a.dst_k);
+  const int64_t layer_off = static_cast<int64_t>(blockIdx.y >> 1) * a.layer_stride;
+  const char* sbase = static_cast<const char*>((blockIdx.y & 1) ? a.src_v : a.src_k) + layer_off;
+  char* dbase = static_cast<char*>((blockIdx.y & 1) ? a.dst_v : a.dst_k) + layer_off;
   const uint4* s = reinterpret_cast<const uint4*>(sbase + static_cast<int64_t>(src) * a.block_bytes);
   uint4* d = reinterpret_cast<uint4*>(dbase + static_cast<int64_t>(dst) * a.block_bytes);
   const int64_t n16 = a.block_bytes / 16;
@@ -205,7 +206,7 @@ int launch_copy_blocks(const CopyBlocksArgs& a, void* stream) {
   int splits = static_cast<int>((n16 + 4 * kThreads - 1) / (4 * kThreads));  // ~4 loads per thread
   if (splits < 1) splits = 1;
   if (splits > 64) splits = 64;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.num_pairs, 2, splits), dim3(kThreads), 0,
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.num_pairs, 2 * a.num_layers, splits), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
 }

@@ -42,6 +42,8 @@ struct CopyBlocksArgs {
   int64_t block_bytes;  // bytes of one block of one pool (all KV heads)
   const int32_t* pairs;
   int32_t num_pairs;
+  int32_t num_layers;    // layer l's pools start layer_stride bytes after layer l - 1's
+  int64_t layer_stride;
 };
 
 struct DecodeArgs {

@@ -51,18 +51,20 @@ class StepInputs:
 class PagedKVEngine:
     """Owns the two pools of one layer and the host allocator of a workload (package `synth`)."""
 
-    def __init__(self, wl, device: str = "cuda", poison: Optional[int] = None):
+    def __init__(self, wl, device: str = "cuda", poison: Optional[int] = None, allocate_pools: bool = True):
         self.wl = wl
         self.device = torch.device(device)
         self.pool = make_pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
                                    _PA[wl.kv_dtype], wl.k_scale, wl.v_scale)
-        # K tiles are [block_size][head_dim] (token-major), V tiles [head_dim][block_size] (dim-major)
-        k_shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
-        v_shape = (wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.block_size)
-        bits = {"f32": 32, "bf16": 16, "fp8": 8}[wl.kv_dtype]
-        fill = 0 if poison is None else (_signed(poison, bits) if wl.kv_dtype != "fp8" else poison)
-        self.k_pool = torch.full(k_shape, fill, dtype=_CODE_TORCH[wl.kv_dtype], device=self.device).view(_VIEW[wl.kv_dtype])
-        self.v_pool = torch.full(v_shape, fill, dtype=_CODE_TORCH[wl.kv_dtype], device=self.device).view(_VIEW[wl.kv_dtype])
+        if allocate_pools:
+            # K tiles are [block_size][head_dim] (token-major), V tiles [head_dim][block_size] (dim-major)
+            k_shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+            v_shape = (wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.block_size)
+            bits = {"f32": 32, "bf16": 16, "fp8": 8}[wl.kv_dtype]
+            fill = 0 if poison is None else (_signed(poison, bits) if wl.kv_dtype != "fp8" else poison)
+            code, view = _CODE_TORCH[wl.kv_dtype], _VIEW[wl.kv_dtype]
+            self.k_pool = torch.full(k_shape, fill, dtype=code, device=self.device).view(view)
+            self.v_pool = torch.full(v_shape, fill, dtype=code, device=self.device).view(view)
         self.alloc = BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
         self.k_tok = wl.k_tok.to(self.device)
         self.v_tok = wl.v_tok.to(self.device)
@@ -103,12 +105,14 @@ class PagedKVEngine:
             end = int(np.max(np.nonzero(slots >= 0)[0])) + 1 if (slots >= 0).any() else h0
             self._write_rows(written[0], end, slots)
             written[0] = end
-            pa_copy_blocks(self.k_pool, self.v_pool, self.pool,
-                           torch.as_tensor(np.asarray(cow, np.int32), device=self.device))
+            self._copy_history_blocks(torch.as_tensor(np.asarray(cow, np.int32), device=self.device))
 
         self._replay(wl.history, on_cow=flush_then_copy, slots_out=slots)
         self._write_rows(written[0], h1, slots)
         self.history_slots = slots[h0:h1].copy()
+
+    def _copy_history_blocks(self, pairs: torch.Tensor) -> None:
+        pa_copy_blocks(self.k_pool, self.v_pool, self.pool, pairs)
 
     def _write_rows(self, a: int, b: int, slots: np.ndarray) -> None:
         if b <= a:

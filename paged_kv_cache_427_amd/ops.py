@@ -74,6 +74,22 @@ def pa_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc, p
                                _dev(pairs, "pairs"), n, _stream(stream)))
 
 
+def pa_copy_blocks_layers(k_pools: torch.Tensor, v_pools: torch.Tensor, pool: PoolDesc, pairs: torch.Tensor,
+                          stream=None) -> None:
+    """Copy-on-write copies in every layer: k_pools, v_pools are [layers, num_blocks, ...] tensors."""
+    if pairs.dtype != torch.int32:
+        raise TypeError("pairs must be int32")
+    n = int(pairs.shape[0]) if pairs.numel() else 0
+    if n == 0:
+        return
+    if k_pools.shape[0] != v_pools.shape[0] or k_pools.stride(0) != v_pools.stride(0):
+        raise ValueError("k_pools and v_pools must have the same layers and layer stride")
+    stride = k_pools.stride(0) * k_pools.element_size()
+    check(lib().pa_copy_blocks_layers(_dev(k_pools, "k_pools"), _dev(v_pools, "v_pools"), stride,
+                                      int(k_pools.shape[0]), ctypes.byref(pool), _dev(pairs, "pairs"), n,
+                                      _stream(stream)))
+
+
 def pa_swap_blocks(dst_k_pool: torch.Tensor, dst_v_pool: torch.Tensor, dst_pool: PoolDesc,
                    src_k_pool: torch.Tensor, src_v_pool: torch.Tensor, src_pool: PoolDesc, pairs: torch.Tensor,
                    stream=None) -> None:

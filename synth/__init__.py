@@ -6,5 +6,5 @@ workload implies.  It holds none of the method's arithmetic (no slot computation
 attention, no fp8 encoding).
 """
 from .workloads import (  # noqa: F401
-    CONFIG_NAMES, Workload, make_workload, poison_code, elem_bytes,
+    CONFIG_NAMES, Workload, make_workload, poison_code, elem_bytes, layer_rows, layer_workload,
 )

@@ -391,3 +391,20 @@ def mixed_workload(name, size, rng, gen, device, *, hq, hkv, d, b, kv, prior, ch
         decode_seqs=dec_ids, decode_lens=np.asarray(dlens, np.int32), q_decode=q_dec,
         prefill_seqs=pre_ids, prefill_prior=np.asarray(prior, np.int32),
         prefill_chunk=np.asarray(chunk, np.int32), q_prefill=q_pre, notes=notes)
+
+
+def layer_rows(rows: torch.Tensor, layer: int) -> torch.Tensor:
+    """Rows of layer `layer` in a many-layer model: the workload's rows rotated by `layer` places along
+    head_dim.  Each layer then holds different values from the same draws (a permutation, exact in
+    any dtype), and the layer-0 rows are the workload's own."""
+    return torch.roll(rows, shifts=int(layer), dims=-1) if layer else rows
+
+
+def layer_workload(wl: Workload, layer: int) -> Workload:
+    """The workload as layer `layer` of a many-layer model sees it: same operations and tables, K, V
+    and Q rows from layer_rows()."""
+    import dataclasses
+    return dataclasses.replace(
+        wl, k_tok=layer_rows(wl.k_tok, layer), v_tok=layer_rows(wl.v_tok, layer),
+        q_decode=None if wl.q_decode is None else layer_rows(wl.q_decode, layer),
+        q_prefill=None if wl.q_prefill is None else layer_rows(wl.q_prefill, layer))
