@@ -11,7 +11,8 @@ instead times 64 prompts behind one shared 1000-token system prompt, prefilled t
 cache and, for comparison, in full without it; `--config swap_llama7b_bf16` times the swap of every
 sequence of the Llama-7B-shaped decode workload to pinned host memory and back;
 `--config llama7b_32layer_bf16` runs that workload's step for all 32 layers of the model, eager and
-as one HIP graph.
+as one HIP graph; `--config serving_llama7b_bf16` runs a continuous-batching loop over a synthetic
+request stream and reports KV utilisation against a max-length reservation.
 
 Prints one JSON line.  `value` is the decode's unique KV bytes per step (each physical block once)
 divided by the step time, in GB/s.  `roofline` prices the decode launch (plan, stream and merge kernels),
@@ -370,6 +371,38 @@ def layers_bench(args, dev, num_layers: int = 32):
                        "pool_GB_all_layers": round(2 * eng.k_layers.numel() * eng.k_layers.element_size() / 1e9, 2)}}
 
 
+def serving_bench(args, dev):
+    """Continuous batching of 2000 synthetic requests (prompts U{64..1024}, outputs U{16..512},
+    Llama-7B-shaped attention) through a 6000-block pool for 1200 steps: every step retires, admits,
+    writes the new K/V and decodes every running request.  Reports the KV utilisation of the paged
+    pool against a 2048-token reservation per request, and the loop's decode throughput."""
+    from synth.serving import make_request_stream
+    from paged_kv_cache_427_amd.batching import ContinuousBatcher, utilisation
+    st = make_request_stream("full", device=dev)
+    nb, steps = 6000, 1200
+    cb = ContinuousBatcher(st, nb, device=dev)
+    cb.run(20)                                  # warm-up (also the loop's first steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(20, steps):
+        cb.step(t)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    decoded = sum(s.decoded for s in cb.stats[20:])
+    u = utilisation(cb.stats, st.block_size, st.max_model_len, nb)
+    return {"metric": "continuous-batching decode tokens/s (one layer) and KV utilisation, paged vs reservation",
+            "value": round(decoded / wall, 1), "unit": "decode tokens/s", "n_gpus": 1, "steps": steps - 20,
+            "warmup": 20, "ms_per_step": round(wall * 1e3 / (steps - 20), 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic request stream",
+            "kv_utilisation": {"paged": round(u["paged"], 4), "reservation_2048": round(u["reservation"], 4)},
+            "mean_running_requests": round(u["mean_running"], 1),
+            "reservation_capacity_requests": u["reservation_capacity"],
+            "finished_requests": int(sum(s.finished for s in cb.stats)), "preemptions": cb.preemptions,
+            "config": {"workload": "serving_llama7b_bf16", "requests": len(st.requests), "pool_blocks": nb,
+                       "steps": steps, "q_heads": st.num_q_heads, "kv_heads": st.num_kv_heads,
+                       "head_dim": st.head_dim, "block_size": st.block_size}}
+
+
 def copy_probe(args, dev, res) -> None:
     """After timing, one device copy of a known size: the kernel that calibrates byte counters."""
     if args.copy_probe_gib <= 0:
@@ -409,7 +442,7 @@ def main():
 
     dev = torch.device("cuda:0")
     modes = {"prefix_cache_bf16": prefix_cache_bench, "swap_llama7b_bf16": swap_bench,
-             "llama7b_32layer_bf16": layers_bench}
+             "llama7b_32layer_bf16": layers_bench, "serving_llama7b_bf16": serving_bench}
     if args.config in modes:
         res = modes[args.config](args, dev)
         copy_probe(args, dev, res)
