@@ -427,6 +427,8 @@ def main():
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--plain-decode", action="store_true",
+                    help="beam workloads: decode every branch on its own instead of reading shared blocks once")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="after timing, run one device copy of this many GiB (a known-size kernel that "
                          "calibrates hardware byte counters)")
@@ -453,6 +455,8 @@ def main():
     eng = PagedKVEngine(wl, device=dev, poison=poison_code(wl.kv_dtype))
     eng.build_history()
     si = eng.prepare_step(args.partition)
+    if wl.beam_width and not args.plain_decode:
+        eng.use_cascade(si, wl.beam_width)      # shared blocks read once for all branches of a request
     torch.cuda.synchronize()
     print(f"[bench] {args.config}: setup {time.time() - t_setup:.1f}s, blocks {wl.num_blocks}, "
           f"tokens {wl.num_tokens}", file=sys.stderr, flush=True)
@@ -503,7 +507,9 @@ def main():
         res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": measured_traffic(args.config, args.block_size),
-                           "kernel": "pa_decode (plan + stream + merge kernels)",
+                           "kernel": ("beam decode: pa_decode_ex over shared blocks + over private tails + "
+                                      "pa_merge_states" if getattr(si, "cascade", None) is not None else
+                                      "pa_decode (plan + stream + merge kernels)"),
                            "algorithmic_bytes_per_launch": int(uniq + other)}
         res["decode_logical_kv_GBps"] = round(logical / (ms_decode * 1e-3) / 1e9, 1)
         cfg["mean_context"] = round(float(np.mean(wl.decode_lens)), 1)

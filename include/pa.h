@@ -214,6 +214,53 @@ pa_status pa_prefill_chunk(const void* q, int32_t q_dtype, const void* k_pool, c
                            pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * pa_decode_ex -- pa_decode with strided q and out and an optional log-sum-exp output.  Beam
+ * branches share their prompt's blocks ([day28] §六 question 3); with these, one call can read a
+ * shared segment once for the queries of every branch (the branches' queries of one KV head as its
+ * query heads), and pa_merge_states combines that result with each branch's private tail.
+ *
+ *   q_strides, out_strides  NULL (dense [num_seqs][num_q_heads][head_dim]) or host int64 [3]:
+ *                 element strides for (sequence, KV head, head within the KV head's group); the
+ *                 head_dim elements of a row are contiguous.  Multiples of 4; with lse_out also
+ *                 multiples of head_dim.
+ *   lse_out       NULL or device float: ln(sum_j exp(scale * q . k_j)) of each (sequence, head) row
+ *                 (k_j with k_scale applied), at the row's out offset divided by head_dim; -inf
+ *                 for L_s == 0.
+ * Everything else as pa_decode; pa_decode is pa_decode_ex with NULL strides and lse_out.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides, const void* k_pool,
+                       const void* v_pool, const pa_pool_desc* pool, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_q_heads, float scale, int32_t partition_size, int32_t max_context_len,
+                       void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
+                       const int64_t* out_strides, float* lse_out, pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_plan_shared_blocks (host) -- for a decode batch laid out as groups of `width` consecutive
+ * sequences (the branches of one request), the number of leading blocks every member of group g
+ * shares: shared_blocks[g] = the longest k such that all members have the same first k table
+ * entries and k * block_size <= every member's length.  tables host int32 [num_seqs][max_blocks],
+ * lens host int32 [num_seqs], shared_blocks host int32 [num_seqs / width].  PA_ERR_INVALID if
+ * num_seqs is not a multiple of width.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_plan_shared_blocks(const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t num_seqs,
+                                int32_t block_size, int32_t width, int32_t* shared_blocks);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_merge_states -- combine two attention results of the same query rows over disjoint key sets
+ * (a shared segment and a private tail), the rescaled combination the split merge uses:
+ *     M = max(lse_a, lse_b),  w_x = exp(lse_x - M),
+ *     out = (o_a w_a + o_b w_b) / (w_a + w_b),  lse_out = M + ln(w_a + w_b).
+ *   o_a, o_b      device float [rows][head_dim];  lse_a, lse_b  device float [rows]
+ *   out           device [rows][head_dim] of out_dtype (PA_F32 or PA_BF16); may be o_a or o_b
+ *   lse_out       NULL or device float [rows]
+ * A row whose two lse are -inf (no keys) gives zeros and -inf.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_merge_states(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                          int64_t rows, int32_t head_dim, void* out, int32_t out_dtype, float* lse_out,
+                          pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Self-check of the device fp8 decoding: out[c] = value of e4m3 code c (c = 0..255) as decoded by
  * the same conversion the attention kernels use (NaN codes give NaN).  out: device float [256].
  * ------------------------------------------------------------------------------------------- */

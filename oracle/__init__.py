@@ -25,5 +25,5 @@ from .cache import (  # noqa: F401
     slot_of, pool_shape, ref_cache_write, ref_copy_blocks, ref_move_blocks, gather_seq,
 )
 from .attention import (  # noqa: F401
-    attend, ref_decode, ref_decode_split, partition_stats, merge_partitions, ref_prefill,
+    attend, ref_decode, ref_decode_split, partition_stats, merge_partitions, ref_prefill, ref_lse,
 )

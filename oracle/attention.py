@@ -57,6 +57,16 @@ def partition_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
     return m, l, (p @ v) / l
 
 
+def ref_lse(q: np.ndarray, k: np.ndarray, scale: float) -> float:
+    """Natural log of the softmax denominator of one query over keys k [L, D]: ln sum_j exp(scale q.k_j),
+    -inf for no keys.  Written as max + ln(sum of exp(z - max)) so that it does not overflow."""
+    if len(k) == 0:
+        return float("-inf")
+    z = float(scale) * (k @ q)
+    m = z.max()
+    return float(m + np.log(np.exp(z - m).sum()))
+
+
 def merge_partitions(ms: Sequence[float], ls: Sequence[float], os: Sequence[np.ndarray]) -> np.ndarray:
     """Combine per-partition (m, l, o) into the full softmax-weighted output."""
     ms = np.asarray(ms, dtype=np.float64)

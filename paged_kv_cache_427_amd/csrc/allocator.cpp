@@ -22,6 +22,7 @@
 // token to compute.  A cached block whose count falls to zero is kept, and is reclaimed (its entry
 // dropped), least recently released first, only when the free list is empty; one release queues
 // its cached blocks from the table's end, so chains shrink from their deepest block.
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <deque>
@@ -411,6 +412,29 @@ pa_status pa_alloc_move_seq(pa_allocator* src, pa_allocator* dst, int64_t id, in
   release_table(src, it->second.table);
   src->seqs.erase(it);
   *n_pairs = static_cast<int32_t>(n);
+  return pa_ok();
+}
+
+pa_status pa_plan_shared_blocks(const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t num_seqs,
+                                int32_t block_size, int32_t width, int32_t* shared_blocks) {
+  if (!shared_blocks || (num_seqs > 0 && (!tables || !lens)))
+    return pa_fail(PA_ERR_INVALID, "pa_plan_shared_blocks: null argument");
+  if (width < 1 || block_size < 1 || max_blocks < 0 || num_seqs < 0 || num_seqs % width != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_plan_shared_blocks: num_seqs must be a multiple of width >= 1");
+  for (int32_t g = 0; g < num_seqs / width; ++g) {
+    const int32_t* t0 = tables + static_cast<int64_t>(g) * width * max_blocks;
+    int64_t k = max_blocks;
+    for (int32_t w = 0; w < width; ++w) {
+      const int32_t s = g * width + w;
+      if (lens[s] < 0) return pa_fail(PA_ERR_INVALID, "pa_plan_shared_blocks: negative length");
+      k = std::min<int64_t>(k, lens[s] / block_size);   // whole blocks inside every member's context
+      const int32_t* t = tables + static_cast<int64_t>(s) * max_blocks;
+      int64_t c = 0;
+      while (c < k && t[c] == t0[c]) ++c;
+      k = c;
+    }
+    shared_blocks[g] = static_cast<int32_t>(k);
+  }
   return pa_ok();
 }
 

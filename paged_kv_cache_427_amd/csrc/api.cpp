@@ -265,6 +265,17 @@ pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const vo
                     const int32_t* lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                     int32_t partition_size, int32_t max_context_len, void* workspace,
                     size_t workspace_bytes, void* out, int32_t out_dtype, pa_stream stream) {
+  return pa_decode_ex(q, q_dtype, nullptr, k_pool, v_pool, pool, tables, max_blocks, lens, num_seqs, num_q_heads,
+                      scale, partition_size, max_context_len, workspace, workspace_bytes, out, out_dtype, nullptr,
+                      nullptr, stream);
+}
+
+pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides, const void* k_pool,
+                       const void* v_pool, const pa_pool_desc* pool, const int32_t* tables, int32_t max_blocks,
+                       const int32_t* lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                       int32_t partition_size, int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                       void* out, int32_t out_dtype, const int64_t* out_strides, float* lse_out,
+                       pa_stream stream) {
   pa_status st = check_pool(pool, "pa_decode");
   if (st != PA_OK) return st;
   if (num_seqs < 0) return pa_fail(PA_ERR_INVALID, "pa_decode: negative num_seqs");
@@ -319,9 +330,41 @@ pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const vo
   a.max_ctx = max_context_len;
   pa::decode_workspace_carve(a, workspace);
   a.out = out;
+  const int64_t D = pool->head_dim;
+  const int64_t G = group;
+  const int64_t dense[3] = {static_cast<int64_t>(num_q_heads) * D, G * D, D};
+  const int64_t* qs = q_strides ? q_strides : dense;
+  const int64_t* os = out_strides ? out_strides : dense;
+  for (int k = 0; k < 3; ++k) {
+    if (qs[k] < 0 || os[k] < 0)
+      return pa_fail(PA_ERR_INVALID, "pa_decode_ex: negative stride");
+    // rows are read and written in 16-byte pieces
+    if (qs[k] % 4 != 0 || os[k] % 4 != 0)
+      return pa_fail(PA_ERR_INVALID, "pa_decode_ex: strides must be multiples of 4 elements");
+    if (lse_out && os[k] % D != 0)
+      return pa_fail(PA_ERR_INVALID, "pa_decode_ex: with lse_out, out strides must be multiples of head_dim");
+  }
+  a.q_sseq = qs[0];
+  a.q_skv = qs[1];
+  a.q_sg = qs[2];
+  a.o_sseq = os[0];
+  a.o_skv = os[1];
+  a.o_sg = os[2];
+  a.lse = lse_out;
   return launch_status(pa::launch_decode(a, pool->dtype, q_dtype, out_dtype, pool->block_size,
                                          pool->head_dim, stream),
                        "pa_decode: no kernel for this dtype / head_dim / block_size combination");
+}
+
+pa_status pa_merge_states(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b, int64_t rows,
+                          int32_t head_dim, void* out, int32_t out_dtype, float* lse_out, pa_stream stream) {
+  if (rows < 0) return pa_fail(PA_ERR_INVALID, "pa_merge_states: negative rows");
+  if (head_dim <= 0 || head_dim % 4 != 0) return pa_fail(PA_ERR_INVALID, "pa_merge_states: head_dim must be a positive multiple of 4");
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return pa_fail(PA_ERR_INVALID, "pa_merge_states: bad out_dtype");
+  if (rows == 0) return pa_ok();
+  if (!o_a || !lse_a || !o_b || !lse_b || !out) return pa_fail(PA_ERR_INVALID, "pa_merge_states: null pointer");
+  pa::MergeStatesArgs a{o_a, lse_a, o_b, lse_b, rows, head_dim, out, lse_out};
+  return launch_status(pa::launch_merge_states(a, out_dtype, stream), "pa_merge_states");
 }
 
 pa_status pa_prefill_chunk(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,

@@ -452,8 +452,7 @@ __device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int seq, int kv
 template <int KV, int D, int G, typename QArr>
 __device__ __forceinline__ void load_q(QArr& qb, const DecodeArgs& a, int seq, int kvh, int i, int kg) {
   using QT = typename std::conditional<KV == kF32, float, uint16_t>::type;
-  const QT* qrow = static_cast<const QT*>(a.q) +
-                   (static_cast<int64_t>(seq) * a.num_q_heads + kvh * G + min(i, G - 1)) * D;
+  const QT* qrow = static_cast<const QT*>(a.q) + seq * a.q_sseq + kvh * a.q_skv + min(i, G - 1) * a.q_sg;
   if constexpr (KV == kF32) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
@@ -489,7 +488,8 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs& a, int out_bf16, 
   if (i >= G) return;
   if (c.j == 0 && np == c.nj) {
     const float inv = l > 0.f ? a.v_scale / l : 0.f;
-    const int64_t base = (static_cast<int64_t>(c.seq) * a.num_q_heads + kvh * G + i) * D;
+    const int64_t base = c.seq * a.o_sseq + kvh * a.o_skv + i * a.o_sg;
+    if (a.lse && kg == 0) a.lse[base / D] = (st.m + __log2f(l)) * 0.6931471805599453f;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
       const int d = 16 * t + 4 * kg;
@@ -676,9 +676,11 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_b
   const ro_i32 pref = ro(a.ws_pref);
   const int n = a.num_seqs;
   const int nj = pref[seq + 1] - pref[seq];
-  const int64_t oi = (static_cast<int64_t>(seq) * a.num_q_heads + h) * D + d;
+  const int64_t orow = seq * a.o_sseq + kvh * a.o_skv + g * a.o_sg;
+  const int64_t oi = orow + d;
   if (nj == 0) {
     store_out(a.out, oi, 0.f, out_bf16 != 0);
+    if (a.lse && d == 0) a.lse[orow / D] = -INFINITY;
     return;
   }
   const int x = kvh % a.streams, hh = kvh / a.streams;
@@ -748,6 +750,7 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_b
 #pragma unroll 8
     for (int q = 0; q < R; ++q) o += a.ws_part[rec_s[q] + 4 + d] * w_s[q];
     store_out(a.out, oi, lsum > 0.f ? o / lsum * a.v_scale : 0.f, out_bf16 != 0);
+    if (a.lse && d == 0) a.lse[orow / D] = (M + __log2f(lsum)) * 0.6931471805599453f;
     return;
   }
   // more records than the LDS list holds: one pass with a running maximum
@@ -765,6 +768,7 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_b
     }
   }
   store_out(a.out, oi, lsum > 0.f ? o / lsum * a.v_scale : 0.f, out_bf16 != 0);
+  if (a.lse && d == 0) a.lse[orow / D] = (mm + __log2f(lsum)) * 0.6931471805599453f;
 }
 
 // Compute units of the current device (cached per device).

@@ -71,6 +71,12 @@ struct DecodeArgs {
   int32_t* ws_share;     // [max_shares][4] start cursor of each share: head slot, sequence, unit, units
   float* ws_part;        // [streams * stream_slots][G][head_dim + 4]: max, sum, -, -, unnormalised o
   void* out;
+  // Element strides of q and out for (sequence, KV head, head within the group); the head_dim
+  // elements of one row are contiguous.  Dense [seq][head][dim] is (Hq * D, G * D, D).
+  int64_t q_sseq, q_skv, q_sg;
+  int64_t o_sseq, o_skv, o_sg;
+  float* lse;            // optional: natural log of each row's softmax denominator, at out's row
+                         // index divided by head_dim (strides o_s* / D)
 };
 
 // Bytes of the decode workspace for a launch of `waves` waves (see pa_decode_workspace_size).
@@ -101,6 +107,18 @@ struct PrefillArgs {
 // Launchers return a hipError_t value as int (0 = success).
 int launch_cache_write(const CacheWriteArgs& a, void* stream);
 int launch_copy_blocks(const CopyBlocksArgs& a, void* stream);
+
+struct MergeStatesArgs {
+  const float* o_a;
+  const float* lse_a;
+  const float* o_b;
+  const float* lse_b;
+  int64_t rows;
+  int32_t head_dim;
+  void* out;
+  float* lse_out;
+};
+int launch_merge_states(const MergeStatesArgs& a, int out_dtype, void* stream);
 // Returns 0 on success, -1 when no kernel exists for the combination, else a hipError_t.
 int launch_decode(const DecodeArgs& a, int kv_dtype, int q_dtype, int out_dtype, int block_size,
                   int head_dim, void* stream);

@@ -167,8 +167,19 @@ class PagedKVEngine:
     def write_step(self, si: StepInputs, stream=None) -> None:
         pa_cache_write(si.k_new, si.v_new, si.slots, self.k_pool, self.v_pool, self.pool, stream)
 
+    def use_cascade(self, si: StepInputs, width: int) -> None:
+        """Decode the batch (requests x `width` branches) reading each request's shared blocks once."""
+        from .cascade import CascadeDecode
+        wl = self.wl
+        si.cascade = CascadeDecode(si.dec_tables.cpu().numpy(), np.asarray(wl.decode_lens, np.int32), wl.block_size,
+                                   width, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, self.device)
+
     def decode_step(self, si: StepInputs, stream=None, out: Optional[torch.Tensor] = None) -> None:
         if si.dec_q is None:
+            return
+        if getattr(si, "cascade", None) is not None:
+            si.cascade.run(si.dec_q, self.k_pool, self.v_pool, self.pool, self.wl.scale,
+                           si.dec_out if out is None else out, stream)
             return
         pa_decode(si.dec_q, self.k_pool, self.v_pool, self.pool, si.dec_tables, si.dec_lens, self.wl.scale,
                   si.dec_out if out is None else out, si.dec_max_len, si.dec_partition, si.dec_workspace, stream)

@@ -139,6 +139,42 @@ def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool:
                           pa_dtype(out), _stream(stream)))
 
 
+def pa_decode_ex(q_base: torch.Tensor, q_strides, num_seqs: int, num_q_heads: int, k_pool: torch.Tensor,
+                 v_pool: torch.Tensor, pool: PoolDesc, tables_ptr: int, max_blocks_per_seq: int,
+                 context_lens: torch.Tensor, scale: float, out_base: torch.Tensor, out_strides, max_context_len: int,
+                 lse: Optional[torch.Tensor], workspace: torch.Tensor, partition_size: int = 0, stream=None) -> None:
+    """pa_decode over strided q and out rows (element strides for sequence, KV head, head in the
+    group; None = dense) with an optional log-sum-exp output.  `tables_ptr` is a device address
+    (a table row stride of max_blocks_per_seq entries may skip rows of a larger table)."""
+    qs = None if q_strides is None else (ctypes.c_int64 * 3)(*[int(x) for x in q_strides])
+    os_ = None if out_strides is None else (ctypes.c_int64 * 3)(*[int(x) for x in out_strides])
+    if context_lens.dtype != torch.int32:
+        raise TypeError("context_lens must be int32")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib().pa_decode_ex(_dev(q_base, "q"), pa_dtype(q_base), qs, _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                             ctypes.byref(pool), int(tables_ptr), int(max_blocks_per_seq),
+                             _dev(context_lens, "context_lens"), int(num_seqs), int(num_q_heads), float(scale),
+                             int(partition_size), int(max_context_len), _dev(workspace, "workspace"), ws_bytes,
+                             _dev(out_base, "out"), pa_dtype(out_base), os_,
+                             None if lse is None else _dev(lse, "lse"), _stream(stream)))
+
+
+def pa_merge_states(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+                    out: torch.Tensor, lse_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Combine two results of the same rows over disjoint key sets (float [rows..., head_dim] each,
+    their log-sum-exps float [rows...]) into out (float or bf16)."""
+    head_dim = int(o_a.shape[-1])
+    rows = o_a.numel() // head_dim
+    for t, name in ((o_a, "o_a"), (o_b, "o_b"), (lse_a, "lse_a"), (lse_b, "lse_b")):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if o_b.numel() != o_a.numel() or out.numel() != o_a.numel() or lse_a.numel() != rows or lse_b.numel() != rows:
+        raise ValueError("shapes disagree")
+    check(lib().pa_merge_states(_dev(o_a, "o_a"), _dev(lse_a, "lse_a"), _dev(o_b, "o_b"), _dev(lse_b, "lse_b"),
+                                rows, head_dim, _dev(out, "out"), pa_dtype(out),
+                                None if lse_out is None else _dev(lse_out, "lse_out"), _stream(stream)))
+
+
 def pa_prefill_chunk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc,
                      block_tables: torch.Tensor, query_start_loc: torch.Tensor,
                      prior_context_lens: torch.Tensor, scale: float, max_chunk_len: int, out: torch.Tensor,

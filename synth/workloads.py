@@ -70,6 +70,7 @@ class Workload:
     prefill_chunk: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))
     q_prefill: Optional[torch.Tensor] = None     # [sum(chunk), Hq, D]
     partition_size: int = 0                      # 0: the library picks
+    beam_width: int = 0                          # > 0: the decode batch is requests x this many branches
     notes: str = ""
 
     @property
@@ -325,6 +326,7 @@ def _fork_storm_bf16(name, size, rng, gen, device, block_size):
         scale=_fp32(1.0 / math.sqrt(d)), k_scale=1.0, v_scale=1.0,
         history=history, step=step, post=[], k_tok=k.to(torch.bfloat16), v_tok=v.to(torch.bfloat16),
         decode_seqs=seqs, decode_lens=np.asarray([lens[s // width] for s in seqs], np.int32), q_decode=q,
+        beam_width=width,
         notes=f"{n_req} requests x {width} branches sharing every prompt block; "
               f"{n_req * (width - 1)} copy-on-write copies in the step")
 

@@ -203,3 +203,37 @@ def test_merge_handles_partitions_far_apart():
     assert max(ms) - min(ms) > 80
     got = merge_partitions(ms, [p[1] for p in parts], [p[2] for p in parts])
     np.testing.assert_allclose(got, attend(q, k, v, 0.9), rtol=0, atol=1e-12)
+
+
+# ---- log-sum-exp (cascade merges) ----------------------------------------------------------------
+
+def test_lse_closed_forms():
+    """One key: the logit itself; L equal keys: logit + ln L; no keys: -inf; a shift of every logit
+    by c shifts the log-sum-exp by c."""
+    from oracle import ref_lse
+    rng = np.random.default_rng(11)
+    q, k = rng.normal(size=8), rng.normal(size=(1, 8))
+    assert ref_lse(q, k, 0.5) == pytest.approx(0.5 * float(k[0] @ q), abs=1e-14)
+    kk = np.repeat(k, 37, axis=0)
+    assert ref_lse(q, kk, 0.5) == pytest.approx(0.5 * float(k[0] @ q) + np.log(37), abs=1e-12)
+    assert ref_lse(q, np.zeros((0, 8)), 0.5) == float("-inf")
+    big = rng.normal(size=(50, 8)) * 30.0       # logits far beyond exp's range
+    z = big @ q
+    assert np.isfinite(ref_lse(q, big, 1.0))
+    assert ref_lse(q, big, 1.0) == pytest.approx(z.max() + np.log(np.exp(z - z.max()).sum()), rel=1e-14)
+
+
+def test_merge_of_two_key_sets_by_lse_is_the_whole_softmax():
+    """Attention over keys [0, S) and [S, L) combined by their log-sum-exps equals attention over all
+    L keys; the combined log-sum-exp is that of all keys."""
+    from oracle import ref_lse
+    rng = np.random.default_rng(12)
+    q, k, v = rng.normal(size=16), rng.normal(size=(90, 16)), rng.normal(size=(90, 16))
+    for S in (0, 1, 45, 89, 90):
+        la, lb = ref_lse(q, k[:S], 0.3), ref_lse(q, k[S:], 0.3)
+        oa = attend(q, k[:S], v[:S], 0.3) if S else np.zeros(16)
+        ob = attend(q, k[S:], v[S:], 0.3) if S < 90 else np.zeros(16)
+        m = max(la, lb)
+        wa, wb = np.exp(la - m), np.exp(lb - m)
+        np.testing.assert_allclose((oa * wa + ob * wb) / (wa + wb), attend(q, k, v, 0.3), atol=1e-13)
+        assert m + np.log(wa + wb) == pytest.approx(ref_lse(q, k, 0.3), abs=1e-12)
