@@ -37,12 +37,12 @@ def _dense_kv(ref, wl, sid, L):
     return gather_seq(kv[0], ref.tables[sid], L), gather_seq(kv[1], ref.tables[sid], L, "v")
 
 
-@pytest.mark.parametrize("name", ["llama7b_bf16", "gqa_long_bf16"])
+@pytest.mark.parametrize("name", ["llama7b_bf16", "gqa_long_bf16", "mixed_fp8", "tiny_fp32"])
 def test_decode_lse_and_strided_rows(name):
     """Dense strides reproduce pa_decode's bits; the log-sum-exp matches the oracle (whole segments,
     split pieces and merged partitions alike); q and out with a sequence stride that skips rows."""
     from paged_kv_cache_427_amd.ops import pa_decode_ex, pa_decode_workspace_size
-    wl, eng, si = _run(name)
+    wl, eng, si = _run(name, "full" if name == "tiny_fp32" else "small")
     ref = run_paged(wl)
     n, hq, d = si.dec_q.shape
     lse = torch.full((n, hq), 7.0, dtype=torch.float32, device="cuda")
@@ -54,7 +54,8 @@ def test_decode_lse_and_strided_rows(name):
                      si.dec_tables.shape[1], si.dec_lens, wl.scale, out, None, si.dec_max_len, lse, ws, part)
         torch.cuda.synchronize()
         if part == si.dec_partition:
-            assert torch.equal(out.view(torch.int16), si.dec_out.view(torch.int16))
+            bits = torch.int32 if out.dtype == torch.float32 else torch.int16
+            assert torch.equal(out.view(bits), si.dec_out.view(bits))
         q = act_values(tensor_bits(wl.q_decode), wl.act_dtype)
         worst = 0.0
         for bi, (sid, L) in enumerate(zip(wl.decode_seqs, wl.decode_lens)):
@@ -74,7 +75,8 @@ def test_decode_lse_and_strided_rows(name):
                  si.dec_tables.shape[1], si.dec_lens, wl.scale, o2, strides, si.dec_max_len, None, si.dec_workspace,
                  si.dec_partition)
     torch.cuda.synchronize()
-    assert torch.equal(o2[::2].view(torch.int16), si.dec_out.view(torch.int16))
+    bits = torch.int32 if o2.dtype == torch.float32 else torch.int16
+    assert torch.equal(o2[::2].view(bits), si.dec_out.view(bits))
     assert torch.all(o2[1::2] == 5.0)
 
 
