@@ -434,7 +434,7 @@ def main():
                          "calibrates hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is a design note, not code)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():

@@ -50,7 +50,7 @@ typedef enum pa_status {
   PA_ERR_INVALID = 1,     /* a host argument is out of range or null */
   PA_ERR_OOM = 2,         /* allocator: not enough free blocks (state unchanged) */
   PA_ERR_HIP = 3,         /* the HIP runtime reported an error (launch or device query) */
-  PA_ERR_UNSUPPORTED = 4  /* a valid combination this build has no kernel for */
+  PA_ERR_UNSUPPORTED = 4  /* a valid combination the library has no kernel for */
 } pa_status;
 
 typedef enum pa_dtype {
