@@ -486,3 +486,41 @@ def test_workspace_size_formula():
     assert n.value == one_part                                 # 0 = no partition cuts
     assert one_part >= 256 + 8 * 4 * (128 + 4) * 4
     assert L.pa_decode_workspace_size(4, 8, 128, 512, 48, ctypes.byref(n)) == PA_ERR_INVALID
+
+
+# ---- validation of the newer device calls (fails before any GPU work) -------------------------------
+
+def test_decode_ex_merge_layers_swap_reject_bad_arguments():
+    L = lib()
+    p = _pool()
+    bad = (ctypes.c_int64 * 3)(6, 2, 1)                 # not multiples of 4 elements
+    assert L.pa_decode_ex(FAKE, 1, bad, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16, FAKE,
+                          1 << 30, FAKE, 1, None, None, None) == PA_ERR_INVALID
+    odd = (ctypes.c_int64 * 3)(256, 4, 4)               # with lse_out, strides must be multiples of head_dim
+    assert L.pa_decode_ex(FAKE, 1, None, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16, FAKE,
+                          1 << 30, FAKE, 1, odd, FAKE, None) == PA_ERR_INVALID
+    assert L.pa_merge_states(FAKE, FAKE, FAKE, FAKE, 4, 6, FAKE, 1, None, None) == PA_ERR_INVALID   # head_dim % 4
+    assert L.pa_merge_states(FAKE, FAKE, FAKE, FAKE, 4, 128, FAKE, 7, None, None) == PA_ERR_INVALID  # dtype
+    assert L.pa_merge_states(None, FAKE, FAKE, FAKE, 4, 128, FAKE, 0, None, None) == PA_ERR_INVALID
+    assert L.pa_merge_states(None, None, None, None, 0, 128, None, 0, None, None) == 0               # empty
+    # layers: stride smaller than one layer's pool, or not a multiple of 16
+    assert L.pa_copy_blocks_layers(FAKE, FAKE, 1024, 2, ctypes.byref(p), FAKE, 1, None) == PA_ERR_INVALID
+    assert L.pa_copy_blocks_layers(FAKE, FAKE, 10**9 + 8, 2, ctypes.byref(p), FAKE, 1, None) == PA_ERR_INVALID
+    assert L.pa_copy_blocks_layers(FAKE, FAKE, 0, 0, ctypes.byref(p), FAKE, 1, None) == PA_ERR_INVALID
+    # swap: pools of different formats
+    q = _pool(block_size=32)
+    assert L.pa_swap_blocks(FAKE, FAKE, ctypes.byref(p), FAKE, FAKE, ctypes.byref(q), FAKE, 1, None) == PA_ERR_INVALID
+    assert L.pa_swap_blocks(FAKE, FAKE, ctypes.byref(p), FAKE, FAKE, ctypes.byref(p), FAKE, 0, None) == 0
+
+
+def test_plan_shared_blocks():
+    from paged_kv_cache_427_amd.cascade import plan_shared_blocks
+    b = 16
+    tabs = np.array([[5, 6, 7, 0], [5, 6, 9, 0], [5, 6, 7, 8], [5, 6, 7, 3],     # group 0: share 2 blocks
+                     [1, 2, 3, 4], [1, 2, 3, 4], [1, 2, 3, 4], [1, 2, 3, 4]],    # group 1: lengths limit it
+                    dtype=np.int32)
+    lens = np.array([40, 40, 60, 60, 33, 64, 64, 64], dtype=np.int32)
+    assert plan_shared_blocks(tabs, lens, b, 4).tolist() == [2, 2]
+    assert plan_shared_blocks(tabs, lens, b, 2).tolist() == [2, 3, 2, 4]
+    with pytest.raises(PaError):
+        plan_shared_blocks(tabs[:6], lens[:6], b, 4)
