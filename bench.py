@@ -18,6 +18,10 @@ Prints one JSON line.  `value` is the decode's unique KV bytes per step (each ph
 divided by the step time, in GB/s.  `roofline` prices the decode launch (plan, stream and merge kernels),
 timed with HIP events on the launch stream, against the 8 TB/s HBM peak.  `cpu_baseline` is the
 fp64 CPU oracle timed on a bounded sample of the same workload on this host's cores.
+
+The default warm-up is 100 untimed steps: the MFMA-bound prefill of the mixed fp8 step runs 12%
+slower in its first ~70 ms of load on MI355X (0.348 ms after 3 warm-up steps, 0.306 ms after 100)
+while the clocks settle; the HBM-bound decode is the same either way.
 """
 import argparse
 import json
@@ -421,12 +425,16 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="shared_prefix_bf16")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--contiguous-blocks", action="store_true",
+                    help="give the allocator the free list 0..N-1 instead of the workload's shuffled order, so "
+                         "each sequence's blocks lie in ascending, mostly adjacent physical order (the cost of "
+                         "the paging indirection is the difference to the default run)")
     ap.add_argument("--plain-decode", action="store_true",
                     help="beam workloads: decode every branch on its own instead of reading shared blocks once")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -452,6 +460,8 @@ def main():
         return
     t_setup = time.time()
     wl = make_workload(args.config, "full", device=dev, block_size=args.block_size)
+    if args.contiguous_blocks:
+        wl.free_order = np.arange(wl.num_blocks, dtype=np.int32)
     eng = PagedKVEngine(wl, device=dev, poison=poison_code(wl.kv_dtype))
     eng.build_history()
     si = eng.prepare_step(args.partition)
@@ -497,7 +507,8 @@ def main():
     cfg = {"workload": args.config, "num_seqs": len(wl.decode_seqs) or len(wl.prefill_seqs),
            "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
            "block_size": wl.block_size, "pool_blocks": wl.num_blocks, "kv_dtype": wl.kv_dtype,
-           "partition": si.dec_partition or 0}
+           "partition": si.dec_partition or 0,
+           "block_order": "ascending" if args.contiguous_blocks else "shuffled"}
     tab = si.dec_tables.cpu().numpy() if si.dec_tables is not None else None
     if tab is not None:
         uniq, logical, other = decode_bytes(wl, tab)
