@@ -541,6 +541,12 @@ def main():
                                 "algorithmic_bytes_per_launch": int(moved)}
     res["kernel_ms"] = {"copy_blocks": round(ms_copy, 4), "cache_write": round(ms_write, 4),
                         "prefill": round(ms_prefill, 4), "decode": round(ms_decode, 4)}
+    # spread over the timed steps (kernel_ms holds the means)
+    res["kernel_ms_spread"] = {name: {"median": round(float(np.median(parts[:, j])), 4),
+                                      "min": round(float(np.min(parts[:, j])), 4),
+                                      "p90": round(float(np.percentile(parts[:, j], 90)), 4)}
+                               for j, name in ((2, "prefill"), (3, "decode"))
+                               if (name == "prefill" and wl.prefill_seqs) or (name == "decode" and wl.decode_seqs)}
     res["config"] = cfg
     copy_probe(args, dev, res)
     if not args.no_cpu_baseline and wl.decode_seqs:
