@@ -31,14 +31,15 @@
 //  * base-2 online softmax with one running max per head.  The max is raised only when a logit
 //    exceeds it by more than 2^8 (so every exp stays <= 256); that test is one wave-wide ballot, and
 //    only then are the lanes' maxima exchanged and the accumulators rescaled.
-//  * one unit of K/V is in flight per wave while the previous one is consumed (three workgroups of
-//    four waves per CU for bf16/fp8).
+//  * one unit of K/V is in flight per wave while the previous one is consumed, with one workgroup of
+//    four waves per CU (one wave per SIMD).
 //  * a piece is a wave's run of units inside one partition of one segment.  A piece that is a whole
 //    segment writes the output directly; any other piece writes (max, sum, unnormalised partial
 //    output) to its own slot, and the merge kernel combines the pieces of each (sequence, head).
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -61,7 +62,7 @@ struct Elem {
   static constexpr int kBytes = KV == kF32 ? 4 : KV == kBF16 ? 2 : 1;
 };
 
-// Workgroups per CU that the register budget of a kernel allows.
+// Workgroups per CU that the register budget of a kernel allows (the launch bound).
 template <int KV, int D>
 struct Pipe {
   static constexpr int kOcc = KV == kF32 ? 2 : 3;
@@ -783,12 +784,18 @@ int device_cus() {
   return n;
 }
 
-constexpr int kMaxOcc = 3;   // the largest Pipe<>::kOcc
+// Workgroups of the persistent grid: one per CU.  Measured on MI355X against three (what the
+// register budget allows), 1.5 and two per CU: one is fastest on every workload (Llama-7B-shaped
+// decode 236 -> 227 us, GQA long 630 -> 614 us, fp8 decode of the mixed step 339 -> 320 us, beam
+// decode 691 -> 670 us, shared-prefix decode unchanged): each wave keeps a three times longer share,
+// so fewer segment starts and fewer partial records, and one unit in flight per wave on every SIMD
+// still keeps HBM busy.  Half a workgroup per CU is slower (260, 742, 482 us).
+int grid_workgroups() { return std::max(8, device_cus() / 8 * 8); }
 
 template <int KV, int D, int BS, int G>
 int launch_one(const DecodeArgs& a0, int out_bf16, hipStream_t s) {
   DecodeArgs a = a0;
-  const int64_t wgs = static_cast<int64_t>(device_cus()) * Pipe<KV, D>::kOcc / 8 * 8;   // resident, multiple of 8
+  const int64_t wgs = grid_workgroups();   // resident, multiple of 8
   a.streams = a.num_kv_heads % 8 == 0 ? 8 : 1;
   a.stream_waves = static_cast<int32_t>(wgs / a.streams * kWaves);
   a.max_shares = kSharesPerWave * a.stream_waves;   // bounds the plan's share count V
@@ -837,7 +844,7 @@ int pick_dim(const DecodeArgs& a, int bs, int d, int out_bf16, hipStream_t s) {
 
 }  // namespace
 
-int decode_max_waves() { return device_cus() * kMaxOcc * kWaves; }
+int decode_max_waves() { return grid_workgroups() * kWaves; }
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
