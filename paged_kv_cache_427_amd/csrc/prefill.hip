@@ -25,7 +25,8 @@
 //    the keys inside each 16-key group;
 //  * scores are formed transposed, S^T = K Q^T (A = K rows from LDS, B = Q held in registers), so the
 //    fp32 result layout (each lane owns one query row and 16 keys) becomes, after bf16 rounding,
-//    exactly the B operand of O^T = V^T P^T; softmax statistics need one cross-half lane exchange;
+//    exactly the B operand of O^T = V^T P^T; softmax statistics need one cross-half lane exchange
+//    (v_permlane32_swap);
 //  * logits are scaled and shifted by one fma before the exp; the rescale of the output accumulators
 //    is skipped while the running max has grown by less than 2^8 (base-2 logits), which keeps every
 //    exp bounded by 256;
@@ -68,6 +69,18 @@ __device__ __forceinline__ uint32_t fp8x2_lo(uint32_t w) {
 }
 __device__ __forceinline__ uint32_t fp8x2_hi(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
+// Combine of each lane with its partner lane ^ 32 through v_permlane32_swap (a VALU exchange, no LDS
+// round trip): given x in both operands, the first result holds lanes 0-31's values in both halves
+// and the second lanes 32-63's, so their max (sum) is the pair's max (sum) in every lane.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Global -> registers -> LDS for one 64-key tile.
@@ -335,7 +348,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) prefill_kernel(Prefill
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[sb][r]);
-    mx = fmaxf(mx, shfl_xor(mx, 32)) * c2;     // base-2 logit units (c2 > 0)
+    mx = half_max(mx) * c2;     // base-2 logit units (c2 > 0)
     // rescale only when the max moved by more than the slack (wave-uniform decision)
     const bool grow = mx > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -361,7 +374,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) prefill_kernel(Prefill
         lsum += p;
         pb[c][e] = static_cast<__bf16>(p);
       }
-    l_run += lsum + shfl_xor(lsum, 32);
+    l_run += half_sum(lsum);
     ld.store_v(odd ? vbuf0 : vbuf1, min(t + 1, last) * kKT, n_keys, wave, lane);
     ld.load_v(vpool, tab, blk_stride, head_off, min(t + 2, last) * kKT, n_keys, wave, lane);
 
