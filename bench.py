@@ -15,7 +15,7 @@ as one HIP graph; `--config serving_llama7b_bf16` runs a continuous-batching loo
 request stream and reports KV utilisation against a max-length reservation.
 
 Prints one JSON line.  `value` is the decode's unique KV bytes per step (each physical block once)
-divided by the step time, in GB/s.  `roofline` prices the decode launch (plan, stream and merge kernels),
+divided by the step time, in GB/s.  `roofline` prices the decode launch (stream and merge kernels),
 timed with HIP events on the launch stream, against the 8 TB/s HBM peak.  `cpu_baseline` is the
 fp64 CPU oracle timed on a bounded sample of the same workload on this host's cores.
 
@@ -367,7 +367,7 @@ def layers_bench(args, dev, num_layers: int = 32):
                       "identical_to_eager": same},
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                         "kernel": "pa_decode of one layer (plan + stream + merge kernels)",
+                         "kernel": "pa_decode of one layer (stream + merge kernels)",
                          "algorithmic_bytes_per_launch": int(uniq + other)},
             "config": {"workload": "llama7b_32layer_bf16", "layers": num_layers, "num_seqs": len(wl.decode_seqs),
                        "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
@@ -520,7 +520,7 @@ def main():
                            "traffic": measured_traffic(args.config, args.block_size),
                            "kernel": ("beam decode: pa_decode_ex over shared blocks + over private tails + "
                                       "pa_merge_states" if getattr(si, "cascade", None) is not None else
-                                      "pa_decode (plan + stream + merge kernels)"),
+                                      "pa_decode (stream + merge kernels)"),
                            "algorithmic_bytes_per_launch": int(uniq + other)}
         res["decode_logical_kv_GBps"] = round(logical / (ms_decode * 1e-3) / 1e9, 1)
         cfg["mean_context"] = round(float(np.mean(wl.decode_lens)), 1)

@@ -151,10 +151,9 @@ pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const pa_pool_desc*
  * current device (the size depends on its compute-unit count).
  *   partition_size 0 means the library's choice (the same choice pa_decode makes for 0).
  * The workspace holds the work plan (per-sequence unit counts, the split of the work among the
- * resident waves, and a counter per XCD that hands out the last few shares) and the partial (max,
- * sum, unnormalised output) records of context pieces: one record of head_dim + 4 floats per
- * (query head, sequence, partition) plus a bounded number per resident wave.  pa_decode rewrites
- * all of it on every call.
+ * resident waves) and the partial (max, sum, unnormalised output) records of context pieces: one
+ * record of head_dim + 4 floats per (query head, sequence, partition) plus a bounded number per
+ * resident wave.  pa_decode rewrites all of it on every call.
  * ------------------------------------------------------------------------------------------- */
 pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t max_context_len, int32_t partition_size, size_t* bytes);
@@ -183,7 +182,7 @@ pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_
  *                 bf16 rounds to nearest-even from the fp32 accumulator)
  * Combinations: pool PA_F32 needs q PA_F32; pools PA_BF16 / PA_FP8_E4M3 need q PA_BF16.
  * Results are deterministic: the pieces and every reduction order depend only on the sizes and
- * lengths (the counter only decides which wave runs a piece, not what the piece computes).
+ * lengths.
  * ------------------------------------------------------------------------------------------- */
 pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
                     const pa_pool_desc* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -315,30 +315,46 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int seq) { retur
 
 // ---- work plan ---------------------------------------------------------------------------------
 // The units (32 keys) of every (KV head, sequence) segment form one stream per XCD, in the order
-// (head slot, sequence, unit).  Each wave of a stream takes one contiguous static share of
-// kStaticPct % of the stream / waves positions; the rest is handed out in shares of at least
-// kMinShare units from a counter to the waves that finish first.  (Measured on MI355X: any larger
-// dynamic part is slower -- each extra share costs the wave a cold start on a new segment's table
-// entries and Q and adds a partial record -- so the static part is the whole stream but the
-// remainder of the division, fewer positions than waves.)  Share v covers [start(v), start(v + 1)):
-//   start(v) = v * S0                       for v <  W0  (W0 = waves of the stream, or 0 if S0 = 0)
-//   start(v) = W0 * S0 + (v - W0) * S1      for v >= W0
-// All streams have the same shape (the same sequences, num_kv_heads / streams heads each), so one
-// table of share start cursors serves them all.
+// (head slot, sequence, unit).  Wave v of a stream takes the contiguous static share [v S, (v + 1) S)
+// of it, S = ceil(units / waves), so no wave has more than S units and the shares need no counter.
+// (Measured on MI355X: handing part of each stream out dynamically, to the waves that finish
+// first, was slower -- each extra share costs a cold start on a new segment's table entries and Q
+// and adds a partial record.)  All streams have the same shape (the same sequences,
+// num_kv_heads / streams heads each), so one schedule serves them all.  A batch of at most
+// kSelfPlanMax sequences is planned by every workgroup of the stream kernel itself: the prefix of
+// per-sequence unit counts in LDS, each wave's start cursor by a binary search in it (no plan
+// launch, whose few microseconds and launch gap are a few percent of a short decode).  A larger
+// batch is planned by the one-workgroup plan kernel, which also writes every share's start cursor.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanLds = 8192;        // prefix entries searched in LDS (larger batches search global memory)
-constexpr int kStaticPct = 100;       // part of a stream taken in static shares
-constexpr int kMinShare = 4;          // units per dynamic share, at least
-constexpr int kDynPerWave = 1;        // dynamic shares per wave of the stream, at most
-constexpr int kSharesPerWave = 1 + kDynPerWave;
-constexpr int kCtrStride = 32;        // ints between two counters (one per 128-byte line)
-constexpr int kSchedInts = kCtrStride * 10;
-// schedule header: [0] S0, [1] S1, [2] W0, [3] V; counter of stream x at [kCtrStride * (x + 1)]
+constexpr int kSelfPlanMax = 4096;    // batches the stream kernel plans itself
+constexpr int kSharesPerWave = 1;
+constexpr int kSchedInts = 64;
+// schedule header: [0] S (units per share), [1] V (shares)
 
 struct Sched {
-  int S0, S1, W0, V;
-  __device__ __forceinline__ int start(int v) const { return v < W0 ? v * S0 : W0 * S0 + (v - W0) * S1; }
-  __device__ __forceinline__ int share_of(int p) const { return p < W0 * S0 ? p / S0 : W0 + (p - W0 * S0) / S1; }
+  int S, V;
+  __device__ __forceinline__ int start(int v) const { return v * S; }
+  __device__ __forceinline__ int share_of(int p) const { return p / S; }
+};
+
+// The schedule of `total` stream positions over `waves` waves.
+__device__ __forceinline__ Sched make_sched(int total, int waves) {
+  Sched sc;
+  sc.S = max(1, (total + waves - 1) / waves);
+  sc.V = (total + sc.S - 1) / sc.S;
+  return sc;
+}
+
+// Prefix of per-sequence unit counts, read from LDS (stream kernel that planned itself) or from the
+// plan kernel's table.
+struct PrefView {
+  const int* lds;
+  const int32_t* g;
+  bool in_lds;
+  __device__ __forceinline__ int operator[](int k) const {
+    return in_lds ? lds[k] : ro(g)[k];
+  }
 };
 
 // Largest s with pref[s] <= r (then pref[s + 1] > r: sequence s holds unit r of its head slot).
@@ -353,7 +369,7 @@ __device__ __forceinline__ int find_seq(const P& pref, int n, int r) {
 }
 
 // One workgroup: pref[s] = sum over sequences s' < s of ceil(L_s' / 32); the schedule header; the
-// start cursor (head slot, sequence, unit, units of the sequence) of every share; zeroed counters.
+// start cursor (head slot, sequence, unit, units of the sequence) of every share.
 __global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(DecodeArgs a) {
   __shared__ int csum[kPlanThreads];
   __shared__ int spref[kPlanLds];
@@ -384,20 +400,11 @@ __global__ void __launch_bounds__(kPlanThreads) decode_plan_kernel(DecodeArgs a)
   }
   const int useq = csum[kPlanThreads - 1];
   const int total = (a.num_kv_heads / a.streams) * useq;
-  const int W = a.stream_waves;
-  Sched sc;
-  sc.S0 = static_cast<int>(static_cast<int64_t>(total) * kStaticPct / 100 / W);
-  sc.W0 = sc.S0 > 0 ? W : 0;
-  const int rest = total - sc.W0 * sc.S0;
-  sc.S1 = max(kMinShare, (rest + kDynPerWave * W - 1) / (kDynPerWave * W));
-  sc.V = sc.W0 + (rest + sc.S1 - 1) / sc.S1;
+  const Sched sc = make_sched(total, a.stream_waves);
   if (tid == 0) {
-    a.ws_sched[0] = sc.S0;
-    a.ws_sched[1] = sc.S1;
-    a.ws_sched[2] = sc.W0;
-    a.ws_sched[3] = sc.V;
+    a.ws_sched[0] = sc.S;
+    a.ws_sched[1] = sc.V;
   }
-  if (tid < 8) a.ws_sched[kCtrStride * (tid + 1)] = 0;
   __syncthreads();   // the prefix written above is read back by other threads of this workgroup
   for (int v = tid; v < sc.V; v += kPlanThreads) {
     const int p = sc.start(v);
@@ -423,7 +430,7 @@ struct Cursor {
 };
 
 // Next stream position (sequences without units are skipped).  Only called while a next position exists.
-__device__ __forceinline__ void advance(Cursor& c, ro_i32 pref, int n) {
+__device__ __forceinline__ void advance(Cursor& c, const PrefView& pref, int n) {
   if (++c.j < c.nj) return;
   c.j = 0;
   do {
@@ -514,39 +521,37 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs& a, int out_bf16, 
 }
 
 // A stream position prepared for loading: its cursor, the view of its segment, its blocks, its
-// share (and the wave's following share), and whether it enters a segment or a share (its Q must be
-// loaded with it).  `live` is false once the wave has no position left: the position then stays on
+// share, and whether it enters a segment or a share (its Q must be loaded with it).  `live` is false once the wave has no position left: the position then stays on
 // the wave's last unit, which is loaded again (in bounds, unused).
 template <int BS>
 struct Pos {
   Cursor c;
   SeqView v;
   UnitBlocks<BS> ub;
-  int pos, end, share, next;
+  int pos, end, share;
   bool enter, live;
 };
 
-// Asks the stream's counter for one more share: lane 0 adds 1 (device scope) and gets the old value.
-// The per-lane address keeps the add a single plain one (no wave-wide rewrite that would read the
-// answer at once).
-__device__ __forceinline__ int grab_share(int32_t* ctr, int lane) {
-  int got = 0;
-  if (lane == 0) {
-    int32_t __attribute__((address_space(1)))* p = (int32_t __attribute__((address_space(1)))*)ctr;
-    asm volatile("" : "+v"(p));
-    got = __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  return got;
-}
-
-// Points P at the first unit of share v (the plan table holds its start cursor).
+// Points P at the first unit of share v: its start cursor from the plan table, or found in the LDS
+// prefix (useq units per head slot).
 template <int KV, int D, int BS>
-__device__ __forceinline__ void enter_share(const DecodeArgs& a, int x, int total, const Sched& sc, Pos<BS>& P, int v) {
-  const ro_i32 e = ro(a.ws_share) + 4 * v;
-  P.c.hh = e[0];
-  P.c.seq = e[1];
-  P.c.j = e[2];
-  P.c.nj = e[3];
+__device__ __forceinline__ void enter_share(const DecodeArgs& a, int x, int total, int useq, const Sched& sc,
+                                            const PrefView& pref, Pos<BS>& P, int v) {
+  if (pref.in_lds) {
+    const int p = sc.start(v);
+    const int hh = p / useq, rem = p - hh * useq;
+    const int seq = find_seq(pref, a.num_seqs, rem);
+    P.c.hh = hh;
+    P.c.seq = seq;
+    P.c.j = rem - pref[seq];
+    P.c.nj = pref[seq + 1] - pref[seq];
+  } else {
+    const ro_i32 e = ro(a.ws_share) + 4 * v;
+    P.c.hh = e[0];
+    P.c.seq = e[1];
+    P.c.j = e[2];
+    P.c.nj = e[3];
+  }
   P.share = v;
   P.pos = sc.start(v);
   P.end = min(total, sc.start(v + 1));
@@ -554,28 +559,20 @@ __device__ __forceinline__ void enter_share(const DecodeArgs& a, int x, int tota
   P.enter = true;
 }
 
-// Moves P to the wave's next position -- the next unit of the share, else the first unit of the
-// wave's next share, which is asked for here -- and reads that position's block-table entries.  It
+// Moves P to the next unit of the wave's share and reads that position's block-table entries.  It
 // runs right after the loads of the current position are issued, so these dependent scalar reads
 // overlap the loads in flight instead of delaying the next issue.
 template <int KV, int D, int BS>
-__device__ __forceinline__ void prepare_next(const DecodeArgs& a, int x, int total, const Sched& sc, int32_t* ctr,
-                                             Pos<BS>& P, int lane) {
+__device__ __forceinline__ void prepare_next(const DecodeArgs& a, int x, const PrefView& pref, Pos<BS>& P) {
   P.enter = false;
   if (P.pos + 1 < P.end) {
     ++P.pos;
-    advance(P.c, ro(a.ws_pref), a.num_seqs);
+    advance(P.c, pref, a.num_seqs);
     if (P.c.j == 0) {
       P.v = seq_view<KV, D, BS>(a, P.c.seq, x + a.streams * P.c.hh);
       P.enter = true;
     }
     P.ub = unit_blocks<BS>(P.v, P.c.j * kUnit);
-  } else if (P.next < sc.V) {
-    enter_share<KV, D, BS>(a, x, total, sc, P, P.next);
-    const int got = grab_share(ctr, lane);
-    P.ub = unit_blocks<BS>(P.v, P.c.j * kUnit);
-    __builtin_amdgcn_sched_barrier(0);
-    P.next = a.stream_waves + __builtin_amdgcn_readfirstlane(got);   // after the table reads are issued
   } else {
     P.live = false;
   }
@@ -591,9 +588,8 @@ __device__ __forceinline__ void issue(const DecodeArgs& a, int x, const Pos<BS>&
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Persistent grid of waves over the unit streams.  A wave starts on the share of its own index and
-// then takes the stream's next untaken share until none is left; one register ring runs across all
-// its shares and segments: each consume is followed by the loads of the next position, and the
+// Persistent grid of waves over the unit streams.  Wave v of stream x walks share v; one register
+// ring runs across all the segments of its share: each consume is followed by the loads of the next position, and the
 // position after that is prepared while those loads are in flight.  With streams == 8 the KV heads
 // of stream x are served by the workgroups on XCD x (initial dispatch is round-robin over the 8
 // XCDs), so blocks shared by many sequences (a common prefix) are re-read from that XCD's L2.
@@ -606,14 +602,51 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
   const int kg = lane >> 4;        // k-group of an operand / row group of an accumulator
   const int x = blockIdx.x % a.streams;
   const int wi = (blockIdx.x / a.streams) * kWaves + wave;
+  const int n = a.num_seqs;
+  const bool self_plan = a.self_plan != 0;
+  __shared__ int spref[kSelfPlanMax + 1];
+  __shared__ int scan_s[kThreads];
+  int useq;
   Sched sc;
-  sc.S0 = ro(a.ws_sched)[0];
-  sc.S1 = ro(a.ws_sched)[1];
-  sc.W0 = ro(a.ws_sched)[2];
-  sc.V = ro(a.ws_sched)[3];
+  if (self_plan) {
+    // spref[s] = units of the sequences before s: a block-wide scan of per-thread runs
+    const int tid = threadIdx.x;
+    const int chunk = (n + kThreads - 1) / kThreads;
+    const int s0 = min(tid * chunk, n), s1 = min(s0 + chunk, n);
+    int local = 0;
+    for (int s = s0; s < s1; ++s) local += (clamped_len(a, s) + kUnit - 1) / kUnit;
+    scan_s[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off *= 2) {
+      const int v = tid >= off ? scan_s[tid - off] : 0;
+      __syncthreads();
+      scan_s[tid] += v;
+      __syncthreads();
+    }
+    int run = scan_s[tid] - local;
+    if (tid == 0) spref[0] = 0;
+    for (int s = s0; s < s1; ++s) {
+      run += (clamped_len(a, s) + kUnit - 1) / kUnit;
+      spref[s + 1] = run;
+    }
+    __syncthreads();
+    useq = spref[n];
+    sc = make_sched((a.num_kv_heads / a.streams) * useq, a.stream_waves);
+    if (blockIdx.x == 0) {   // the merge kernel reads the prefix and the schedule
+      for (int s = tid; s <= n; s += kThreads) a.ws_pref[s] = spref[s];
+      if (tid == 0) {
+        a.ws_sched[0] = sc.S;
+        a.ws_sched[1] = sc.V;
+      }
+    }
+  } else {
+    useq = ro(a.ws_pref)[n];
+    sc.S = ro(a.ws_sched)[0];
+    sc.V = ro(a.ws_sched)[1];
+  }
   if (wi >= sc.V) return;
-  const int total = (a.num_kv_heads / a.streams) * ro(a.ws_pref)[a.num_seqs];
-  int32_t* ctr = a.ws_sched + kCtrStride * (x + 1);
+  const int total = (a.num_kv_heads / a.streams) * useq;
+  const PrefView pref{spref, a.ws_pref, self_plan};
   const int PU = a.part_tokens / kUnit;
 
   St st;
@@ -621,14 +654,12 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
   UnitRegs<KV, D> R;
   Pos<BS> P;
   P.live = true;
-  enter_share<KV, D, BS>(a, x, total, sc, P, wi);
-  const int got = grab_share(ctr, lane);
+  enter_share<KV, D, BS>(a, x, total, useq, sc, pref, P, wi);
   P.ub = unit_blocks<BS>(P.v, P.c.j * kUnit);
   issue<KV, D, BS, G>(a, x, P, R, qnext, i, kg);
-  P.next = a.stream_waves + __builtin_amdgcn_readfirstlane(got);
   Cursor cc = P.c;                      // the position whose unit R holds
   int share = P.share, pos = P.pos, end = P.end;
-  prepare_next<KV, D, BS>(a, x, total, sc, ctr, P, lane);
+  prepare_next<KV, D, BS>(a, x, pref, P);
 
 #pragma unroll 1
   for (;;) {
@@ -648,10 +679,10 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
       share = P.share;
       pos = P.pos;
       end = P.end;
-      prepare_next<KV, D, BS>(a, x, total, sc, ctr, P, lane);
+      prepare_next<KV, D, BS>(a, x, pref, P);
     }
     finish_piece<KV, D, G>(a, out_bf16, x, share0, st, c0, np, PU, i, kg);
-    if (!more) break;   // the last issue was a reload: every share of the wave is done
+    if (!more) break;   // the last issue was a reload: the wave's share is done
   }
 }
 
@@ -686,9 +717,8 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_b
   }
   const int x = kvh % a.streams, hh = kvh / a.streams;
   Sched sc;
-  sc.S0 = ro(a.ws_sched)[0];
-  sc.S1 = ro(a.ws_sched)[1];
-  sc.W0 = ro(a.ws_sched)[2];
+  sc.S = ro(a.ws_sched)[0];
+  sc.V = ro(a.ws_sched)[1];
   const int P0 = hh * pref[n] + pref[seq];   // stream position of the segment's first unit
   const int PU = a.part_tokens / kUnit;
   const int nparts = (nj + PU - 1) / PU;
@@ -798,11 +828,15 @@ int launch_one(const DecodeArgs& a0, int out_bf16, hipStream_t s) {
   const int64_t wgs = grid_workgroups();   // resident, multiple of 8
   a.streams = a.num_kv_heads % 8 == 0 ? 8 : 1;
   a.stream_waves = static_cast<int32_t>(wgs / a.streams * kWaves);
-  a.max_shares = kSharesPerWave * a.stream_waves;   // bounds the plan's share count V
+  a.max_shares = kSharesPerWave * a.stream_waves;   // bounds the share count V
+  a.self_plan = a.num_seqs <= kSelfPlanMax;
   a.stream_slots = static_cast<int64_t>(a.num_kv_heads / a.streams) * a.num_seqs * a.max_parts + a.max_shares;
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return static_cast<int>(e);
+  hipError_t e;
+  if (!a.self_plan) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return static_cast<int>(e);
+  }
   hipLaunchKernelGGL((decode_stream_kernel<KV, D, BS, G>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s,
                      a, out_bf16);
   e = hipGetLastError();

@@ -65,9 +65,10 @@ struct DecodeArgs {
   int32_t streams;       // unit streams: 8 (one per XCD; KV head h in stream h % 8) or 1
   int32_t stream_waves;  // waves per stream
   int32_t max_shares;    // bound on the shares of one stream
+  int32_t self_plan;     // 1: the stream kernel plans the launch itself (no plan kernel)
   int64_t stream_slots;  // partial-record slots per stream
   int32_t* ws_pref;      // [num_seqs + 1] units (32 keys) of sequences before s, for one KV head
-  int32_t* ws_sched;     // share size, share count, one share counter per stream
+  int32_t* ws_sched;     // share size, share count
   int32_t* ws_share;     // [max_shares][4] start cursor of each share: head slot, sequence, unit, units
   float* ws_part;        // [streams * stream_slots][G][head_dim + 4]: max, sum, -, -, unnormalised o
   void* out;
