@@ -1,6 +1,8 @@
-"""GPU parity of pa_decode at the edges of its work plan: more sequences than the plan kernel ranks
-in LDS (8192), and more pieces per (sequence, head) than the merge kernel lists in LDS (1024), each
-against the fp64 oracle on sampled or all outputs (bf16 tolerance 2e-2)."""
+"""GPU parity of pa_decode at the edges of its work plan: the largest batch the stream kernel plans
+itself (4096 sequences), the smallest one planned by the plan kernel (4097, prefix searched in LDS),
+more sequences than the plan kernel ranks in LDS (more than 8192), and more pieces per (sequence,
+head) than the merge kernel lists in LDS (1024), each against the fp64 oracle on sampled or all
+outputs (bf16 tolerance 2e-2)."""
 import numpy as np
 import pytest
 import torch
@@ -62,13 +64,17 @@ def _decode(q, kpool, vpool, tabs, lens, scale, max_ctx, partition):
     return out.float().cpu().numpy().astype(np.float64)
 
 
-def test_more_sequences_than_the_plan_ranks_in_lds():
-    """9000 short sequences (some empty): the plan kernel searches its prefix in global memory."""
+@pytest.mark.parametrize("n", [4096, 4097, 9000])
+def test_batches_at_the_plan_limits(n):
+    """n short sequences (some empty): up to 4096 the stream kernel plans the launch itself; above,
+    the plan kernel does, searching its prefix in LDS up to 8192 sequences and in global memory
+    beyond."""
     rng = np.random.Generator(np.random.PCG64(4271))
     gen = torch.Generator().manual_seed(4271)
-    n, hq, hkv, b, d = 9000, 16, 8, 16, 64
+    hq, hkv, b, d = 16, 8, 16, 64
     lens = rng.integers(1, 41, size=n).astype(np.int32)
-    lens[[5, 4000, 8999]] = 0
+    empty = [5, n // 2, n - 1]
+    lens[empty] = 0
     need = sum(-(-int(L) // b) for L in lens)
     num_blocks = need + 64
     kpool, vpool = _pools(gen, num_blocks, hkv, b, d)
@@ -77,9 +83,10 @@ def test_more_sequences_than_the_plan_ranks_in_lds():
     scale = float(np.float32(1.0 / np.sqrt(d)))
     _say("decode", n, "sequences, blocks", num_blocks)
     got = _decode(q, kpool, vpool, tabs, lens, scale, 40, 0)
-    for s in (5, 4000, 8999):
+    for s in empty:
         assert np.count_nonzero(got[s]) == 0
-    sample = [0, 1, 8191, 8192, 8193, 8998] + rng.choice(n, size=40, replace=False).tolist()
+    edges = [0, 1, 4095, 4096, 8191, 8192, 8193, n - 2]
+    sample = [s for s in edges if s < n] + rng.choice(n, size=40, replace=False).tolist()
     sample = [s for s in sample if lens[s] > 0]
     ref = _oracle_rows(kpool, vpool, tabs, lens, q, scale, sample)
     err = max(float(np.max(np.abs(got[s] - ref[s]))) for s in sample)
