@@ -639,6 +639,18 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
         a.ws_sched[1] = sc.V;
       }
     }
+    if (a.fill_empty) {      // no merge launch: zeros (and -inf log-sum-exps) of empty sequences here
+      const int hq = a.num_kv_heads * G;
+      for (int seq = blockIdx.x; seq < n; seq += gridDim.x) {
+        if (spref[seq + 1] != spref[seq]) continue;
+        for (int k = tid; k < hq * D; k += kThreads) {
+          const int hd = k / D, kvh = hd / G, g = hd % G;
+          const int64_t row = seq * a.o_sseq + kvh * a.o_skv + g * a.o_sg;
+          store_out(a.out, row + k % D, 0.f, out_bf16 != 0);
+          if (a.lse && k % D == 0) a.lse[row / D] = -INFINITY;
+        }
+      }
+    }
   } else {
     useq = ro(a.ws_pref)[n];
     sc.S = ro(a.ws_sched)[0];
@@ -820,16 +832,24 @@ int device_cus() {
 // decode 691 -> 670 us, shared-prefix decode unchanged): each wave keeps a three times longer share,
 // so fewer segment starts and fewer partial records, and one unit in flight per wave on every SIMD
 // still keeps HBM busy.  Half a workgroup per CU is slower (260, 742, 482 us).
-int grid_workgroups() { return std::max(8, device_cus() / 8 * 8); }
+// Contexts of at most kShortCtx tokens are the exception: each wave then walks many one- or two-unit
+// segments, each a cold start on its table entries and Q, so the launch is bound by latency and
+// takes as many waves as the registers allow (the tails of the beam decode: 92 -> 76 us).
+constexpr int kShortCtx = 2 * kUnit;
+constexpr int kMaxOcc = 3;   // the largest Pipe<>::kOcc
+int grid_workgroups(int per_cu) { return std::max(8, device_cus() * per_cu / 8 * 8); }
 
 template <int KV, int D, int BS, int G>
 int launch_one(const DecodeArgs& a0, int out_bf16, hipStream_t s) {
   DecodeArgs a = a0;
-  const int64_t wgs = grid_workgroups();   // resident, multiple of 8
+  const int64_t wgs = grid_workgroups(a.max_ctx <= kShortCtx ? Pipe<KV, D>::kOcc : 1);   // resident, multiple of 8
   a.streams = a.num_kv_heads % 8 == 0 ? 8 : 1;
   a.stream_waves = static_cast<int32_t>(wgs / a.streams * kWaves);
   a.max_shares = kSharesPerWave * a.stream_waves;   // bounds the share count V
   a.self_plan = a.num_seqs <= kSelfPlanMax;
+  // One-unit contexts are never split, so no piece needs merging: the stream kernel then writes the
+  // zeros of empty sequences itself and the merge launch is left out.
+  a.fill_empty = a.self_plan && a.max_ctx <= kUnit;
   a.stream_slots = static_cast<int64_t>(a.num_kv_heads / a.streams) * a.num_seqs * a.max_parts + a.max_shares;
   hipError_t e;
   if (!a.self_plan) {
@@ -841,6 +861,7 @@ int launch_one(const DecodeArgs& a0, int out_bf16, hipStream_t s) {
                      a, out_bf16);
   e = hipGetLastError();
   if (e != hipSuccess) return static_cast<int>(e);
+  if (a.fill_empty) return 0;
   const int64_t rw = static_cast<int64_t>(a.num_q_heads) * a.num_seqs;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<unsigned>(rw)), dim3(D), 0, s, a, out_bf16);
   return static_cast<int>(hipGetLastError());
@@ -878,7 +899,7 @@ int pick_dim(const DecodeArgs& a, int bs, int d, int out_bf16, hipStream_t s) {
 
 }  // namespace
 
-int decode_max_waves() { return grid_workgroups() * kWaves; }
+int decode_max_waves() { return grid_workgroups(kMaxOcc) * kWaves; }
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 

@@ -66,6 +66,7 @@ struct DecodeArgs {
   int32_t stream_waves;  // waves per stream
   int32_t max_shares;    // bound on the shares of one stream
   int32_t self_plan;     // 1: the stream kernel plans the launch itself (no plan kernel)
+  int32_t fill_empty;    // 1: no merge launch; the stream kernel writes the zeros of empty sequences
   int64_t stream_slots;  // partial-record slots per stream
   int32_t* ws_pref;      // [num_seqs + 1] units (32 keys) of sequences before s, for one KV head
   int32_t* ws_sched;     // share size, share count
