@@ -180,6 +180,12 @@ pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_
  *                 entry does not matter.  Calls that share a workspace must not overlap.
  *   out           device [num_seqs][num_q_heads][head_dim] of out_dtype (PA_F32 or PA_BF16;
  *                 bf16 rounds to nearest-even from the fp32 accumulator)
+ *   shared_blocks optional device int32 [num_seqs]: how many leading entries of each sequence's
+ *                 table other sequences of the call also read (a shared prefix, [day28] §六 question
+ *                 2).  Only the cache policy depends on it, never the results: K/V of those blocks
+ *                 are read through the caches so that their repeats hit; every other block is
+ *                 streamed with non-temporal loads (read once, kept out of the way of the shared
+ *                 ones): its V, and for fp8 pools its K too.  NULL: no block is shared.
  * Combinations: pool PA_F32 needs q PA_F32; pools PA_BF16 / PA_FP8_E4M3 need q PA_BF16.
  * Results are deterministic: the pieces and every reduction order depend only on the sizes and
  * lengths.
@@ -188,7 +194,8 @@ pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const vo
                     const pa_pool_desc* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                     int32_t partition_size, int32_t max_context_len, void* workspace,
-                    size_t workspace_bytes, void* out, int32_t out_dtype, pa_stream stream);
+                    size_t workspace_bytes, void* out, int32_t out_dtype, const int32_t* shared_blocks,
+                    pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
  * pa_prefill_chunk -- causal attention of a chunk of new query tokens per sequence over the
@@ -232,7 +239,8 @@ pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides,
                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                        int32_t num_q_heads, float scale, int32_t partition_size, int32_t max_context_len,
                        void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
-                       const int64_t* out_strides, float* lse_out, pa_stream stream);
+                       const int64_t* out_strides, float* lse_out, const int32_t* shared_blocks,
+                       pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
  * pa_plan_shared_blocks (host) -- for a decode batch laid out as groups of `width` consecutive

@@ -264,10 +264,11 @@ pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const vo
                     const pa_pool_desc* pool, const int32_t* tables, int32_t max_blocks,
                     const int32_t* lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                     int32_t partition_size, int32_t max_context_len, void* workspace,
-                    size_t workspace_bytes, void* out, int32_t out_dtype, pa_stream stream) {
+                    size_t workspace_bytes, void* out, int32_t out_dtype, const int32_t* shared_blocks,
+                    pa_stream stream) {
   return pa_decode_ex(q, q_dtype, nullptr, k_pool, v_pool, pool, tables, max_blocks, lens, num_seqs, num_q_heads,
                       scale, partition_size, max_context_len, workspace, workspace_bytes, out, out_dtype, nullptr,
-                      nullptr, stream);
+                      nullptr, shared_blocks, stream);
 }
 
 pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides, const void* k_pool,
@@ -275,7 +276,7 @@ pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides,
                        const int32_t* lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                        int32_t partition_size, int32_t max_context_len, void* workspace, size_t workspace_bytes,
                        void* out, int32_t out_dtype, const int64_t* out_strides, float* lse_out,
-                       pa_stream stream) {
+                       const int32_t* shared_blocks, pa_stream stream) {
   pa_status st = check_pool(pool, "pa_decode");
   if (st != PA_OK) return st;
   if (num_seqs < 0) return pa_fail(PA_ERR_INVALID, "pa_decode: negative num_seqs");
@@ -319,6 +320,7 @@ pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides,
   a.tables = tables;
   a.max_blocks = max_blocks;
   a.lens = lens;
+  a.shared_blocks = shared_blocks;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;

@@ -118,15 +118,45 @@ struct UnitRegs {
   uint32_t v[D / 16][VW];
 };
 
-template <int VW>
+// K/V loads.  NT: non-temporal (streamed: a block that no other sequence of the launch reads is read
+// once, and should not push the shared ones out of L2); otherwise through the caches.  Streaming
+// applies to the V loads of unshared blocks, and to their K loads only for fp8 pools.  Measured on
+// MI355X, decode launch inside the step (copy, write, decode), bf16: streaming V only 1.371 ms on
+// the shared-prefix decode (all through the caches 1.466, K and V streamed 1.490), 0.562 / 0.609 /
+// 0.587 ms on the GQA decode, 0.210 / 0.230 / 0.208 ms on the Llama-7B-shaped one; fp8 (mixed
+// step): K and V streamed 0.294 ms, V only 0.316, none 0.323.  A bf16 K row is two cache lines
+// that consecutive loads read in halves, and the second half is then refetched when the first
+// was not kept.
+typedef uint32_t ld_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t ld_u32x2 __attribute__((ext_vector_type(2)));
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const char* p) {
+  if constexpr (NT) {
+    const ld_u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const ld_u32x4*>(p));
+    return make_uint4(w.x, w.y, w.z, w.w);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ uint2 ld8(const char* p) {
+  if constexpr (NT) {
+    const ld_u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const ld_u32x2*>(p));
+    return make_uint2(w.x, w.y);
+  } else {
+    return *reinterpret_cast<const uint2*>(p);
+  }
+}
+
+template <int VW, bool NT>
 __device__ __forceinline__ void load_piece(uint32_t (&dst)[VW], const char* p) {
   if constexpr (VW == 2) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    const uint2 w = ld8<NT>(p);
     dst[0] = w.x; dst[1] = w.y;
   } else {
 #pragma unroll
     for (int h = 0; h < VW / 4; ++h) {
-      const uint4 w = *reinterpret_cast<const uint4*>(p + 16 * h);
+      const uint4 w = ld16<NT>(p + 16 * h);
       dst[4 * h] = w.x; dst[4 * h + 1] = w.y; dst[4 * h + 2] = w.z; dst[4 * h + 3] = w.w;
     }
   }
@@ -139,6 +169,7 @@ struct SeqView {
   ro_i32 tab;              // this sequence's block table
   int64_t blk_stride;      // bytes of one block of one pool (all KV heads)
   int nblk;                // valid table entries: ceil(L / BS)
+  int shared_units;        // units touching the sequence's shared leading blocks: read through the caches
 };
 
 // Physical blocks of the unit starting at key U (32 keys: 4, 2 or 1 blocks of 8, 16 or 32 tokens).
@@ -170,7 +201,7 @@ __device__ __forceinline__ UnitBlocks<BS> unit_blocks(const SeqView& sv, int U) 
 }
 
 // Issues the loads of the unit starting at key U (a multiple of 32) from its blocks `ub`.
-template <int KV, int D, int BS>
+template <int KV, int D, int BS, bool NT>
 __device__ __forceinline__ void load_unit(UnitRegs<KV, D>& R, const SeqView& sv, const UnitBlocks<BS>& ub, int i,
                                           int kg) {
   using R_t = UnitRegs<KV, D>;
@@ -180,12 +211,12 @@ __device__ __forceinline__ void load_unit(UnitRegs<KV, D>& R, const SeqView& sv,
     const int key = tile_row_key(t, i);                 // the unit's key in row i of tile t
     const char* krow = sv.kbase + static_cast<int64_t>(pick_block(ub.b, key / BS)) * sv.blk_stride + (key % BS) * (D * E);
 #pragma unroll
-    for (int c = 0; c < KL; ++c) R.k[t][c] = *reinterpret_cast<const uint4*>(krow + 64 * c + 16 * kg);
+    for (int c = 0; c < KL; ++c) R.k[t][c] = ld16<NT && KV == kFP8>(krow + 64 * c + 16 * kg);
   }
   const int key0 = 8 * kg;                              // keys 8kg .. 8kg+7: one block, consecutive
   const char* vrow = sv.vbase + static_cast<int64_t>(pick_block(ub.b, key0 / BS)) * sv.blk_stride + (key0 % BS) * E;
 #pragma unroll
-  for (int d = 0; d < D / 16; ++d) load_piece<VW>(R.v[d], vrow + (16 * d + i) * BS * E);
+  for (int d = 0; d < D / 16; ++d) load_piece<VW, NT>(R.v[d], vrow + (16 * d + i) * BS * E);
 }
 
 template <int KV, int D, int G>
@@ -451,6 +482,7 @@ __device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int seq, int kv
   sv.tab = ro(a.tables) + static_cast<int64_t>(seq) * a.max_blocks;
   sv.blk_stride = static_cast<int64_t>(a.num_kv_heads) * TILE;
   sv.nblk = (clamped_len(a, seq) + BS - 1) / BS;
+  sv.shared_units = a.shared_blocks ? (max(ro(a.shared_blocks)[seq], 0) * BS + kUnit - 1) / kUnit : 0;
   return sv;
 }
 
@@ -584,7 +616,10 @@ template <int KV, int D, int BS, int G, typename QArr>
 __device__ __forceinline__ void issue(const DecodeArgs& a, int x, const Pos<BS>& P, UnitRegs<KV, D>& R, QArr& qnext,
                                       int i, int kg) {
   if (P.enter) load_q<KV, D, G>(qnext, a, P.c.seq, x + a.streams * P.c.hh, i, kg);
-  load_unit<KV, D, BS>(R, P.v, P.ub, i, kg);
+  if (P.c.j < P.v.shared_units)
+    load_unit<KV, D, BS, false>(R, P.v, P.ub, i, kg);
+  else
+    load_unit<KV, D, BS, true>(R, P.v, P.ub, i, kg);
   __builtin_amdgcn_sched_barrier(0);
 }
 

@@ -53,6 +53,7 @@ struct DecodeArgs {
   const int32_t* tables;
   int32_t max_blocks;
   const int32_t* lens;
+  const int32_t* shared_blocks;   // optional: leading table entries per sequence that other rows also read
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;

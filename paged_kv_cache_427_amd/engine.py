@@ -24,6 +24,21 @@ def _signed(code: int, bits: int) -> int:
     return code - (1 << bits) if code >= (1 << (bits - 1)) else code
 
 
+def leading_shared_blocks(tables: np.ndarray, lens: np.ndarray, block_size: int) -> np.ndarray:
+    """For each row, how many leading entries of its table (within its length) are physical blocks
+    that another row of the same batch also reads: the pa_decode `shared_blocks` hint."""
+    tables = np.asarray(tables)
+    nblk = -(-np.asarray(lens, np.int64) // block_size)
+    valid = np.arange(tables.shape[1])[None, :] < nblk[:, None]
+    blocks = tables[valid]
+    uniq, counts = np.unique(blocks, return_counts=True)
+    multi = np.zeros(tables.shape, dtype=bool)
+    multi[valid] = counts[np.searchsorted(uniq, blocks)] > 1
+    # length of the leading run of shared entries in each row
+    run = np.where(multi.all(axis=1), tables.shape[1], np.argmin(multi, axis=1))
+    return np.minimum(run, nblk).astype(np.int32)
+
+
 @dataclass
 class StepInputs:
     """Device-resident inputs of one step (everything the timed region needs)."""
@@ -38,6 +53,7 @@ class StepInputs:
     dec_max_len: int = 0
     dec_workspace: Optional[torch.Tensor] = None
     dec_partition: int = 0
+    dec_shared: Optional[torch.Tensor] = None   # int32 [seqs]: leading blocks other rows also read
     pre_tables: Optional[torch.Tensor] = None
     pre_qsl: Optional[torch.Tensor] = None
     pre_prior: Optional[torch.Tensor] = None
@@ -139,8 +155,11 @@ class PagedKVEngine:
             max_len = int(lens.max())
             tabs = [len(self.alloc.table(s)) for s in wl.decode_seqs]
             mb = max(max(tabs), -(-max_len // wl.block_size), 1)
-            si.dec_tables = torch.as_tensor(self.alloc.fill_tables(wl.decode_seqs, mb), device=dev)
+            host_tabs = self.alloc.fill_tables(wl.decode_seqs, mb)
+            si.dec_tables = torch.as_tensor(host_tabs, device=dev)
             si.dec_lens = torch.as_tensor(lens, device=dev)
+            shared = leading_shared_blocks(host_tabs, np.asarray(lens), wl.block_size)
+            si.dec_shared = torch.as_tensor(shared, device=dev) if shared.any() else None
             si.dec_q = wl.q_decode.to(dev)
             si.dec_out = torch.empty_like(si.dec_q)
             si.dec_max_len = max_len
@@ -182,7 +201,8 @@ class PagedKVEngine:
                            si.dec_out if out is None else out, stream)
             return
         pa_decode(si.dec_q, self.k_pool, self.v_pool, self.pool, si.dec_tables, si.dec_lens, self.wl.scale,
-                  si.dec_out if out is None else out, si.dec_max_len, si.dec_partition, si.dec_workspace, stream)
+                  si.dec_out if out is None else out, si.dec_max_len, si.dec_partition, si.dec_workspace, stream,
+                  shared_blocks=si.dec_shared)
 
     def prefill_step(self, si: StepInputs, stream=None) -> None:
         if si.pre_q is None:

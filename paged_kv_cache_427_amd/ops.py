@@ -119,11 +119,21 @@ def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max
     return int(out.value)
 
 
+def _shared(shared_blocks: Optional[torch.Tensor], num_seqs: int):
+    if shared_blocks is None:
+        return None
+    if shared_blocks.dtype != torch.int32 or shared_blocks.numel() < num_seqs:
+        raise TypeError("shared_blocks must be int32 with one entry per sequence")
+    return _dev(shared_blocks, "shared_blocks")
+
+
 def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc,
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, out: torch.Tensor,
               max_context_len: int, partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
-              stream=None) -> None:
-    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over each sequence's paged context."""
+              stream=None, shared_blocks: Optional[torch.Tensor] = None) -> None:
+    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over each sequence's paged context.
+    `shared_blocks` (int32 [num_seqs], optional): leading table entries of each sequence that other
+    sequences of the call also read (a cache-policy hint; engine.leading_shared_blocks computes it)."""
     num_seqs, num_q_heads, head_dim = q.shape
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("block_tables and context_lens must be int32")
@@ -136,13 +146,14 @@ def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool:
                           ctypes.byref(pool), _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
                           _dev(context_lens, "context_lens"), num_seqs, num_q_heads, float(scale),
                           partition_size, int(max_context_len), ws_ptr, ws_bytes, _dev(out, "out"),
-                          pa_dtype(out), _stream(stream)))
+                          pa_dtype(out), _shared(shared_blocks, num_seqs), _stream(stream)))
 
 
 def pa_decode_ex(q_base: torch.Tensor, q_strides, num_seqs: int, num_q_heads: int, k_pool: torch.Tensor,
                  v_pool: torch.Tensor, pool: PoolDesc, tables_ptr: int, max_blocks_per_seq: int,
                  context_lens: torch.Tensor, scale: float, out_base: torch.Tensor, out_strides, max_context_len: int,
-                 lse: Optional[torch.Tensor], workspace: torch.Tensor, partition_size: int = 0, stream=None) -> None:
+                 lse: Optional[torch.Tensor], workspace: torch.Tensor, partition_size: int = 0, stream=None,
+                 shared_blocks: Optional[torch.Tensor] = None) -> None:
     """pa_decode over strided q and out rows (element strides for sequence, KV head, head in the
     group; None = dense) with an optional log-sum-exp output.  `tables_ptr` is a device address
     (a table row stride of max_blocks_per_seq entries may skip rows of a larger table)."""
@@ -156,7 +167,8 @@ def pa_decode_ex(q_base: torch.Tensor, q_strides, num_seqs: int, num_q_heads: in
                              _dev(context_lens, "context_lens"), int(num_seqs), int(num_q_heads), float(scale),
                              int(partition_size), int(max_context_len), _dev(workspace, "workspace"), ws_bytes,
                              _dev(out_base, "out"), pa_dtype(out_base), os_,
-                             None if lse is None else _dev(lse, "lse"), _stream(stream)))
+                             None if lse is None else _dev(lse, "lse"), _shared(shared_blocks, num_seqs),
+                             _stream(stream)))
 
 
 def pa_merge_states(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,

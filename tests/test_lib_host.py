@@ -420,7 +420,7 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation rejects the ca
 ])
 def test_decode_rejects_bad_pools(pool, expect):
     st_ = lib().pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(pool), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16,
-                          None, 0, FAKE, 1, None)
+                          None, 0, FAKE, 1, None, None)
     assert st_ == expect
     assert lib().pa_last_error()
 
@@ -430,26 +430,26 @@ def test_decode_rejects_bad_shapes():
     L = lib()
     # query heads not a multiple of KV heads
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 3, 0.1, 0, 16, None, 0, FAKE, 1,
-                       None) == PA_ERR_INVALID
+                       None, None) == PA_ERR_INVALID
     # group size 16 has no kernel
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 32, 0.1, 0, 16, None, 0, FAKE, 1,
-                       None) == PA_ERR_UNSUPPORTED
+                       None, None) == PA_ERR_UNSUPPORTED
     # table narrower than the longest context
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 1, FAKE, 1, 2, 0.1, 0, 17, None, 0, FAKE, 1,
-                       None) == PA_ERR_INVALID
+                       None, None) == PA_ERR_INVALID
     # workspace needed but missing
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 64, FAKE, 1, 2, 0.1, 512, 1000, None, 0, FAKE,
-                       1, None) == PA_ERR_INVALID
+                       1, None, None) == PA_ERR_INVALID
     # f32 pool with bf16 q
     pf = _pool(dtype=0)
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(pf), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16, None, 0, FAKE, 1,
-                       None) == PA_ERR_UNSUPPORTED
+                       None, None) == PA_ERR_UNSUPPORTED
     # partition not a multiple of 32
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 2, 0.1, 100, 16, None, 0, FAKE, 1,
-                       None) == PA_ERR_INVALID
+                       None, None) == PA_ERR_INVALID
     # null pointers
     assert L.pa_decode(None, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16, None, 0, FAKE, 1,
-                       None) == PA_ERR_INVALID
+                       None, None) == PA_ERR_INVALID
 
 
 def test_cache_write_and_copy_validation():
@@ -495,10 +495,10 @@ def test_decode_ex_merge_layers_swap_reject_bad_arguments():
     p = _pool()
     bad = (ctypes.c_int64 * 3)(6, 2, 1)                 # not multiples of 4 elements
     assert L.pa_decode_ex(FAKE, 1, bad, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16, FAKE,
-                          1 << 30, FAKE, 1, None, None, None) == PA_ERR_INVALID
+                          1 << 30, FAKE, 1, None, None, None, None) == PA_ERR_INVALID
     odd = (ctypes.c_int64 * 3)(256, 4, 4)               # with lse_out, strides must be multiples of head_dim
     assert L.pa_decode_ex(FAKE, 1, None, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16, FAKE,
-                          1 << 30, FAKE, 1, odd, FAKE, None) == PA_ERR_INVALID
+                          1 << 30, FAKE, 1, odd, FAKE, None, None) == PA_ERR_INVALID
     assert L.pa_merge_states(FAKE, FAKE, FAKE, FAKE, 4, 6, FAKE, 1, None, None) == PA_ERR_INVALID   # head_dim % 4
     assert L.pa_merge_states(FAKE, FAKE, FAKE, FAKE, 4, 128, FAKE, 7, None, None) == PA_ERR_INVALID  # dtype
     assert L.pa_merge_states(None, FAKE, FAKE, FAKE, 4, 128, FAKE, 0, None, None) == PA_ERR_INVALID
