@@ -7,15 +7,16 @@
 //
 // Design (HBM-bound: at most 8 flop per byte of K/V, far below the MI355X ridge, so the goal is to
 // keep HBM busy and the vector ALUs out of the way of the loads):
-//  * three launches: a one-workgroup plan kernel (per-sequence unit counts as a prefix sum, the
-//    share schedule and its table of start cursors), the stream kernel, and a merge kernel.
+//  * two launches, the stream kernel and a merge kernel; the stream kernel plans the launch itself
+//    (per-sequence unit counts as a prefix sum in LDS, each wave's start by a binary search), and
+//    only a batch of more than 4096 sequences takes a one-workgroup plan kernel first.
 //  * a unit is 32 keys of one (sequence, KV head) segment, for all G query heads of the group, so
 //    each K/V byte is read once.  The units of all segments form one stream per XCD (KV head h in
 //    stream h % 8; initial dispatch is round-robin over the 8 XCDs), so blocks shared by many
 //    sequences -- a common prefix -- are re-read from that XCD's L2, not from HBM.
-//  * a persistent grid of wave64s (as many as are resident) walks the streams; each wave takes one
-//    contiguous share of its stream, so every wave does the same number of units and the K/V of a
-//    segment is read in order.  The unit's physical blocks come from wave-uniform scalar reads of
+//  * a persistent grid of wave64s (one workgroup of four per CU; three for contexts of at most 64
+//    tokens) walks the streams; each wave takes one contiguous share of its stream, so every wave
+//    does the same number of units and the K/V of a segment is read in order.  The unit's physical blocks come from wave-uniform scalar reads of
 //    the block table: one lookup per block, prepared one unit ahead so they overlap the loads.
 //  * both products of a unit run on 16x16 MFMA tiles fed straight from the loads, no LDS staging:
 //      S^T[key][head] = K[key][:] . Q[head][:]       A = K rows (token-major tile), B = Q^T
@@ -31,8 +32,10 @@
 //  * base-2 online softmax with one running max per head.  The max is raised only when a logit
 //    exceeds it by more than 2^8 (so every exp stays <= 256); that test is one wave-wide ballot, and
 //    only then are the lanes' maxima exchanged and the accumulators rescaled.
-//  * one unit of K/V is in flight per wave while the previous one is consumed, with one workgroup of
-//    four waves per CU (one wave per SIMD).
+//  * one unit of K/V is in flight per wave while the previous one is consumed.  Blocks that no other
+//    sequence of the launch reads (the caller's shared_blocks hint says which are shared) are
+//    streamed with non-temporal loads, V always and K for fp8 pools, so that they do not push the
+//    shared ones out of L2.
 //  * a piece is a wave's run of units inside one partition of one segment.  A piece that is a whole
 //    segment writes the output directly; any other piece writes (max, sum, unnormalised partial
 //    output) to its own slot, and the merge kernel combines the pieces of each (sequence, head).
