@@ -29,6 +29,8 @@ def leading_shared_blocks(tables: np.ndarray, lens: np.ndarray, block_size: int)
     that another row of the same batch also reads: the pa_decode `shared_blocks` hint."""
     tables = np.asarray(tables)
     nblk = -(-np.asarray(lens, np.int64) // block_size)
+    if tables.shape[1] == 0:
+        return np.zeros(len(nblk), dtype=np.int32)
     valid = np.arange(tables.shape[1])[None, :] < nblk[:, None]
     blocks = tables[valid]
     uniq, counts = np.unique(blocks, return_counts=True)

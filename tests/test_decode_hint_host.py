@@ -32,3 +32,8 @@ def test_whole_table_shared():
     tables = np.array([[1, 2], [1, 2]], dtype=np.int32)
     lens = np.array([16, 9], dtype=np.int32)
     assert leading_shared_blocks(tables, lens, b).tolist() == [2, 2]
+
+
+def test_empty_tables():
+    tables = np.zeros((3, 0), dtype=np.int32)
+    assert leading_shared_blocks(tables, np.zeros(3, np.int32), 16).tolist() == [0, 0, 0]
