@@ -361,7 +361,8 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int seq) { retur
 // batch is planned by the one-workgroup plan kernel, which also writes every share's start cursor.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanLds = 8192;        // prefix entries searched in LDS (larger batches search global memory)
-constexpr int kSelfPlanMax = 4096;    // batches the stream kernel plans itself
+constexpr int kSelfPlanMax = 4096;    // batches the stream kernel plans itself (a multiple of its threads)
+static_assert(kSelfPlanMax % kThreads == 0, "a thread's run of sequences has a fixed bound");
 constexpr int kSharesPerWave = 1;
 constexpr int kSchedInts = 64;
 // schedule header: [0] S (units per share), [1] V (shares)
@@ -648,11 +649,17 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
   Sched sc;
   if (self_plan) {
     // spref[s] = units of the sequences before s: a block-wide scan of per-thread runs
+    // (a thread's run is at most kSelfPlanMax / kThreads sequences, loaded all at once)
+    constexpr int kRun = kSelfPlanMax / kThreads;
     const int tid = threadIdx.x;
     const int chunk = (n + kThreads - 1) / kThreads;
     const int s0 = min(tid * chunk, n), s1 = min(s0 + chunk, n);
+    int units[kRun];
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) units[k] = s0 + k < s1 ? (clamped_len(a, s0 + k) + kUnit - 1) / kUnit : 0;
     int local = 0;
-    for (int s = s0; s < s1; ++s) local += (clamped_len(a, s) + kUnit - 1) / kUnit;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) local += units[k];
     scan_s[tid] = local;
     __syncthreads();
     for (int off = 1; off < kThreads; off *= 2) {
@@ -663,9 +670,10 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
     }
     int run = scan_s[tid] - local;
     if (tid == 0) spref[0] = 0;
-    for (int s = s0; s < s1; ++s) {
-      run += (clamped_len(a, s) + kUnit - 1) / kUnit;
-      spref[s + 1] = run;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      run += units[k];
+      if (s0 + k < s1) spref[s0 + k + 1] = run;
     }
     __syncthreads();
     useq = spref[n];
