@@ -78,6 +78,14 @@ def test_decode_lse_and_strided_rows(name):
     bits = torch.int32 if o2.dtype == torch.float32 else torch.int16
     assert torch.equal(o2[::2].view(bits), si.dec_out.view(bits))
     assert torch.all(o2[1::2] == 5.0)
+    # the cache-policy hint (every block marked shared) leaves the strided results' bits unchanged
+    o3 = torch.full_like(q2, 5.0)
+    hint = torch.full((n,), si.dec_tables.shape[1], dtype=torch.int32, device="cuda")
+    pa_decode_ex(q2, strides, n, hq, eng.k_pool, eng.v_pool, eng.pool, si.dec_tables.data_ptr(),
+                 si.dec_tables.shape[1], si.dec_lens, wl.scale, o3, strides, si.dec_max_len, None, si.dec_workspace,
+                 si.dec_partition, shared_blocks=hint)
+    torch.cuda.synchronize()
+    assert torch.equal(o3.view(bits), o2.view(bits))
 
 
 def test_merge_states_against_the_oracle():
