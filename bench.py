@@ -17,11 +17,18 @@ request stream and reports KV utilisation against a max-length reservation.
 Prints one JSON line.  `value` is the decode's unique KV bytes per step (each physical block once)
 divided by the step time, in GB/s.  `roofline` prices the decode launch (stream and merge kernels),
 timed with HIP events on the launch stream, against the 8 TB/s HBM peak.  `cpu_baseline` is the
-fp64 CPU oracle timed on a bounded sample of the same workload on this host's cores.
+fp64 CPU oracle (gather through the block tables, then attention) timed on a bounded sample of the
+same workload on this host's cores, in decode tokens/s per layer like `decode_tokens_per_s_per_layer`.
 
-The default warm-up is 100 untimed steps: the MFMA-bound prefill of the mixed fp8 step runs 12%
-slower in its first ~70 ms of load on MI355X (0.348 ms after 3 warm-up steps, 0.306 ms after 100)
-while the clocks settle; the HBM-bound decode is the same either way.
+The default run adds labelled side legs to the same line: `prefill_roofline`, the chunked prefill of
+the mixed fp8 step (16 chunks of 512 queries over prior contexts of 0..4096 tokens, 32/8 heads, fp8
+K/V) against the 2.5 PFLOP/s bf16 MFMA peak, at block sizes 16 (the figure) and 8 and 32; and
+`decode_roofline_other_workloads`, the decode of the Llama-7B-shaped, GQA long-context and mixed fp8
+workloads against 8 TB/s.  The MFMA-bound prefill runs 12% slower in its first ~70 ms of load on
+MI355X while the clocks settle, so every workload with a prefill is warmed up with at least 150 ms
+of prefill launches after the `--warmup` steps; the HBM-bound decode is the same either way.  After
+timing, a device copy of known size gives the achievable HBM rate (`hbm_achievable`), and the decode
+roofline is also stated as a fraction of it.
 """
 import argparse
 import json
@@ -89,37 +96,83 @@ def prefill_flops(wl) -> float:
     return 4.0 * wl.head_dim * wl.num_q_heads * tot
 
 
-def cpu_baseline(wl, budget_s: float):
-    """fp64 oracle decode on a bounded sample of the workload's sequences (host cores)."""
-    from oracle import ref_decode
-    from oracle.run import logical_view, tensor_bits, act_values, _stored_values
+def host_cores() -> int:
+    """Cores this process may run on (the affinity mask, not the machine's count)."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The fp64 oracle on a bounded sample of the workload's decode sequences, on this host's cores.
+
+    Paged form (the value): the oracle's allocator replays the workload's operations to get every
+    sequence's block table; the sampled sequences' K/V are written into a pool of stored codes
+    (untimed; pool pages no sample touches are never written); the timed part is the oracle's
+    gather through the table, the decoding of the gathered codes and the attention.  Dense form
+    (reported beside it): the same sequences' attention on their logical rows alone."""
+    from oracle import (RefAllocator, decode_pool, gather_seq, pool_shape, ref_cache_write, ref_decode)
+    from oracle.run import logical_view, tensor_bits, act_values, _stored_values
+    cores = host_cores()
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:
-        threads = 1
+        limiter = None
+    alloc = RefAllocator(wl.num_blocks, wl.block_size, wl.free_order)
+    for op in list(wl.history) + list(wl.step):
+        if op[0] == "add":
+            alloc.add_seq(op[1])
+        elif op[0] == "fork":
+            alloc.fork(op[1], op[2])
+        elif op[0] == "free":
+            alloc.free_seq(op[1])
+        elif op[0] == "append":
+            alloc.append(op[1], op[2])
+    code_dt = {"f32": np.uint32, "bf16": np.uint16, "fp8": np.uint8}[wl.kv_dtype]
+    b, hkv, d = wl.block_size, wl.num_kv_heads, wl.head_dim
+    k_codes = np.zeros(pool_shape(wl.num_blocks, hkv, b, d, "k"), dtype=code_dt)   # lazily backed
+    v_codes = np.zeros(pool_shape(wl.num_blocks, hkv, b, d, "v"), dtype=code_dt)
     lg = logical_view(wl)
     order = np.random.default_rng(0).permutation(len(wl.decode_seqs))
-    done_seqs, done_bytes, spent = 0, 0, 0.0
-    row = wl.num_kv_heads * wl.head_dim * elem_bytes(wl.kv_dtype) * 2
+    done, tokens, spent, spent_dense = 0, 0, 0.0, 0.0
     for bi in order:
         sid = wl.decode_seqs[bi]
         L = int(wl.decode_lens[bi])
-        idx = torch.as_tensor(lg.token_rows(sid, L), dtype=torch.long, device=wl.k_tok.device)
-        k = _stored_values(tensor_bits(wl.k_tok.index_select(0, idx)), wl, "k")   # inputs staged untimed
-        v = _stored_values(tensor_bits(wl.v_tok.index_select(0, idx)), wl, "v")
+        table = alloc.table(sid)
+        rows = lg.token_rows(sid, L)
+        idx = torch.as_tensor(rows, dtype=torch.long, device=wl.k_tok.device)
+        kb = tensor_bits(wl.k_tok.index_select(0, idx))
+        vb = tensor_bits(wl.v_tok.index_select(0, idx))
+        slots = [table[p // b] * b + p % b for p in range(L)]
+        ref_cache_write(k_codes, kb, slots, wl.kv_dtype, wl.act_dtype, wl.k_scale)              # untimed
+        ref_cache_write(v_codes, vb, slots, wl.kv_dtype, wl.act_dtype, wl.v_scale, which="v")
         q = act_values(tensor_bits(wl.q_decode[bi:bi + 1]), wl.act_dtype)
         t = time.perf_counter()
+        k = decode_pool(gather_seq(k_codes, table, L).astype(code_dt), wl.kv_dtype, wl.k_scale)
+        v = decode_pool(gather_seq(v_codes, table, L, "v").astype(code_dt), wl.kv_dtype, wl.v_scale)
         ref_decode(q, [(k, v)], wl.scale)
         spent += time.perf_counter() - t
-        done_seqs += 1
-        done_bytes += L * row
-        if spent >= budget_s:
+        kd, vd = _stored_values(kb, wl, "k"), _stored_values(vb, wl, "v")                    # untimed
+        t = time.perf_counter()
+        ref_decode(q, [(kd, vd)], wl.scale)
+        spent_dense += time.perf_counter() - t
+        done += 1
+        tokens += L
+        if spent + spent_dense >= budget_s:
             break
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done_seqs} of {len(wl.decode_seqs)} decode sequences, all {wl.num_q_heads} query heads, "
-                      f"fp64 NumPy, {spent:.1f} s",
-            "decode_tokens_per_s_per_layer": round(done_seqs / spent, 3)}
+    if limiter is not None:
+        limiter.unregister()
+    row = hkv * d * elem_bytes(wl.kv_dtype) * 2
+    return {"value": round(done / spent, 3), "unit": "decode tokens/s per layer", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(wl.decode_seqs)} decode sequences ({tokens} cached tokens), all "
+                      f"{wl.num_q_heads} query heads, fp64 NumPy: gather through the block table, decode of "
+                      f"the stored codes, attention; {spent:.1f} s",
+            "logical_kv_GBps": round(tokens * row / spent / 1e9, 4),
+            "dense": {"value": round(done / spent_dense, 3), "unit": "decode tokens/s per layer",
+                      "note": "the same sequences' attention on their logical rows, no table gather",
+                      "seconds": round(spent_dense, 2)}}
 
 
 def chunk_flops(prior, chunk, head_dim: int, q_heads: int) -> float:
@@ -206,11 +259,12 @@ def prefix_cache_bench(args, dev):
 def prefix_cpu_baseline(b, pc, budget_s: float):
     """fp64 oracle prefill of the cached batch's tails, request by request, on the host cores."""
     from oracle import ref_prefill
+    threads = host_cores()
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads)
     except Exception:
-        threads = 1
+        limiter = None
     done, tokens, spent = 0, 0, 0.0
     for i in range(len(pc.chunk)):
         L = b.prompt_len(i)
@@ -223,6 +277,8 @@ def prefix_cpu_baseline(b, pc, budget_s: float):
         tokens += L
         if spent >= budget_s:
             break
+    if limiter is not None:
+        limiter.unregister()
     return {"value": round(tokens / spent, 2), "unit": "prompt tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} of {len(pc.chunk)} requests' uncached tails, all {b.num_q_heads} query heads, "
                       f"fp64 NumPy, {spent:.1f} s"}
@@ -408,16 +464,33 @@ def serving_bench(args, dev):
 
 
 def copy_probe(args, dev, res) -> None:
-    """After timing, one device copy of a known size: the kernel that calibrates byte counters."""
+    """After timing (outside the timed region): device copies of a known size.  They calibrate the
+    hardware byte counters under rocprofv3, and their rate is the achievable HBM bandwidth that the
+    decode's roofline is also priced against (beside the 8 TB/s data-sheet peak)."""
     if args.copy_probe_gib <= 0:
         return
     n = int(args.copy_probe_gib * 2**30) // 4
     src = torch.ones(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    dst.copy_(src)
-    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
     res["copy_probe_bytes"] = {"read": n * 4, "write": n * 4}
+    gbs = 2 * n * 4 / (float(np.median(times[1:])) * 1e-3) / 1e9
+    res["hbm_achievable"] = {"GBps": round(gbs, 1), "kernel": "device copy (torch copy_), read + write bytes",
+                             "bytes_per_copy": 2 * n * 4, "copies_timed": len(times) - 1}
+    for key in ("roofline",):
+        r = res.get(key)
+        if r and r.get("bound") == "hbm":
+            r["achievable_peak"] = round(gbs, 1)
+            r["frac_of_achievable"] = round(r["achieved"] / gbs, 4)
     del src, dst
 
 
@@ -437,7 +510,9 @@ def main():
                          "the paging indirection is the difference to the default run)")
     ap.add_argument("--plain-decode", action="store_true",
                     help="beam workloads: decode every branch on its own instead of reading shared blocks once")
-    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+    ap.add_argument("--no-legs", action="store_true",
+                    help="default workload only: skip the side legs (mixed fp8 prefill sweep, other decodes)")
+    ap.add_argument("--copy-probe-gib", type=float, default=2.0,
                     help="after timing, run one device copy of this many GiB (a known-size kernel that "
                          "calibrates hardware byte counters)")
     args = ap.parse_args()
@@ -448,8 +523,6 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    from paged_kv_cache_427_amd.engine import PagedKVEngine
-
     dev = torch.device("cuda:0")
     modes = {"prefix_cache_bf16": prefix_cache_bench, "swap_llama7b_bf16": swap_bench,
              "llama7b_32layer_bf16": layers_bench, "serving_llama7b_bf16": serving_bench}
@@ -458,22 +531,41 @@ def main():
         copy_probe(args, dev, res)
         print(json.dumps(res), flush=True)
         return
+    res = step_bench(args, dev, args.config, args.block_size, args.steps, args.warmup, partition=args.partition,
+                     contiguous=args.contiguous_blocks, plain_decode=args.plain_decode,
+                     with_cpu=not args.no_cpu_baseline, prefill_warmup_ms=PREFILL_WARMUP_MS)
+    if args.config == DEFAULT_CONFIG and not args.no_legs:
+        legs(args, dev, res)
+    copy_probe(args, dev, res)
+    print(json.dumps(res), flush=True)
+
+
+DEFAULT_CONFIG = "shared_prefix_bf16"
+# Prefill clocks settle only after ~70 ms of MFMA load; each prefill leg warms up for at least this long.
+PREFILL_WARMUP_MS = 150.0
+
+
+def step_bench(args, dev, config, block_size, steps, warmup, partition=None, contiguous=False,
+               plain_decode=False, with_cpu=False, prefill_warmup_ms=0.0):
+    """Time `steps` whole steps of one workload (copy-on-write copies, cache write, prefill, decode)
+    after `warmup` untimed ones, each launch bracketed by HIP events on the launch stream."""
+    from paged_kv_cache_427_amd.engine import PagedKVEngine
     t_setup = time.time()
-    wl = make_workload(args.config, "full", device=dev, block_size=args.block_size)
-    if args.contiguous_blocks:
+    wl = make_workload(config, "full", device=dev, block_size=block_size)
+    if contiguous:
         wl.free_order = np.arange(wl.num_blocks, dtype=np.int32)
     eng = PagedKVEngine(wl, device=dev, poison=poison_code(wl.kv_dtype))
     eng.build_history()
-    si = eng.prepare_step(args.partition)
-    if wl.beam_width and not args.plain_decode:
+    si = eng.prepare_step(partition)
+    if wl.beam_width and not plain_decode:
         eng.use_cascade(si, wl.beam_width)      # shared blocks read once for all branches of a request
     torch.cuda.synchronize()
-    print(f"[bench] {args.config}: setup {time.time() - t_setup:.1f}s, blocks {wl.num_blocks}, "
+    print(f"[bench] {config} b={wl.block_size}: setup {time.time() - t_setup:.1f}s, blocks {wl.num_blocks}, "
           f"tokens {wl.num_tokens}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
     nev = 5
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
 
     def step(ev=None):
         if ev: ev[0].record(stream)
@@ -486,29 +578,41 @@ def main():
         eng.decode_step(si)
         if ev: ev[4].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
+    if prefill_warmup_ms > 0 and wl.prefill_seqs:
+        # MFMA clocks settle under sustained load: run prefill launches until they add up to at
+        # least prefill_warmup_ms (timed with events, a few launches at a time)
+        spent = 0.0
+        while spent < prefill_warmup_ms:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                eng.prefill_step(si)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            spent += e0.elapsed_time(e1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_step = (t1 - t0) * 1e3 / steps
     parts = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(nev - 1)]
-                      for i in range(args.steps)])
+                      for i in range(steps)])
     ms_copy, ms_write, ms_prefill, ms_decode = parts.mean(axis=0)
 
     res = {"metric": "paged decode KV-read GB/s (% of MI355X HBM peak); decode tokens/s per layer",
-           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
            "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": {"bf16": "bf16", "f32": "f32", "fp8": "fp8_e4m3 KV, bf16 q"}[wl.kv_dtype],
            "data": "synthetic (seeded N(0,1) K/V/Q, lengths and block order as in the workload)"}
-    cfg = {"workload": args.config, "num_seqs": len(wl.decode_seqs) or len(wl.prefill_seqs),
+    cfg = {"workload": config, "num_seqs": len(wl.decode_seqs) or len(wl.prefill_seqs),
            "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
            "block_size": wl.block_size, "pool_blocks": wl.num_blocks, "kv_dtype": wl.kv_dtype,
            "partition": si.dec_partition or 0,
-           "block_order": "ascending" if args.contiguous_blocks else "shuffled"}
+           "block_order": "ascending" if contiguous else "shuffled"}
     tab = si.dec_tables.cpu().numpy() if si.dec_tables is not None else None
     if tab is not None:
         uniq, logical, other = decode_bytes(wl, tab)
@@ -517,7 +621,10 @@ def main():
         achieved = (uniq + other) / (ms_decode * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": measured_traffic(args.config, args.block_size),
+                           "traffic": measured_traffic(config, block_size),
+                           "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of this decode source, scaled by "
+                                             "a device copy of known size, read from the committed profile "
+                                             "(null when the source changed since)",
                            "kernel": ("beam decode: pa_decode_ex over shared blocks + over private tails + "
                                       "pa_merge_states" if getattr(si, "cascade", None) is not None else
                                       "pa_decode (stream + merge kernels)"),
@@ -530,6 +637,7 @@ def main():
         fl = prefill_flops(wl)
         res["prefill_tflops"] = round(fl / (ms_prefill * 1e-3) / 1e12, 1)
         res["prefill_mfma_frac"] = round(fl / (ms_prefill * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+        res["prefill_flops_per_launch"] = fl
     if len(si.host_cow):
         # copy-on-write copies: each pair reads and writes one whole block, K and V, all KV heads
         blk = 2 * wl.num_kv_heads * wl.block_size * wl.head_dim * elem_bytes(wl.kv_dtype)
@@ -548,11 +656,46 @@ def main():
                                for j, name in ((2, "prefill"), (3, "decode"))
                                if (name == "prefill" and wl.prefill_seqs) or (name == "decode" and wl.decode_seqs)}
     res["config"] = cfg
-    copy_probe(args, dev, res)
-    if not args.no_cpu_baseline and wl.decode_seqs:
+    if with_cpu and wl.decode_seqs:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    del eng, si, wl
+    torch.cuda.empty_cache()
+    return res
+
+
+def legs(args, dev, res) -> None:
+    """Side legs of the default run: the chunked prefill of the mixed fp8 step at each block size
+    (MFMA roofline, with its own warm-up), and the decode roofline of the other decode workloads."""
+    steps = max(5, min(args.steps, 20))
+    sweep = {}
+    for bs in (16, 8, 32):
+        r = step_bench(args, dev, "mixed_fp8", bs, steps, max(args.warmup, 3), prefill_warmup_ms=PREFILL_WARMUP_MS)
+        sweep[bs] = r
+    main_r = sweep[16]
+    achieved = main_r["prefill_tflops"]
+    res["prefill_roofline"] = {
+        "bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": main_r["prefill_mfma_frac"], "traffic": None,
+        "kernel": "pa_prefill_chunk (bf16 MFMA, fp8 K/V widened in LDS)",
+        "algorithmic_flops_per_launch": main_r["prefill_flops_per_launch"],
+        "flops_counted": "4 x head_dim x q_heads x causal query-key pairs (masked pairs not counted)",
+        "ms_per_launch": main_r["kernel_ms"]["prefill"],
+        "ms_spread": main_r["kernel_ms_spread"].get("prefill"),
+        "warmup": f"{max(args.warmup, 3)} steps, then at least {PREFILL_WARMUP_MS:.0f} ms of prefill launches",
+        "config": {"workload": "mixed_fp8", "prefill_seqs": 16, "chunk": 512, "prior": "U{0..4096}",
+                   "q_heads": 32, "kv_heads": 8, "head_dim": 128, "kv_dtype": "fp8_e4m3", "block_size": 16},
+        "block_size_sweep": {str(bs): {"frac": r["prefill_mfma_frac"], "tflops": r["prefill_tflops"],
+                                       "ms": r["kernel_ms"]["prefill"]} for bs, r in sorted(sweep.items())},
+    }
+    dec = {"mixed_fp8": {str(bs): {"frac": r["roofline"]["frac"], "ms": r["kernel_ms"]["decode"]}
+                         for bs, r in sorted(sweep.items())}}
+    for cfg in ("llama7b_bf16", "gqa_long_bf16"):
+        r = step_bench(args, dev, cfg, None, steps, max(args.warmup, 3))
+        dec[cfg] = {"frac": r["roofline"]["frac"], "achieved": r["roofline"]["achieved"],
+                    "ms": r["kernel_ms"]["decode"], "algorithmic_bytes_per_launch":
+                    r["roofline"]["algorithmic_bytes_per_launch"], "partition": r["config"]["partition"]}
+    res["decode_roofline_other_workloads"] = dec
 
 
 if __name__ == "__main__":

@@ -149,12 +149,32 @@ def run_paged(wl, split: Optional[int] = None) -> OracleResult:
 
 # ---- dense (pool-free) reference for sampled outputs -------------------------------------------
 
+def _fp8_stored(vals_f32: np.ndarray, scale: float) -> np.ndarray:
+    """The value an fp8 pool holds for fp32 inputs: decode(quantise(x)) * scale."""
+    return e4m3_decode(e4m3_quantise(vals_f32, scale)) * float(np.float32(scale))
+
+
+_BF16_FP8_TABLES: Dict[float, np.ndarray] = {}
+
+
+def bf16_fp8_table(scale: float) -> np.ndarray:
+    """_fp8_stored evaluated once for each of the 65536 bf16 bit patterns: a bf16 input's stored fp8
+    value depends on its 16 bits alone, so the table gives, by indexing, exactly what the per-element
+    evaluation gives (a pin test compares the two)."""
+    key = float(np.float32(scale))
+    if key not in _BF16_FP8_TABLES:
+        every = bf16_bits_to_f64(np.arange(65536, dtype=np.uint32).astype(np.uint16)).astype(np.float32)
+        _BF16_FP8_TABLES[key] = _fp8_stored(every, scale)
+    return _BF16_FP8_TABLES[key]
+
+
 def _stored_values(rows_bits: np.ndarray, wl, which: str) -> np.ndarray:
     """Values the pool holds for these token rows: the activation value, or its fp8 round trip."""
     if wl.kv_dtype == "fp8":
-        vals = act_values(rows_bits, wl.act_dtype).astype(np.float32)
         scale = wl.k_scale if which == "k" else wl.v_scale
-        return e4m3_decode(e4m3_quantise(vals, scale)) * float(np.float32(scale))
+        if wl.act_dtype == "bf16":
+            return bf16_fp8_table(scale)[np.asarray(rows_bits, dtype=np.uint16)]
+        return _fp8_stored(act_values(rows_bits, wl.act_dtype).astype(np.float32), scale)
     return act_values(rows_bits, wl.act_dtype)
 
 

@@ -114,6 +114,9 @@ def test_mixed_fp8_other_block_sizes(block_size):
     assert np.array_equal(tensor_bits(eng.k_pool), ref.k_pool)
     assert np.array_equal(tensor_bits(eng.v_pool), ref.v_pool)
     assert _out_err(si.dec_out, ref.decode_out) <= TOL["fp8"]
+    err = _out_err(si.pre_out, ref.prefill_out)
+    _say("mixed_fp8 small b", block_size, "prefill max err", err)
+    assert err <= TOL["fp8"]
 
 
 @pytest.mark.parametrize("name", ["shared_prefix_bf16", "mixed_fp8"])
@@ -216,15 +219,21 @@ def test_prefill_variants(kv, hq, hkv, b):
     assert _out_err(si.dec_out, ref.decode_out) <= TOL[kv]
 
 
-# ---- full-size workloads: sampled outputs against the pool-free dense oracle ---------------------
+# ---- full-size workloads against the pool-free dense oracle --------------------------------------
 
-FULL = ["llama7b_bf16", "shared_prefix_bf16", "gqa_long_bf16", "mixed_fp8", "fork_storm_bf16"]
+FULL = [("llama7b_bf16", None), ("shared_prefix_bf16", None), ("gqa_long_bf16", None), ("mixed_fp8", None),
+        ("mixed_fp8", 8), ("mixed_fp8", 32), ("fork_storm_bf16", None)]
+# chunk rows at the edges of the prefill's 64-, 128- and 256-row query tiles
+EDGE_ROWS = (0, 63, 64, 127, 128, 255, 256, 511)
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
-    wl = make_workload(name, "full", device="cuda")
-    _say(name, "full: blocks", wl.num_blocks, "tokens", wl.num_tokens)
+@pytest.mark.parametrize("name,block_size", FULL)
+def test_full_size(name, block_size):
+    """Full-size step: every (sequence, query head) decode row against the dense oracle; the prefill
+    rows at query-tile edges of every sequence, for every head of the first and the last KV group;
+    copy-on-write copies and sampled slots byte for byte."""
+    wl = make_workload(name, "full", device="cuda", block_size=block_size)
+    _say(name, "b", wl.block_size, "full: blocks", wl.num_blocks, "tokens", wl.num_tokens)
     eng = _engine()(wl, poison=poison_code(wl.kv_dtype))
     eng.build_history()
     si = eng.prepare_step()
@@ -238,15 +247,13 @@ def test_full_size_sampled(name):
     rng = np.random.default_rng(5)
     tol = TOL[wl.kv_dtype]
     if wl.decode_seqs:
-        lens = np.asarray(wl.decode_lens)
-        picks = sorted(set([int(np.argmax(lens)), int(np.argmin(lens))] +
-                           rng.choice(len(lens), 4, replace=False).tolist()))
+        heads = list(range(wl.num_q_heads))
+        got_all = si.dec_out.float().cpu().numpy().astype(np.float64)
         worst = 0.0
-        for bi in picks:
-            heads = sorted(set([0, wl.num_q_heads - 1] + rng.choice(wl.num_q_heads, 2, replace=False).tolist()))
+        for bi in range(len(wl.decode_seqs)):
             want = dense_decode(wl, bi, heads, lg)
-            worst = max(worst, _out_err(si.dec_out[bi, heads], want))
-        _say(name, "decode sampled max err", worst)
+            worst = max(worst, float(np.max(np.abs(got_all[bi] - want))))
+        _say(name, "decode, all", len(wl.decode_seqs), "x", wl.num_q_heads, "rows: max err", worst)
         assert worst <= tol
     if len(si.host_cow):
         # every copy holds its source block's rows below the new token; sources the step did not
@@ -281,13 +288,15 @@ def test_full_size_sampled(name):
         assert np.array_equal(got_v, row_v)
     if wl.prefill_seqs:
         worst = 0.0
+        g = wl.group
+        heads = list(range(g)) + list(range(wl.num_q_heads - g, wl.num_q_heads))
         starts = np.concatenate([[0], np.cumsum(wl.prefill_chunk)])
-        for si_ in rng.choice(len(wl.prefill_seqs), 3, replace=False):
-            c = int(wl.prefill_chunk[si_])
-            rows = sorted(set([0, c - 1] + rng.choice(c, 2, replace=False).tolist()))
-            heads = [0, 5, wl.num_q_heads - 1]
-            want = dense_prefill(wl, int(si_), rows, heads, lg)
-            got = si.pre_out[int(starts[si_]) + np.asarray(rows)][:, heads]
-            worst = max(worst, _out_err(got, want))
-        _say(name, "prefill sampled max err", worst)
+        pre = si.pre_out.float().cpu().numpy().astype(np.float64)
+        for s_ in range(len(wl.prefill_seqs)):
+            c = int(wl.prefill_chunk[s_])
+            rows = sorted(set([r for r in EDGE_ROWS if r < c] + [c - 1]))
+            want = dense_prefill(wl, s_, rows, heads, lg)
+            got = pre[int(starts[s_]) + np.asarray(rows)][:, heads]
+            worst = max(worst, float(np.max(np.abs(got - want))))
+        _say(name, "prefill, tile-edge rows of all", len(wl.prefill_seqs), "sequences: max err", worst)
         assert worst <= tol

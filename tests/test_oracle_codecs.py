@@ -89,3 +89,17 @@ def test_bf16_and_f32_bits_match_torch():
     assert np.array_equal(bf16_bits_to_f64(bits), xb.to(torch.float64).numpy())
     fbits = x.view(torch.int32).numpy().view(np.uint32)
     assert np.array_equal(f32_bits_to_f64(fbits), x.to(torch.float64).numpy())
+
+
+def test_bf16_fp8_table_equals_elementwise_round_trip():
+    """The memoised table of stored fp8 values (one entry per bf16 bit pattern) equals quantise then
+    decode evaluated element by element, for every pattern, NaN positions included."""
+    from oracle.run import bf16_fp8_table
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = bf16_bits_to_f64(bits).astype(np.float32)
+    for s in (0.0103, 1.0, float(np.float32(4.7 / 448.0))):
+        want = e4m3_decode(e4m3_quantise(x, s)) * float(np.float32(s))
+        got = bf16_fp8_table(s)[bits]
+        assert np.array_equal(np.isnan(got), np.isnan(want))
+        ok = ~np.isnan(want)
+        assert np.array_equal(got[ok], want[ok])
