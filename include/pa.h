@@ -77,7 +77,7 @@ typedef void* pa_stream; /* hipStream_t */
 const char* pa_status_str(int32_t status);
 /* Detail of the last failure on this thread (static thread-local buffer; "" after success). */
 const char* pa_last_error(void);
-/* ABI version: (major << 16) | minor. */
+/* ABI version: (major << 16) | minor (2.0: pa_decode without the cache hint). */
 int32_t pa_version(void);
 
 /* ---------------------------------------------------------------------------------------------
@@ -180,22 +180,17 @@ pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_
  *                 entry does not matter.  Calls that share a workspace must not overlap.
  *   out           device [num_seqs][num_q_heads][head_dim] of out_dtype (PA_F32 or PA_BF16;
  *                 bf16 rounds to nearest-even from the fp32 accumulator)
- *   shared_blocks optional device int32 [num_seqs]: how many leading entries of each sequence's
- *                 table other sequences of the call also read (a shared prefix, [day28] §六 question
- *                 2).  Only the cache policy depends on it, never the results: K/V of those blocks
- *                 are read through the caches so that their repeats hit; every other block is
- *                 streamed with non-temporal loads (read once, kept out of the way of the shared
- *                 ones): its V, and for fp8 pools its K too.  NULL: no block is shared.
+ * q must start at a 16-byte boundary and out at a boundary of 4 elements (rows are read in 16-byte
+ * pieces and written 4 elements at a time).
  * Combinations: pool PA_F32 needs q PA_F32; pools PA_BF16 / PA_FP8_E4M3 need q PA_BF16.
  * Results are deterministic: the pieces and every reduction order depend only on the sizes and
- * lengths.
+ * lengths.  The cache-policy hint of a shared prefix is an argument of pa_decode_ex.
  * ------------------------------------------------------------------------------------------- */
 pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
                     const pa_pool_desc* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                     int32_t partition_size, int32_t max_context_len, void* workspace,
-                    size_t workspace_bytes, void* out, int32_t out_dtype, const int32_t* shared_blocks,
-                    pa_stream stream);
+                    size_t workspace_bytes, void* out, int32_t out_dtype, pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
  * pa_prefill_chunk -- causal attention of a chunk of new query tokens per sequence over the
@@ -227,12 +222,20 @@ pa_status pa_prefill_chunk(const void* q, int32_t q_dtype, const void* k_pool, c
  *
  *   q_strides, out_strides  NULL (dense [num_seqs][num_q_heads][head_dim]) or host int64 [3]:
  *                 element strides for (sequence, KV head, head within the KV head's group); the
- *                 head_dim elements of a row are contiguous.  Multiples of 4; with lse_out also
- *                 multiples of head_dim.
+ *                 head_dim elements of a row are contiguous.  q strides are multiples of 16 bytes
+ *                 (4 f32 or 8 bf16 elements), out strides multiples of 4 elements; with lse_out, out
+ *                 strides are also multiples of head_dim.  Base pointers as for pa_decode.
  *   lse_out       NULL or device float: ln(sum_j exp(scale * q . k_j)) of each (sequence, head) row
  *                 (k_j with k_scale applied), at the row's out offset divided by head_dim; -inf
  *                 for L_s == 0.
- * Everything else as pa_decode; pa_decode is pa_decode_ex with NULL strides and lse_out.
+ *   shared_blocks NULL or device int32 [num_seqs]: how many leading entries of each sequence's
+ *                 table other sequences of the call also read (a shared prefix, [day28] §六 question
+ *                 2).  Only the cache policy depends on it, never the results: K/V of those blocks
+ *                 are read through the caches so that their repeats hit; every other block is
+ *                 streamed with non-temporal loads (read once, kept out of the way of the shared
+ *                 ones): its V, and for fp8 pools its K too.  NULL: no block is shared.
+ * Everything else as pa_decode; pa_decode is pa_decode_ex with NULL strides, lse_out and
+ * shared_blocks.
  * ------------------------------------------------------------------------------------------- */
 pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides, const void* k_pool,
                        const void* v_pool, const pa_pool_desc* pool, const int32_t* block_tables,

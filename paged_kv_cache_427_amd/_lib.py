@@ -52,7 +52,7 @@ _PROTOS = {
     "pa_decode_workspace_size": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_size_t)]),
     "pa_decode": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_int32,
                             c_void_p, c_int32, c_int32, c_float, c_int32, c_int32, c_void_p, c_size_t,
-                            c_void_p, c_int32, c_void_p, c_void_p]),
+                            c_void_p, c_int32, c_void_p]),
     "pa_prefill_chunk": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p,
                                    c_int32, c_void_p, c_void_p, c_int32, c_int32, c_float, c_int32,
                                    c_void_p, c_int32, c_void_p]),

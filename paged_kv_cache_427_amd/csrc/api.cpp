@@ -97,7 +97,7 @@ const char* pa_status_str(int32_t s) {
 
 const char* pa_last_error(void) { return g_err; }
 
-int32_t pa_version(void) { return (1 << 16) | 0; }
+int32_t pa_version(void) { return (2 << 16) | 0; }
 
 pa_status pa_cache_write(const void* k, const void* v, int32_t in_dtype, int64_t num_tokens,
                          const int64_t* slots, void* k_pool, void* v_pool, const pa_pool_desc* pool,
@@ -264,11 +264,10 @@ pa_status pa_decode(const void* q, int32_t q_dtype, const void* k_pool, const vo
                     const pa_pool_desc* pool, const int32_t* tables, int32_t max_blocks,
                     const int32_t* lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                     int32_t partition_size, int32_t max_context_len, void* workspace,
-                    size_t workspace_bytes, void* out, int32_t out_dtype, const int32_t* shared_blocks,
-                    pa_stream stream) {
+                    size_t workspace_bytes, void* out, int32_t out_dtype, pa_stream stream) {
   return pa_decode_ex(q, q_dtype, nullptr, k_pool, v_pool, pool, tables, max_blocks, lens, num_seqs, num_q_heads,
                       scale, partition_size, max_context_len, workspace, workspace_bytes, out, out_dtype, nullptr,
-                      nullptr, shared_blocks, stream);
+                      nullptr, nullptr, stream);
 }
 
 pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides, const void* k_pool,
@@ -337,15 +336,23 @@ pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides,
   const int64_t dense[3] = {static_cast<int64_t>(num_q_heads) * D, G * D, D};
   const int64_t* qs = q_strides ? q_strides : dense;
   const int64_t* os = out_strides ? out_strides : dense;
+  // q rows are read in 16-byte pieces (4 f32 or 8 bf16 elements); out rows are written 4 elements
+  // at a time (16 bytes of f32, 8 of bf16)
+  const int64_t q_step = 16 / elem_bytes(q_dtype);
   for (int k = 0; k < 3; ++k) {
     if (qs[k] < 0 || os[k] < 0)
       return pa_fail(PA_ERR_INVALID, "pa_decode_ex: negative stride");
-    // rows are read and written in 16-byte pieces
-    if (qs[k] % 4 != 0 || os[k] % 4 != 0)
-      return pa_fail(PA_ERR_INVALID, "pa_decode_ex: strides must be multiples of 4 elements");
+    if (qs[k] % q_step != 0)
+      return pa_fail(PA_ERR_INVALID, "pa_decode_ex: q strides must be multiples of 16 bytes (8 bf16 / 4 f32 elements)");
+    if (os[k] % 4 != 0)
+      return pa_fail(PA_ERR_INVALID, "pa_decode_ex: out strides must be multiples of 4 elements");
     if (lse_out && os[k] % D != 0)
       return pa_fail(PA_ERR_INVALID, "pa_decode_ex: with lse_out, out strides must be multiples of head_dim");
   }
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode: q must start at a 16-byte boundary");
+  if (reinterpret_cast<uintptr_t>(out) % (4 * elem_bytes(out_dtype)) != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode: out must start at a boundary of 4 elements");
   a.q_sseq = qs[0];
   a.q_skv = qs[1];
   a.q_sg = qs[2];

@@ -133,7 +133,8 @@ def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool:
               stream=None, shared_blocks: Optional[torch.Tensor] = None) -> None:
     """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over each sequence's paged context.
     `shared_blocks` (int32 [num_seqs], optional): leading table entries of each sequence that other
-    sequences of the call also read (a cache-policy hint; engine.leading_shared_blocks computes it)."""
+    sequences of the call also read (a cache-policy hint of pa_decode_ex; engine.leading_shared_blocks
+    computes it).  Without it the call is pa_decode; with it, pa_decode_ex with dense strides."""
     num_seqs, num_q_heads, head_dim = q.shape
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("block_tables and context_lens must be int32")
@@ -142,11 +143,18 @@ def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    check(lib().pa_decode(_dev(q, "q"), pa_dtype(q), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-                          ctypes.byref(pool), _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
-                          _dev(context_lens, "context_lens"), num_seqs, num_q_heads, float(scale),
-                          partition_size, int(max_context_len), ws_ptr, ws_bytes, _dev(out, "out"),
-                          pa_dtype(out), _shared(shared_blocks, num_seqs), _stream(stream)))
+    if shared_blocks is None:
+        check(lib().pa_decode(_dev(q, "q"), pa_dtype(q), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                              ctypes.byref(pool), _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
+                              _dev(context_lens, "context_lens"), num_seqs, num_q_heads, float(scale),
+                              partition_size, int(max_context_len), ws_ptr, ws_bytes, _dev(out, "out"),
+                              pa_dtype(out), _stream(stream)))
+        return
+    check(lib().pa_decode_ex(_dev(q, "q"), pa_dtype(q), None, _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                             ctypes.byref(pool), _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
+                             _dev(context_lens, "context_lens"), num_seqs, num_q_heads, float(scale),
+                             partition_size, int(max_context_len), ws_ptr, ws_bytes, _dev(out, "out"),
+                             pa_dtype(out), None, None, _shared(shared_blocks, num_seqs), _stream(stream)))
 
 
 def pa_decode_ex(q_base: torch.Tensor, q_strides, num_seqs: int, num_q_heads: int, k_pool: torch.Tensor,

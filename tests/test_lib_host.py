@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lib().pa_version() >> 16 == 1
+    assert lib().pa_version() >> 16 == 2
     assert lib().pa_status_str(PA_ERR_OOM) == b"PA_ERR_OOM"
 
 
@@ -420,7 +420,7 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation rejects the ca
 ])
 def test_decode_rejects_bad_pools(pool, expect):
     st_ = lib().pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(pool), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16,
-                          None, 0, FAKE, 1, None, None)
+                          None, 0, FAKE, 1, None)
     assert st_ == expect
     assert lib().pa_last_error()
 
@@ -430,26 +430,26 @@ def test_decode_rejects_bad_shapes():
     L = lib()
     # query heads not a multiple of KV heads
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 3, 0.1, 0, 16, None, 0, FAKE, 1,
-                       None, None) == PA_ERR_INVALID
+                       None) == PA_ERR_INVALID
     # group size 16 has no kernel
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 32, 0.1, 0, 16, None, 0, FAKE, 1,
-                       None, None) == PA_ERR_UNSUPPORTED
+                       None) == PA_ERR_UNSUPPORTED
     # table narrower than the longest context
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 1, FAKE, 1, 2, 0.1, 0, 17, None, 0, FAKE, 1,
-                       None, None) == PA_ERR_INVALID
+                       None) == PA_ERR_INVALID
     # workspace needed but missing
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 64, FAKE, 1, 2, 0.1, 512, 1000, None, 0, FAKE,
-                       1, None, None) == PA_ERR_INVALID
+                       1, None) == PA_ERR_INVALID
     # f32 pool with bf16 q
     pf = _pool(dtype=0)
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(pf), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16, None, 0, FAKE, 1,
-                       None, None) == PA_ERR_UNSUPPORTED
+                       None) == PA_ERR_UNSUPPORTED
     # partition not a multiple of 32
     assert L.pa_decode(FAKE, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 2, 0.1, 100, 16, None, 0, FAKE, 1,
-                       None, None) == PA_ERR_INVALID
+                       None) == PA_ERR_INVALID
     # null pointers
     assert L.pa_decode(None, 1, FAKE, FAKE, ctypes.byref(p), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16, None, 0, FAKE, 1,
-                       None, None) == PA_ERR_INVALID
+                       None) == PA_ERR_INVALID
 
 
 def test_cache_write_and_copy_validation():
@@ -511,6 +511,31 @@ def test_decode_ex_merge_layers_swap_reject_bad_arguments():
     q = _pool(block_size=32)
     assert L.pa_swap_blocks(FAKE, FAKE, ctypes.byref(p), FAKE, FAKE, ctypes.byref(q), FAKE, 1, None) == PA_ERR_INVALID
     assert L.pa_swap_blocks(FAKE, FAKE, ctypes.byref(p), FAKE, FAKE, ctypes.byref(p), FAKE, 0, None) == 0
+
+
+def test_decode_ex_refuses_misaligned_rows():
+    """q rows are read in 16-byte pieces and out rows written 4 elements at a time: bf16 q strides must
+    be multiples of 8 elements, f32 q strides of 4, out strides of 4; q must start at a 16-byte
+    boundary and out at a boundary of 4 elements."""
+    L = lib()
+    p = _pool()
+    ws = 1 << 30
+
+    def call(q=FAKE, q_dtype=1, qs=None, out=FAKE, out_dtype=1, os_=None, pool=p):
+        qs_ = None if qs is None else (ctypes.c_int64 * 3)(*qs)
+        os2 = None if os_ is None else (ctypes.c_int64 * 3)(*os_)
+        return L.pa_decode_ex(q, q_dtype, qs_, FAKE, FAKE, ctypes.byref(pool), FAKE, 8, FAKE, 1, 2, 0.1, 0, 16,
+                              FAKE, ws, out, out_dtype, os2, None, None, None)
+
+    assert call(qs=(256, 128, 4)) == PA_ERR_INVALID                 # bf16 q: 4 elements = 8 bytes
+    assert call(qs=(256, 128, 12)) == PA_ERR_INVALID
+    assert call(os_=(256, 128, 6)) == PA_ERR_INVALID                # out: 6 elements
+    assert call(q=ctypes.c_void_p(0x1008)) == PA_ERR_INVALID        # q base 8 bytes past 16
+    assert call(out=ctypes.c_void_p(0x1004)) == PA_ERR_INVALID      # bf16 out base: 2 elements
+    assert call(out=ctypes.c_void_p(0x1008), out_dtype=0) == PA_ERR_INVALID   # f32 out base: 2 elements
+    assert "16-byte" in L.pa_last_error().decode() or "4 elements" in L.pa_last_error().decode()
+    pf = _pool(dtype=0)
+    assert call(q_dtype=0, qs=(256, 128, 6), out_dtype=0, pool=pf) == PA_ERR_INVALID   # f32 q: 6 elements
 
 
 def test_plan_shared_blocks():
