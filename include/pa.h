@@ -15,7 +15,9 @@
  *   - Every call returns pa_status; no exception or abort crosses this boundary.  On failure the
  *     text of pa_last_error() (thread-local) says what was wrong.
  *   - Device pointers are caller-owned (typically allocated by PyTorch) and must stay valid until
- *     the work queued on `stream` has finished.  The library never allocates device memory.
+ *     the work queued on `stream` has finished.  The library never allocates device memory; the
+ *     one device array it owns, the static workspace of pa_decode_noalloc, is reserved by the code
+ *     object loader on each GPU the library runs on.
  *   - Host arguments are validated (null pointers, dtypes, shapes, sizes); values that live in
  *     device memory (slots, tables, lengths, copy pairs) are NOT validated: an out-of-range value
  *     there is undefined behaviour (the caller's allocator produces them; see pa_alloc_*).
@@ -77,7 +79,7 @@ typedef void* pa_stream; /* hipStream_t */
 const char* pa_status_str(int32_t status);
 /* Detail of the last failure on this thread (static thread-local buffer; "" after success). */
 const char* pa_last_error(void);
-/* ABI version: (major << 16) | minor (2.0: pa_decode without the cache hint). */
+/* ABI version: (major << 16) | minor (2.0: pa_decode without the cache hint, pa_decode_noalloc). */
 int32_t pa_version(void);
 
 /* ---------------------------------------------------------------------------------------------
@@ -244,6 +246,29 @@ pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides,
                        void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
                        const int64_t* out_strides, float* lse_out, const int32_t* shared_blocks,
                        pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_decode_noalloc -- pa_decode_ex for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Instead of a caller
+ * workspace it uses a static device array that the library holds on each GPU it runs on, of
+ * PA_DECODE_STATIC_WORKSPACE_BYTES (64 MiB), until the process ends.  The call itself allocates
+ * nothing.
+ *   Arguments as pa_decode_ex without workspace and workspace_bytes.  PA_ERR_INVALID (nothing
+ *   launched) when pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+ *   partition_size) exceeds PA_DECODE_STATIC_WORKSPACE_BYTES: with partition_size 0 that holds
+ *   up to about 40 000 (sequence, query head) rows at head_dim 128.
+ * Every call on one GPU shares that GPU's array, and each call rewrites what it uses (nothing in it
+ * needs to start at zero), so calls on one GPU must not overlap: two streams, or two threads,
+ * that decode at the same time race on it.  Results are bit-identical to pa_decode_ex with a
+ * workspace of its own.
+ * ------------------------------------------------------------------------------------------- */
+#define PA_DECODE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+pa_status pa_decode_noalloc(const void* q, int32_t q_dtype, const int64_t* q_strides, const void* k_pool,
+                            const void* v_pool, const pa_pool_desc* pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t num_q_heads, float scale, int32_t partition_size, int32_t max_context_len,
+                            void* out, int32_t out_dtype, const int64_t* out_strides, float* lse_out,
+                            const int32_t* shared_blocks, pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
  * pa_plan_shared_blocks (host) -- for a decode batch laid out as groups of `width` consecutive

@@ -53,6 +53,9 @@ _PROTOS = {
     "pa_decode": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_int32,
                             c_void_p, c_int32, c_int32, c_float, c_int32, c_int32, c_void_p, c_size_t,
                             c_void_p, c_int32, c_void_p]),
+    "pa_decode_noalloc": (c_int32, [c_void_p, c_int32, _I64P, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p,
+                                    c_int32, c_void_p, c_int32, c_int32, c_float, c_int32, c_int32, c_void_p,
+                                    c_int32, _I64P, c_void_p, c_void_p, c_void_p]),
     "pa_prefill_chunk": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p,
                                    c_int32, c_void_p, c_void_p, c_int32, c_int32, c_float, c_int32,
                                    c_void_p, c_int32, c_void_p]),

@@ -365,6 +365,36 @@ pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides,
                        "pa_decode: no kernel for this dtype / head_dim / block_size combination");
 }
 
+pa_status pa_decode_noalloc(const void* q, int32_t q_dtype, const int64_t* q_strides, const void* k_pool,
+                            const void* v_pool, const pa_pool_desc* pool, const int32_t* tables, int32_t max_blocks,
+                            const int32_t* lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                            int32_t partition_size, int32_t max_context_len, void* out, int32_t out_dtype,
+                            const int64_t* out_strides, float* lse_out, const int32_t* shared_blocks,
+                            pa_stream stream) {
+  pa_status st = check_pool(pool, "pa_decode_noalloc");
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads <= 0) return pa_fail(PA_ERR_INVALID, "pa_decode_noalloc: bad num_seqs or num_q_heads");
+  size_t need = 0;
+  st = pa_decode_workspace_size(num_seqs, num_q_heads, pool->head_dim, max_context_len, partition_size, &need);
+  if (st != PA_OK) return st;
+  if (need > PA_DECODE_STATIC_WORKSPACE_BYTES) {
+    static thread_local char msg[256];
+    std::snprintf(msg, sizeof msg,
+                  "pa_decode_noalloc: this call needs %zu bytes of workspace, more than the static %zu; "
+                  "use fewer sequences or partitions, or pa_decode with a workspace",
+                  need, static_cast<size_t>(PA_DECODE_STATIC_WORKSPACE_BYTES));
+    return pa_fail(PA_ERR_INVALID, msg);
+  }
+  if (num_seqs == 0) return pa_ok();
+  size_t cap = 0;
+  void* ws = nullptr;
+  const int rc = pa::decode_static_workspace(&ws, &cap);
+  if (rc != 0) return hip_fail(rc, "pa_decode_noalloc: device address of the static workspace");
+  return pa_decode_ex(q, q_dtype, q_strides, k_pool, v_pool, pool, tables, max_blocks, lens, num_seqs, num_q_heads,
+                      scale, partition_size, max_context_len, ws, cap, out, out_dtype, out_strides, lse_out,
+                      shared_blocks, stream);
+}
+
 pa_status pa_merge_states(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b, int64_t rows,
                           int32_t head_dim, void* out, int32_t out_dtype, float* lse_out, pa_stream stream) {
   if (rows < 0) return pa_fail(PA_ERR_INVALID, "pa_merge_states: negative rows");

@@ -42,6 +42,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -957,6 +959,35 @@ size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t hea
   const int64_t g = num_q_heads < 8 ? num_q_heads : 8;   // G <= 8 and G <= num_q_heads
   const int64_t records = num_q_heads * num_seqs * max_parts + kSharesPerWave * waves * g;
   return static_cast<size_t>(plan + records * (head_dim + 4) * 4);
+}
+
+// The workspace of pa_decode_noalloc: one copy per GPU, reserved by the code object loader when the
+// library is loaded on that GPU and held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: every use goes through the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device current.
+static __device__ __align__(256) char scratch[PA_DECODE_STATIC_WORKSPACE_BYTES];
+
+int decode_static_workspace(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex lock;
+  static void* addr[kMaxDevices] = {};
+  *ptr = nullptr;
+  *bytes = PA_DECODE_STATIC_WORKSPACE_BYTES;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  std::lock_guard<std::mutex> guard(lock);
+  if (dev >= 0 && dev < kMaxDevices && addr[dev]) {
+    *ptr = addr[dev];
+    return 0;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (!p) return static_cast<int>(hipErrorInvalidSymbol);
+  if (dev >= 0 && dev < kMaxDevices) addr[dev] = p;
+  *ptr = p;
+  return 0;
 }
 
 void decode_workspace_carve(DecodeArgs& a, void* workspace) {

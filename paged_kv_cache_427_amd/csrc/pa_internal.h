@@ -89,6 +89,9 @@ size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t hea
 int decode_max_waves();
 // Sets the workspace pointers of `a` (num_seqs set) inside a workspace of decode_workspace_bytes().
 void decode_workspace_carve(DecodeArgs& a, void* workspace);
+// The current device's copy of the library's static decode workspace (PA_DECODE_STATIC_WORKSPACE_BYTES):
+// its device address in *ptr and its size in *bytes.  Returns 0, or the hipError_t of the lookup.
+int decode_static_workspace(void** ptr, size_t* bytes);
 
 struct PrefillArgs {
   const void* q;

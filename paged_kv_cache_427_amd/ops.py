@@ -157,6 +157,23 @@ def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool:
                              pa_dtype(out), None, None, _shared(shared_blocks, num_seqs), _stream(stream)))
 
 
+def pa_decode_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                      max_context_len: int, partition_size: int = 0, stream=None,
+                      shared_blocks: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> None:
+    """pa_decode that allocates nothing: the library's static per-GPU workspace replaces the caller's
+    (calls on one GPU must not overlap).  Dense q and out; optional log-sum-exp output."""
+    num_seqs, num_q_heads, _ = q.shape
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    check(lib().pa_decode_noalloc(_dev(q, "q"), pa_dtype(q), None, _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                  ctypes.byref(pool), _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
+                                  _dev(context_lens, "context_lens"), num_seqs, num_q_heads, float(scale),
+                                  partition_size, int(max_context_len), _dev(out, "out"), pa_dtype(out), None,
+                                  None if lse is None else _dev(lse, "lse"), _shared(shared_blocks, num_seqs),
+                                  _stream(stream)))
+
+
 def pa_decode_ex(q_base: torch.Tensor, q_strides, num_seqs: int, num_q_heads: int, k_pool: torch.Tensor,
                  v_pool: torch.Tensor, pool: PoolDesc, tables_ptr: int, max_blocks_per_seq: int,
                  context_lens: torch.Tensor, scale: float, out_base: torch.Tensor, out_strides, max_context_len: int,

@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _header_functions()
-    assert len(names) == 34
+    assert len(names) == 35
     handle = lib()
     for n in names:
         assert hasattr(handle, n), n
@@ -536,6 +536,25 @@ def test_decode_ex_refuses_misaligned_rows():
     assert "16-byte" in L.pa_last_error().decode() or "4 elements" in L.pa_last_error().decode()
     pf = _pool(dtype=0)
     assert call(q_dtype=0, qs=(256, 128, 6), out_dtype=0, pool=pf) == PA_ERR_INVALID   # f32 q: 6 elements
+
+
+def test_decode_noalloc_refuses_workspace_beyond_static_size():
+    """The static workspace holds PA_DECODE_STATIC_WORKSPACE_BYTES; a call that would need more is refused
+    before anything is launched, and the size check agrees with pa_decode_workspace_size."""
+    L = lib()
+    p = _pool(num_kv_heads=8)
+    cap = 64 << 20
+    n = ctypes.c_size_t()
+    # 4096 sequences x 32 heads x 16 partitions of 512 tokens: far more than 64 MiB
+    assert L.pa_decode_workspace_size(4096, 32, 128, 8192, 512, ctypes.byref(n)) == 0 and n.value > cap
+    st_ = L.pa_decode_noalloc(FAKE, 1, None, FAKE, FAKE, ctypes.byref(p), FAKE, 512, FAKE, 4096, 32, 0.1, 512, 8192,
+                              FAKE, 1, None, None, None, None)
+    assert st_ == PA_ERR_INVALID
+    assert "static" in L.pa_last_error().decode()
+    # the same shape without partitions fits; zero sequences is a no-op that touches no device
+    assert L.pa_decode_workspace_size(64, 32, 128, 2048, 0, ctypes.byref(n)) == 0 and n.value <= cap
+    assert L.pa_decode_noalloc(FAKE, 1, None, FAKE, FAKE, ctypes.byref(p), FAKE, 512, FAKE, 0, 32, 0.1, 0, 8192,
+                               FAKE, 1, None, None, None, None) == 0
 
 
 def test_plan_shared_blocks():
