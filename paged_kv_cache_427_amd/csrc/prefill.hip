@@ -59,10 +59,15 @@ constexpr int kKBytes = kKT * kKStride;
 constexpr int kVBytes = kD * kVStride;
 constexpr float kRescaleSlack = 8.0f;    // log2 of the largest unrescaled growth
 constexpr int kMaxRanked = 64;           // sequences ordered by length when there are at most this many
+constexpr int kMaxLdsTable = 16384;      // table entries the pipelined kernel holds in LDS (64 KiB)
 
 // Inside each 16-key group of a V^T row, key k sits at LDS position k with bits 2 and 3 swapped:
 // keys 0-3, 8-11 | 4-7, 12-15.  The P^T operand of lane half h holds keys 4h..4h+3 and 8+4h..8+4h+3
 // of the group (the S^T accumulator layout), which are then the 8 contiguous positions 8h..8h+7.
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
+}
 
 __device__ __forceinline__ uint32_t fp8x2_lo(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
@@ -153,6 +158,73 @@ struct TileLoader {
     }
   }
 
+  // The loads above, split in two: fetch_*() reads the tile's physical block ids from a table (for
+  // the pipelined kernel, its copy in LDS), load_*_fetched() issues the loads at those blocks.  A
+  // caller fetches a few instructions before loading, so that the loads never wait on the table.
+  static constexpr int kVB = BS >= 16 ? 1 : 2;          // blocks one 16-key V piece spans
+  int pk[kKU];
+  int pvb[kVU][kVB];
+  __device__ __forceinline__ void fetch_k(const int32_t* tab, int key0, int n_keys, int wave) {
+    const int jlast = (n_keys - 1) / BS;
+#pragma unroll
+    for (int u = 0; u < kKU; ++u) {
+      const int kw = key0 + (u * kThreads + 64 * wave) / kCPR;
+      pk[u] = tab[min(kw / BS, jlast)];
+    }
+  }
+  __device__ __forceinline__ void fetch_v(const int32_t* tab, int key0, int n_keys, int wave) {
+    const int jlast = (n_keys - 1) / BS;
+#pragma unroll
+    for (int u = 0; u < kVU; ++u) {
+      const int kg = key0 + 16 * ((W / 2) * u + (wave >> 1));
+#pragma unroll
+      for (int hb = 0; hb < kVB; ++hb) pvb[u][hb] = tab[min(kg / BS + hb, jlast)];
+    }
+  }
+  __device__ __forceinline__ void load_k_fetched(const char* kpool, int64_t blk_stride, int64_t head_off, int key0,
+                                                 int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < kKU; ++u) {
+      const int key = key0 + (u * kThreads + 64 * wave + lane) / kCPR;
+      const int ch = lane % kCPR;
+      const int64_t phys = __builtin_amdgcn_readfirstlane(pk[u]);
+      k[u] = *reinterpret_cast<const u32x4*>(kpool + phys * blk_stride + head_off +
+                                             static_cast<int64_t>(key % BS) * kRowBytes + ch * 16);
+    }
+  }
+  __device__ __forceinline__ void load_v_fetched(const char* vpool, int64_t blk_stride, int64_t head_off, int key0,
+                                                 int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < kVU; ++u) {
+      const int g16 = (W / 2) * u + (wave >> 1);
+      const int dim = 64 * (wave & 1) + lane;
+      const int kg = key0 + 16 * g16;
+      if constexpr (BS >= 16) {
+        const int64_t phys = __builtin_amdgcn_readfirstlane(pvb[u][0]);
+        const char* row = vpool + phys * blk_stride + head_off + static_cast<int64_t>(dim) * BS * kE +
+                          (kg % BS) * kE;
+#pragma unroll
+        for (int j = 0; j < kVW / 4; ++j) {
+          const uint4 w = reinterpret_cast<const uint4*>(row)[j];
+          v[u][4 * j] = w.x; v[u][4 * j + 1] = w.y; v[u][4 * j + 2] = w.z; v[u][4 * j + 3] = w.w;
+        }
+      } else {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int64_t phys = __builtin_amdgcn_readfirstlane(pvb[u][hb]);
+          const char* row = vpool + phys * blk_stride + head_off + static_cast<int64_t>(dim) * 8 * kE;
+          if constexpr (kE == 1) {
+            const uint2 w = *reinterpret_cast<const uint2*>(row);
+            v[u][2 * hb] = w.x; v[u][2 * hb + 1] = w.y;
+          } else {
+            const uint4 w = *reinterpret_cast<const uint4*>(row);
+            v[u][4 * hb] = w.x; v[u][4 * hb + 1] = w.y; v[u][4 * hb + 2] = w.z; v[u][4 * hb + 3] = w.w;
+          }
+        }
+      }
+    }
+  }
+
   // K rows widened to bf16, [key][dim] with stride kKStride.
   __device__ __forceinline__ void store_k(char* ks, int wave, int lane) const {
 #pragma unroll
@@ -170,6 +242,26 @@ struct TileLoader {
             make_uint4(fp8x2_lo(c.z), fp8x2_hi(c.z), fp8x2_lo(c.w), fp8x2_hi(c.w));
       }
     }
+  }
+
+  // store_v() with the masking of keys >= n_keys done by a scalar-computed mask per dword instead
+  // of a branch (keys below n_keys keep every bit), so that a caller's instruction schedule is one
+  // basic block.
+  __device__ __forceinline__ void store_v_masked(char* vt, int key0, int n_keys, int wave, int lane) {
+    constexpr int kPer = 4 / kE;   // elements per dword: fp8 4, bf16 2
+#pragma unroll
+    for (int u = 0; u < kVU; ++u) {
+      const int g16 = (W / 2) * u + (wave >> 1);
+      // keys of the group below n_keys (wave-uniform: the masks are computed on the scalar unit)
+      const int valid = __builtin_amdgcn_readfirstlane(n_keys - (key0 + 16 * g16));
+#pragma unroll
+      for (int m = 0; m < kVW; ++m) {
+        const int nv = min(max(valid - kPer * m, 0), kPer);
+        const uint32_t keep = nv >= kPer ? 0xffffffffu : ((1u << (8 * kE * nv)) - 1u);
+        v[u][m] &= keep;
+      }
+    }
+    store_v(vt, 0, 1 << 30, wave, lane);
   }
 
   // V^T rows widened to bf16, [dim][key position] with stride kVStride.  Values of keys >= n_keys
@@ -436,6 +528,329 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) prefill_kernel(Prefill
     }
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// a + b + c of a packed bf16 pair and an fp32 sum (one v_dot2c against (1, 1))
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+}
+
+// The 8-wave kernel as one balanced software pipeline.  Step t of a workgroup issues 32 MFMAs, each
+// in a chunk of its own: even chunks the products O^T += V^T(t - 1) P^T(t - 1) (the probabilities
+// of the previous tile), odd chunks S^T(t + 1) = K(t + 1) Q^T (the scores of the next one).  Beside
+// each MFMA a wave computes one probability of tile t (an fma and an exp2; every second one also
+// packs the pair to bf16 and adds it to the row sum with a bf16 dot), so that every MFMA of a wave
+// has about as much vector work beside it as the MFMA itself takes (MI355X issues 32 x 32 x 16 bf16
+// MFMAs every 32 cycles per SIMD; an exp2 takes 8 cycles of the vector unit, an fma 2).  LDS
+// fragments are read kAhead chunks before their MFMA; the tile loads and LDS stores sit in the
+// first chunks; one barrier ends the step.
+//
+// Probabilities are exp2(c2 s - m) against the row's reference max m, with no per-tile max: a lane
+// whose 32 probabilities of the tile sum above 2^8 (so one may exceed 2^8), or to NaN, sends its wave
+// to a rare path that takes the tile's true row max, rescales O and the sums to it and recomputes the
+// tile.  The row sum adds the bf16-rounded probabilities that the P.V product uses.
+template <int KV, int BS, int G, int W>
+__global__ void __launch_bounds__(64 * W, 1) prefill_pipe_kernel(PrefillArgs a, int out_bf16, int num_qtiles,
+                                                                 int xcd_remap) {
+  constexpr int kRows = 32 * W;      // (query, head) rows per workgroup
+  constexpr int QT = kRows / G;      // queries per workgroup
+  constexpr int kAhead = 3;          // chunks between an LDS fragment read and its MFMA
+  constexpr float kSumBound = 256.f;
+  __shared__ __attribute__((aligned(16))) char smem[2 * (kKBytes + kVBytes)];
+  extern __shared__ int32_t tab_s[];   // the sequence's block-table row (dynamic, max_blocks entries)
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  int rank, kvh, qt;
+  if (xcd_remap) {
+    const int x = blockIdx.x % 8;
+    const int j = blockIdx.x / 8;
+    qt = num_qtiles - 1 - j % num_qtiles;
+    const int rr = j / num_qtiles;
+    const int hpx = a.num_kv_heads / 8;
+    rank = rr / hpx;
+    kvh = (rr % hpx) * 8 + x;
+  } else {
+    qt = num_qtiles - 1 - blockIdx.x % num_qtiles;
+    const int rr = blockIdx.x / num_qtiles;
+    rank = rr / a.num_kv_heads;
+    kvh = rr % a.num_kv_heads;
+  }
+  if (rank >= a.num_seqs) return;
+  const int seq = a.num_seqs <= kMaxRanked ? seq_of_rank(a, rank, lane) : rank;
+  const int q_base = a.qsl[seq];
+  const int C = a.qsl[seq + 1] - q_base;
+  const int q0 = qt * QT;
+  if (q0 >= C) return;
+  const int P = a.prior[seq];
+  const int q_end = min(q0 + QT, C);
+  const int n_keys = P + q_end;
+  const int n_tiles = (n_keys + kKT - 1) / kKT;
+
+  const int h = lane >> 5;
+  const int row = wave * 32 + (lane & 31);
+  const int g = row / QT;
+  const int qi = q0 + row % QT;
+  const bool row_ok = qi < C;
+  const int qpos = P + qi;
+  const int head = kvh * G + g;
+
+  bf16x8 qb[8];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<int64_t>(q_base + qi) * a.num_q_heads + head) * kD;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint4 w = row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * c + 8 * h) : make_uint4(0, 0, 0, 0);
+      qb[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  const char* kpool = static_cast<const char*>(a.k_pool);
+  const char* vpool = static_cast<const char*>(a.v_pool);
+  constexpr int kTile = BS * TileLoader<KV, BS, W>::kRowBytes;
+  const int64_t head_off = static_cast<int64_t>(kvh) * kTile;
+  const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * kTile;
+  {
+    // the table entries of this workgroup's keys, into LDS (ready after the prologue's first barrier)
+    const int32_t* tab_g = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+    const int nblk = min((n_keys + BS - 1) / BS, a.max_blocks);
+    for (int i = threadIdx.x; i < nblk; i += 64 * W) tab_s[i] = tab_g[i];
+  }
+  const int32_t* const tab = tab_s;
+
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m_run = -INFINITY;   // reference max (base-2 logits) of this row
+  float l_lane = 0.f;        // this lane's share of the row's probability sum (its half of the keys)
+  const float c2 = a.qk_scale;
+
+  char* const kbuf0 = smem;
+  char* const kbuf1 = smem + kKBytes;
+  char* const vbuf0 = smem + 2 * kKBytes;
+  char* const vbuf1 = smem + 2 * kKBytes + kVBytes;
+  const int last = n_tiles - 1;
+  TileLoader<KV, BS, W> ld;
+
+  // One step; on entry: sc = S(t); pp = P(t - 1) (bf16 pairs); LDS holds K(t + 1) and V(t - 1);
+  // the register stage holds K(t + 2) and V(t).
+  // One step; on entry: sc = S(t); pp = P(t - 1) (bf16 pairs); LDS holds K(t + 1) and V(t - 1);
+  // the register stage holds K(t + 2) and V(t).
+  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], uint32_t (&pp)[4][4], uint32_t (&pn)[4][4])
+      __attribute__((always_inline)) {
+    const bool odd = t & 1;
+    const char* const kread = odd ? kbuf0 : kbuf1;     // K(t + 1)
+    const char* const vread = odd ? vbuf0 : vbuf1;     // V(t - 1)
+    char* const kwrite = odd ? kbuf1 : kbuf0;          // K(t + 2) replaces K(t)
+    char* const vwrite = odd ? vbuf1 : vbuf0;          // V(t) replaces V(t - 2)
+    const int key_base = t * kKT;
+    if (key_base + kKT - 1 > P + q0) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key_base + sb * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+          sc[sb][r] = key <= qpos ? sc[sb][r] : -INFINITY;
+        }
+    }
+    const float nm = -m_run;
+    float lsum2[2] = {0.f, 0.f};   // two accumulators halve the dependent chain of row-sum dots
+    bf16x8 frag[32];
+    // MFMA order: even chunks the O products (dt, c) with dt fastest, odd chunks the S products
+    // (sb, c) with sb fastest, so an accumulator recurs only every 8 (O) or 4 (S) chunks
+    auto read_frag = [&](int i) __attribute__((always_inline)) {
+      const int k = i >> 1;
+      const char* src = (i & 1) ? kread + ((k & 1) * 32 + (lane & 31)) * kKStride + 16 * h + 32 * (k >> 1)
+                                : vread + ((k & 3) * 32 + (lane & 31)) * kVStride + 16 * h + 32 * (k >> 2);
+      frag[i] = *reinterpret_cast<const bf16x8*>(src);
+    };
+    // score j of tile t: P^T operand c = j / 8, element e = j % 8
+    auto score = [&](int j) __attribute__((always_inline)) {
+      const int c = j >> 3, e = j & 7;
+      return sc[c >> 1][8 * (c & 1) + e];
+    };
+    float x[32], pr[32];
+    uint32_t wp[16];
+    x[0] = __builtin_fmaf(score(0), c2, nm);
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) read_frag(i);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + kAhead < 32) read_frag(i + kAhead);
+      const int k = i >> 1;
+      if (i & 1) {
+        const int sb = k & 1, c = k >> 1;
+        if (c == 0) {
+          f32x16 z;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z[r] = 0.f;
+          sn[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i], qb[c], z, 0, 0, 0);
+        } else {
+          sn[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i], qb[c], sn[sb], 0, 0, 0);
+        }
+      } else {
+        const int dt = k & 3, c = k >> 2;
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            frag[i], as_bf16x8(pp[c][0], pp[c][1], pp[c][2], pp[c][3]), o[dt], 0, 0, 0);
+      }
+      // softmax of tile t, lagged so that no instruction waits on the one before it: the logit of
+      // score i + 1, the probability of score i, the bf16 pair of scores i - 4, i - 3, and the row
+      // sum of the pair packed two chunks earlier
+      if (i + 1 < 32) x[i + 1] = __builtin_fmaf(score(i + 1), c2, nm);
+      pr[i] = __builtin_amdgcn_exp2f(x[i]);
+      if (i >= 4 && ((i - 3) & 1)) {
+        const int jp = i - 3;
+        wp[jp >> 1] = pack_bf16(pr[jp - 1], pr[jp]);
+        pn[jp >> 3][(jp & 7) >> 1] = wp[jp >> 1];
+      }
+      if (i >= 6 && ((i - 5) & 1)) {
+        const int jd = i - 5;
+        lsum2[(jd >> 1) & 1] = add_pair(wp[jd >> 1], lsum2[(jd >> 1) & 1]);
+      }
+      if (i == 0) ld.fetch_v(tab, min(t + 1, last) * kKT, n_keys, wave);
+      if (i == 1) ld.fetch_k(tab, min(t + 3, last) * kKT, n_keys, wave);
+      if (i == 4) ld.store_v_masked(vwrite, t * kKT, n_keys, wave, lane);
+      if (i == 5) ld.load_v_fetched(vpool, blk_stride, head_off, min(t + 1, last) * kKT, wave, lane);
+      if (i == 8) ld.store_k(kwrite, wave, lane);
+      if (i == 9) ld.load_k_fetched(kpool, blk_stride, head_off, min(t + 3, last) * kKT, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the pairs and sums the lag left: pairs (28, 29), (30, 31); sums of pairs 13, 14, 15
+#pragma unroll
+    for (int jp = 29; jp < 32; jp += 2) {
+      wp[jp >> 1] = pack_bf16(pr[jp - 1], pr[jp]);
+      pn[jp >> 3][(jp & 7) >> 1] = wp[jp >> 1];
+    }
+#pragma unroll
+    for (int jd = 27; jd < 32; jd += 2) lsum2[(jd >> 1) & 1] = add_pair(wp[jd >> 1], lsum2[(jd >> 1) & 1]);
+    float lsum = lsum2[0] + lsum2[1];
+    if (__builtin_amdgcn_ballot_w64(row_ok && !(lsum <= kSumBound)) != 0) {
+      // the tile's true row max; rescale everything accumulated so far to it and recompute the tile
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[sb][r]);
+      mx = half_max(mx) * c2;
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_lane *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      const float nm2 = m_new == -INFINITY ? 0.f : -m_new;
+      lsum = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c >> 1][8 * (c & 1) + e], c2, nm2));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c >> 1][8 * (c & 1) + e + 1], c2, nm2));
+          const uint32_t w = pack_bf16(p0, p1);
+          pn[c][e >> 1] = w;
+          lsum = add_pair(w, lsum);
+        }
+    }
+    l_lane += lsum;
+    __syncthreads();
+  };
+
+  // Prologue: S(0) from K(0); K(1) in kbuf1; V(-1) = zeros in vbuf1 with P(-1) = 0 (O(-1) adds 0);
+  // the register stage then holds K(2) and V(0).
+  __syncthreads();   // the table in LDS
+  ld.load_k(kpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+  ld.load_v(vpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+  ld.store_k(kbuf0, wave, lane);
+  ld.load_k(kpool, tab, blk_stride, head_off, min(1, last) * kKT, n_keys, wave, lane);
+  for (int i = threadIdx.x; i < kVBytes / 16; i += 64 * W)
+    reinterpret_cast<uint4*>(vbuf1)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  f32x16 sa[2], sb2[2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sa[sb][r] = 0.f;
+    const char* krow = kbuf0 + (sb * 32 + (lane & 31)) * kKStride + 16 * h;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      sa[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(krow + 32 * c), qb[c],
+                                                       sa[sb], 0, 0, 0);
+  }
+  ld.store_k(kbuf1, wave, lane);
+  ld.load_k(kpool, tab, blk_stride, head_off, min(2, last) * kKT, n_keys, wave, lane);
+  __syncthreads();
+
+  uint32_t pA[4][4], pB[4][4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pA[c][w] = 0u;
+  int t = 0;
+#pragma unroll 1
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, sa, sb2, pA, pB);
+    step(t + 1, sb2, sa, pB, pA);
+  }
+  // V(last) was stored into vbuf[last & 1] by the last step
+  const char* const vlast = (last & 1) ? vbuf1 : vbuf0;
+  if (t < n_tiles) {
+    step(t, sa, sb2, pA, pB);
+    // the last tile's O products: P(last) in pB
+    const char* vread = vlast;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const char* vrow = vread + (dt * 32 + (lane & 31)) * kVStride + 16 * h;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vrow + 32 * c),
+                                                        as_bf16x8(pB[c][0], pB[c][1], pB[c][2], pB[c][3]), o[dt],
+                                                        0, 0, 0);
+    }
+  } else {
+    const char* vread = vlast;                       // P(last) in pA
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const char* vrow = vread + (dt * 32 + (lane & 31)) * kVStride + 16 * h;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vrow + 32 * c),
+                                                        as_bf16x8(pA[c][0], pA[c][1], pA[c][2], pA[c][3]), o[dt],
+                                                        0, 0, 0);
+    }
+  }
+
+  if (!row_ok) return;
+  const float l = half_sum(l_lane);
+  const float inv = l > 0.f ? a.v_scale / l : 0.f;
+  const int64_t obase = (static_cast<int64_t>(q_base + qi) * a.num_q_heads + head) * kD;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int d = dt * 32 + 8 * rr + 4 * h;
+      const float x0 = o[dt][4 * rr] * inv, x1 = o[dt][4 * rr + 1] * inv;
+      const float x2 = o[dt][4 * rr + 2] * inv, x3 = o[dt][4 * rr + 3] * inv;
+      if (out_bf16) {
+        uint16_t* op = static_cast<uint16_t*>(a.out) + obase + d;
+        *reinterpret_cast<uint2*>(op) = make_uint2(f32_to_bf16_bits(x0) | (f32_to_bf16_bits(x1) << 16),
+                                                   f32_to_bf16_bits(x2) | (f32_to_bf16_bits(x3) << 16));
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d) = make_float4(x0, x1, x2, x3);
+      }
+    }
+}
+
 template <int KV, int BS, int G, int W>
 int launch_g(const PrefillArgs& a, int out_bf16, hipStream_t s) {
   constexpr int QT = 32 * W / G;
@@ -444,6 +859,25 @@ int launch_g(const PrefillArgs& a, int out_bf16, hipStream_t s) {
   const int xcd_remap = a.num_kv_heads % 8 == 0;
   const int64_t wgs = groups * num_qtiles;
   if (wgs > 0x7fffffff) return -1;
+  // The pipelined kernel keeps the sequence's table row in LDS beside its 70 KiB of tiles; rows
+  // longer than kMaxLdsTable entries take the kernel that reads the table from memory.
+  const size_t tab_bytes = (static_cast<size_t>(a.max_blocks) * 4 + 15) / 16 * 16;
+  // 8-wave tiles only: with 4 waves the pipelined kernel measured 4% slower on the mixed fp8 step,
+  // and its bf16 instances spill.
+  if constexpr (W == 8) {
+    if (a.max_blocks <= kMaxLdsTable) {
+      static bool attr_set = false;
+      if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pipe_kernel<KV, BS, G, W>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsTable * 4);
+        if (e != hipSuccess) return static_cast<int>(e);
+        attr_set = true;
+      }
+      hipLaunchKernelGGL((prefill_pipe_kernel<KV, BS, G, W>), dim3(static_cast<unsigned>(wgs)), dim3(64 * W),
+                         tab_bytes, s, a, out_bf16, num_qtiles, xcd_remap);
+      return static_cast<int>(hipGetLastError());
+    }
+  }
   hipLaunchKernelGGL((prefill_kernel<KV, BS, G, W>), dim3(static_cast<unsigned>(wgs)), dim3(64 * W), 0, s, a,
                      out_bf16, num_qtiles, xcd_remap);
   return static_cast<int>(hipGetLastError());
