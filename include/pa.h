@@ -18,9 +18,12 @@
  *     the work queued on `stream` has finished.  The library never allocates device memory; the
  *     one device array it owns, the static workspace of pa_decode_noalloc, is reserved by the code
  *     object loader on each GPU the library runs on.
- *   - Host arguments are validated (null pointers, dtypes, shapes, sizes); values that live in
- *     device memory (slots, tables, lengths, copy pairs) are NOT validated: an out-of-range value
- *     there is undefined behaviour (the caller's allocator produces them; see pa_alloc_*).
+ *   - Host arguments are validated (null pointers, dtypes, shapes, sizes, alignment).  Values that
+ *     live in device memory (slots, tables, lengths, copy pairs) are checked on the host only by
+ *     pa_validate_* (the caller's allocator, pa_alloc_*, produces valid ones).  On the device a block
+ *     id outside the pool is clamped into it, and a slot or copy pair outside it is skipped, so a bad
+ *     value gives a wrong result but no access outside the pools; lengths are clamped to the
+ *     launch's bounds.  Prefill's query_start_loc must stay inside q and out (pa_validate_prefill).
  *   - Launches are asynchronous on `stream` (a hipStream_t; NULL = the default stream), in order,
  *     with no implicit synchronisation.  Calls that overlap on different streams and touch the same
  *     pool blocks race.
@@ -79,7 +82,8 @@ typedef void* pa_stream; /* hipStream_t */
 const char* pa_status_str(int32_t status);
 /* Detail of the last failure on this thread (static thread-local buffer; "" after success). */
 const char* pa_last_error(void);
-/* ABI version: (major << 16) | minor (2.0: pa_decode without the cache hint, pa_decode_noalloc). */
+/* ABI version: (major << 16) | minor (2.0: pa_decode without the cache hint, pa_decode_noalloc;
+ * 2.1: pa_validate_*, pa_plan_beam_tails, device-side clamping of block ids). */
 int32_t pa_version(void);
 
 /* ---------------------------------------------------------------------------------------------
@@ -282,6 +286,19 @@ pa_status pa_plan_shared_blocks(const int32_t* tables, int32_t max_blocks, const
                                 int32_t block_size, int32_t width, int32_t* shared_blocks);
 
 /* ---------------------------------------------------------------------------------------------
+ * pa_plan_beam_tails (host) -- the private tails of a beam decode batch laid out as in
+ * pa_plan_shared_blocks: sequence s of group g = s / width keeps its blocks from shared_blocks[g]
+ * on.  tail_lens host int32 [num_seqs] receives lens[s] - shared_blocks[g] * block_size;
+ * tail_tables host int32 [num_seqs][tail_max_blocks] receives each tail's table entries, padded
+ * with 0; *needed_max_blocks (may be NULL) the longest tail in blocks.  tail_tables may be NULL to
+ * get only the lengths and the needed width.  PA_ERR_INVALID if a group's shared blocks exceed a
+ * member's length, a row is shorter than its length, or tail_max_blocks is too small.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_plan_beam_tails(const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t num_seqs,
+                             int32_t block_size, int32_t width, const int32_t* shared_blocks, int32_t* tail_tables,
+                             int32_t tail_max_blocks, int32_t* tail_lens, int32_t* needed_max_blocks);
+
+/* ---------------------------------------------------------------------------------------------
  * pa_merge_states -- combine two attention results of the same query rows over disjoint key sets
  * (a shared segment and a private tail), the rescaled combination the split merge uses:
  *     M = max(lse_a, lse_b),  w_x = exp(lse_x - M),
@@ -294,6 +311,32 @@ pa_status pa_plan_shared_blocks(const int32_t* tables, int32_t max_blocks, const
 pa_status pa_merge_states(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
                           int64_t rows, int32_t head_dim, void* out, int32_t out_dtype, float* lse_out,
                           pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Host checks of device-resident inputs (no GPU).  The kernels use these values as given; out of
+ * range they would address the wrong memory, so the kernels also clamp a block id into the pool and
+ * skip slots and copy pairs outside it -- a bad value then gives a wrong result for its sequence or
+ * token, never an access outside the pools.  These calls check host copies of the values before
+ * they are sent to the device, and name the first bad entry in pa_last_error() ([day28] §三 3.1:
+ * logical block j of a sequence lives in physical block table[j]; FAQ Q3).
+ *   pa_validate_decode   table entries 0 .. ceil(L_s / block_size) - 1 of every sequence inside the
+ *                        pool; 0 <= L_s <= max_context_len; ceil(L_s / b) <= max_blocks_per_seq
+ *   pa_validate_prefill  query_start_loc non-decreasing from >= 0, every chunk <= max_chunk_len,
+ *                        qsl[num_seqs] <= total_q, prior lengths >= 0, table entries of
+ *                        prior + chunk tokens inside the pool
+ *   pa_validate_slots    every non-negative slot < num_blocks * block_size, and distinct
+ *   pa_validate_pairs    sources inside src_pool, destinations inside dst_pool and distinct; with
+ *                        in_place != 0 (copy-on-write) no destination is also a source
+ * All pointers are host pointers.  PA_OK, or PA_ERR_INVALID.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_validate_decode(const pa_pool_desc* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len);
+pa_status pa_validate_prefill(const pa_pool_desc* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* query_start_loc, const int32_t* prior_context_lens, int32_t num_seqs,
+                              int32_t max_chunk_len, int64_t total_q);
+pa_status pa_validate_slots(const pa_pool_desc* pool, const int64_t* slot_mapping, int64_t num_tokens);
+pa_status pa_validate_pairs(const pa_pool_desc* src_pool, const pa_pool_desc* dst_pool, const int32_t* pairs,
+                            int32_t num_pairs, int32_t in_place);
 
 /* ---------------------------------------------------------------------------------------------
  * Self-check of the device fp8 decoding: out[c] = value of e4m3 code c (c = 0..255) as decoded by

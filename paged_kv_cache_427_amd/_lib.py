@@ -47,6 +47,12 @@ _PROTOS = {
     "pa_merge_states": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_int32,
                                   c_void_p, c_void_p]),
     "pa_plan_shared_blocks": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, c_int32, _I32P]),
+    "pa_plan_beam_tails": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, c_int32, _I32P, _I32P, c_int32, _I32P,
+                                     _I32P]),
+    "pa_validate_decode": (c_int32, [POINTER(PoolDesc), _I32P, c_int32, _I32P, c_int32, c_int32]),
+    "pa_validate_prefill": (c_int32, [POINTER(PoolDesc), _I32P, c_int32, _I32P, _I32P, c_int32, c_int32, c_int64]),
+    "pa_validate_slots": (c_int32, [POINTER(PoolDesc), _I64P, c_int64]),
+    "pa_validate_pairs": (c_int32, [POINTER(PoolDesc), POINTER(PoolDesc), _I32P, c_int32, c_int32]),
     "pa_swap_blocks": (c_int32, [c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_void_p, POINTER(PoolDesc),
                                  c_void_p, c_int32, c_void_p]),
     "pa_decode_workspace_size": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_size_t)]),

@@ -26,6 +26,23 @@ def plan_shared_blocks(tables: np.ndarray, lens: np.ndarray, block_size: int, wi
     return out
 
 
+def plan_beam_tails(tables: np.ndarray, lens: np.ndarray, block_size: int, width: int, shared: np.ndarray):
+    """Each branch's private tail after its group's shared blocks (host, pa_plan_beam_tails): the
+    tail table rows (int32 [num_seqs][longest tail in blocks, at least 1]) and lengths."""
+    t = np.ascontiguousarray(tables, dtype=np.int32)
+    l = np.ascontiguousarray(lens, dtype=np.int32)
+    k = np.ascontiguousarray(shared, dtype=np.int32)
+    tail_lens = np.zeros(len(l), dtype=np.int32)
+    need = np.zeros(1, dtype=np.int32)
+    args = (t.ctypes.data_as(_I32P), t.shape[1], l.ctypes.data_as(_I32P), len(l), int(block_size), int(width),
+            k.ctypes.data_as(_I32P))
+    check(lib().pa_plan_beam_tails(*args, None, 0, tail_lens.ctypes.data_as(_I32P), need.ctypes.data_as(_I32P)))
+    nb = max(int(need[0]), 1)
+    tt = np.zeros((len(l), nb), dtype=np.int32)
+    check(lib().pa_plan_beam_tails(*args, tt.ctypes.data_as(_I32P), nb, tail_lens.ctypes.data_as(_I32P), None))
+    return tt, tail_lens
+
+
 class CascadeDecode:
     """Device inputs of a beam decode over fixed tables and lengths (rebuilt when they change)."""
 
@@ -48,13 +65,7 @@ class CascadeDecode:
         self.pre_lens = torch.as_tensor((k * b).astype(np.int32), device=dev)
         self.pre_max = int((k * b).max()) if self.groups else 0
         # private tails: each branch's blocks from its group's k on
-        tail_len = lens - np.repeat(self.shared_tokens, width)
-        nb = max(int(-(-tail_len.max() // b)) if self.n else 1, 1)
-        tt = np.zeros((self.n, nb), np.int32)
-        for s in range(self.n):
-            kk = int(k[s // width])
-            row = tables[s, kk:kk + -(-int(tail_len[s]) // b)]
-            tt[s, :len(row)] = row
+        tt, tail_len = plan_beam_tails(tables, lens, b, width, k)
         self.tail_tables = torch.as_tensor(tt, device=dev)
         self.tail_lens = torch.as_tensor(tail_len.astype(np.int32), device=dev)
         self.tail_max = int(tail_len.max()) if self.n else 0

@@ -438,6 +438,37 @@ pa_status pa_plan_shared_blocks(const int32_t* tables, int32_t max_blocks, const
   return pa_ok();
 }
 
+pa_status pa_plan_beam_tails(const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t num_seqs,
+                             int32_t block_size, int32_t width, const int32_t* shared_blocks, int32_t* tail_tables,
+                             int32_t tail_max_blocks, int32_t* tail_lens, int32_t* needed_max_blocks) {
+  if (!shared_blocks || !tail_lens || (num_seqs > 0 && (!tables || !lens)))
+    return pa_fail(PA_ERR_INVALID, "pa_plan_beam_tails: null argument");
+  if (width < 1 || block_size < 1 || max_blocks < 0 || num_seqs < 0 || num_seqs % width != 0 || tail_max_blocks < 0)
+    return pa_fail(PA_ERR_INVALID, "pa_plan_beam_tails: num_seqs must be a multiple of width >= 1");
+  int64_t need = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t k = shared_blocks[s / width];
+    const int64_t tail = static_cast<int64_t>(lens[s]) - k * block_size;
+    if (k < 0 || tail < 0) return pa_fail(PA_ERR_INVALID, "pa_plan_beam_tails: shared blocks beyond a length");
+    const int64_t nb = (tail + block_size - 1) / block_size;
+    if (k + nb > max_blocks) return pa_fail(PA_ERR_INVALID, "pa_plan_beam_tails: table row shorter than the length");
+    need = std::max(need, nb);
+    tail_lens[s] = static_cast<int32_t>(tail);
+  }
+  if (needed_max_blocks) *needed_max_blocks = static_cast<int32_t>(need);
+  if (!tail_tables) return pa_ok();
+  if (need > tail_max_blocks)
+    return pa_fail(PA_ERR_INVALID, "pa_plan_beam_tails: tail_max_blocks is smaller than the longest tail");
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t k = shared_blocks[s / width];
+    const int64_t nb = (static_cast<int64_t>(tail_lens[s]) + block_size - 1) / block_size;
+    const int32_t* row = tables + static_cast<int64_t>(s) * max_blocks + k;
+    int32_t* out = tail_tables + static_cast<int64_t>(s) * tail_max_blocks;
+    for (int64_t j = 0; j < tail_max_blocks; ++j) out[j] = j < nb ? row[j] : 0;
+  }
+  return pa_ok();
+}
+
 pa_status pa_alloc_cache_stats(const pa_allocator* a, int32_t* num_cached, int32_t* num_evictable) {
   if (!a) return pa_fail(PA_ERR_INVALID, "allocator is null");
   if (num_cached) *num_cached = static_cast<int32_t>(a->entries.size());

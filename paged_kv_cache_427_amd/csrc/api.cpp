@@ -11,12 +11,12 @@
 
 namespace {
 
-thread_local char g_err[512];
 constexpr int kMaxGridYZ = 65535;
 
 pa_status hip_fail(int e, const char* where) {
-  std::snprintf(g_err, sizeof g_err, "%s: %s", where, hipGetErrorString(static_cast<hipError_t>(e)));
-  return PA_ERR_HIP;
+  char msg[512];
+  std::snprintf(msg, sizeof msg, "%s: %s", where, hipGetErrorString(static_cast<hipError_t>(e)));
+  return pa_fail(PA_ERR_HIP, msg);
 }
 
 pa_status launch_status(int rc, const char* where) {
@@ -72,32 +72,7 @@ int64_t decode_max_parts(int32_t max_ctx, int32_t part) {
 
 }  // namespace
 
-pa_status pa_fail(pa_status st, const char* msg) {
-  std::snprintf(g_err, sizeof g_err, "%s", msg);
-  return st;
-}
-
-pa_status pa_ok() {
-  g_err[0] = '\0';
-  return PA_OK;
-}
-
 extern "C" {
-
-const char* pa_status_str(int32_t s) {
-  switch (s) {
-    case PA_OK: return "PA_OK";
-    case PA_ERR_INVALID: return "PA_ERR_INVALID";
-    case PA_ERR_OOM: return "PA_ERR_OOM";
-    case PA_ERR_HIP: return "PA_ERR_HIP";
-    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
-    default: return "PA_ERR_UNKNOWN";
-  }
-}
-
-const char* pa_last_error(void) { return g_err; }
-
-int32_t pa_version(void) { return (2 << 16) | 0; }
 
 pa_status pa_cache_write(const void* k, const void* v, int32_t in_dtype, int64_t num_tokens,
                          const int64_t* slots, void* k_pool, void* v_pool, const pa_pool_desc* pool,
@@ -127,6 +102,7 @@ pa_status pa_cache_write(const void* k, const void* v, int32_t in_dtype, int64_t
   a.pool_dtype = pool->dtype;
   a.k_inv_scale = pool->dtype == PA_FP8_E4M3 ? 1.0f / pool->k_scale : 1.0f;
   a.v_inv_scale = pool->dtype == PA_FP8_E4M3 ? 1.0f / pool->v_scale : 1.0f;
+  a.num_slots = static_cast<int64_t>(pool->num_blocks) * pool->block_size;
   return launch_status(pa::launch_cache_write(a, stream), "pa_cache_write");
 }
 
@@ -148,6 +124,7 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool, c
   a.num_pairs = num_pairs;
   a.num_layers = 1;
   a.layer_stride = 0;
+  a.src_blocks = a.dst_blocks = pool->num_blocks;
   return launch_status(pa::launch_copy_blocks(a, stream), "pa_copy_blocks");
 }
 
@@ -177,6 +154,7 @@ pa_status pa_copy_blocks_layers(void* k_pools, void* v_pools, int64_t layer_stri
   a.num_pairs = num_pairs;
   a.num_layers = num_layers;
   a.layer_stride = layer_stride_bytes;
+  a.src_blocks = a.dst_blocks = pool->num_blocks;
   return launch_status(pa::launch_copy_blocks(a, stream), "pa_copy_blocks_layers");
 }
 
@@ -243,6 +221,8 @@ pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const pa_pool_desc*
   a.num_pairs = num_pairs;
   a.num_layers = 1;
   a.layer_stride = 0;
+  a.src_blocks = src_pool->num_blocks;
+  a.dst_blocks = dst_pool->num_blocks;
   return launch_status(pa::launch_copy_blocks(a, stream), "pa_swap_blocks");
 }
 
@@ -323,6 +303,7 @@ pa_status pa_decode_ex(const void* q, int32_t q_dtype, const int64_t* q_strides,
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
+  a.num_blocks = pool->num_blocks;
   const float kscale = pool->dtype == PA_FP8_E4M3 ? pool->k_scale : 1.0f;
   a.qk_scale = static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
   a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
@@ -442,6 +423,7 @@ pa_status pa_prefill_chunk(const void* q, int32_t q_dtype, const void* k_pool, c
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
+  a.num_blocks = pool->num_blocks;
   const float kscale = pool->dtype == PA_FP8_E4M3 ? pool->k_scale : 1.0f;
   a.qk_scale = static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
   a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;

@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(kThreads) cache_write_k_kernel(CacheWriteArgs 
   const int head = static_cast<int>(row % a.num_kv_heads);
   const int64_t t = row / a.num_kv_heads;
   const int64_t slot = a.slots[t];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= a.num_slots) return;   // skipped token, or a slot outside the pool
   const int64_t blk = slot >> log2_bs;
   const int64_t off = slot & ((1 << log2_bs) - 1);
   constexpr int kOutElem = POOL == kF32 ? 4 : POOL == kBF16 ? 2 : 1;
@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(kThreads) cache_write_v_kernel(CacheWriteArgs 
   const int64_t t = (rest / a.num_kv_heads) * 8 + (lane >> 3);
   if (t >= a.num_tokens) return;
   const int64_t slot = a.slots[t];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= a.num_slots) return;   // skipped token, or a slot outside the pool
   const int bs = 1 << log2_bs;
   const int64_t blk = slot >> log2_bs;
   const int off = static_cast<int>(slot & (bs - 1));
@@ -153,6 +153,8 @@ __global__ void __launch_bounds__(kThreads) copy_blocks_kernel(CopyBlocksArgs a)
   const int pair = blockIdx.x;
   const int32_t src = a.pairs[2 * pair];
   const int32_t dst = a.pairs[2 * pair + 1];
+  // a pair naming a block outside its pool is skipped (no memory outside the pools is touched)
+  if (src < 0 || src >= a.src_blocks || dst < 0 || dst >= a.dst_blocks) return;
   const int64_t layer_off = static_cast<int64_t>(blockIdx.y >> 1) * a.layer_stride;
   const char* sbase = static_cast<const char*>((blockIdx.y & 1) ? a.src_v : a.src_k) + layer_off;
   char* dbase = static_cast<char*>((blockIdx.y & 1) ? a.dst_v : a.dst_k) + layer_off;

@@ -175,6 +175,7 @@ struct SeqView {
   int64_t blk_stride;      // bytes of one block of one pool (all KV heads)
   int nblk;                // valid table entries: ceil(L / BS)
   int shared_units;        // units touching the sequence's shared leading blocks: read through the caches
+  int pool_blocks;         // blocks of the pool (table entries are clamped below it)
 };
 
 // Physical blocks of the unit starting at key U (32 keys: 4, 2 or 1 blocks of 8, 16 or 32 tokens).
@@ -201,7 +202,12 @@ __device__ __forceinline__ UnitBlocks<BS> unit_blocks(const SeqView& sv, int U) 
   const int j0 = U / BS;
   UnitBlocks<BS> ub;
 #pragma unroll
-  for (int q = 0; q < UnitBlocks<BS>::N; ++q) ub.b[q] = sv.tab[min(j0 + q, sv.nblk - 1)];
+  for (int q = 0; q < UnitBlocks<BS>::N; ++q) {
+    // a table entry outside the pool is clamped into it: a wrong result for this sequence, but no
+    // read outside the pool
+    const int e = sv.tab[min(j0 + q, sv.nblk - 1)];
+    ub.b[q] = min(max(e, 0), sv.pool_blocks - 1);
+  }
   return ub;
 }
 
@@ -488,6 +494,7 @@ __device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int seq, int kv
   sv.tab = ro(a.tables) + static_cast<int64_t>(seq) * a.max_blocks;
   sv.blk_stride = static_cast<int64_t>(a.num_kv_heads) * TILE;
   sv.nblk = (clamped_len(a, seq) + BS - 1) / BS;
+  sv.pool_blocks = a.num_blocks;
   sv.shared_units = a.shared_blocks ? (max(ro(a.shared_blocks)[seq], 0) * BS + kUnit - 1) / kUnit : 0;
   return sv;
 }

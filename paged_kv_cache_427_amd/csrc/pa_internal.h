@@ -30,6 +30,7 @@ struct CacheWriteArgs {
   int pool_dtype;
   float k_inv_scale;  // fp32(1 / k_scale), rounded once on the host
   float v_inv_scale;
+  int64_t num_slots;  // num_blocks * block_size: slots at or beyond it are skipped
 };
 
 // Whole-block copies from (src_k, src_v) to (dst_k, dst_v); the same pools for copy-on-write,
@@ -44,6 +45,8 @@ struct CopyBlocksArgs {
   int32_t num_pairs;
   int32_t num_layers;    // layer l's pools start layer_stride bytes after layer l - 1's
   int64_t layer_stride;
+  int32_t src_blocks;    // blocks of the source and destination pools: pairs outside are skipped
+  int32_t dst_blocks;
 };
 
 struct DecodeArgs {
@@ -57,6 +60,7 @@ struct DecodeArgs {
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
+  int32_t num_blocks;    // pool blocks: a table entry outside [0, num_blocks) is clamped into it
   float qk_scale;        // scale * k_scale * log2(e): logits in base-2 units
   float v_scale;
   int32_t part_tokens;   // tokens per partition (a multiple of 16; no sequence crosses one when it
@@ -104,6 +108,7 @@ struct PrefillArgs {
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
+  int32_t num_blocks;    // pool blocks: a table entry outside [0, num_blocks) is clamped into it
   float qk_scale;        // scale * k_scale * log2(e)
   float v_scale;
   int32_t max_chunk;

@@ -103,6 +103,10 @@ struct TileLoader {
   static constexpr int kVW = 16 * kE / 4;               // dwords of one 16-key piece (fp8 4, bf16 8)
   u32x4 k[kKU];
   uint32_t v[kVU][kVW];
+  int max_blocks;    // entries of a table row: lookups stay inside it
+  int pool_blocks;   // blocks of the pool: a table entry outside it is clamped into it (wrong result, no
+                     // read outside the pool)
+  __device__ __forceinline__ int64_t clamp_blk(int e) const { return min(max(e, 0), pool_blocks - 1); }
 
   // K or V of tile keys [key0, key0 + 64).  Every load is issued unconditionally, so that the only
   // wait for them is the one before the matching store; a block past the last one holding a key
@@ -110,14 +114,14 @@ struct TileLoader {
   // zeroed in store_v()).
   __device__ __forceinline__ void load_k(const char* kpool, const int32_t* tab, int64_t blk_stride, int64_t head_off,
                                          int key0, int n_keys, int wave, int lane) {
-    const int jlast = (n_keys - 1) / BS;
+    const int jlast = min((n_keys - 1) / BS, max_blocks - 1);
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
       // keys of this wave's instruction: key0 + (u*256 + 64*wave) / CPR .. + 64/CPR (one block)
       const int kw = key0 + (u * kThreads + 64 * wave) / kCPR;
       const int key = key0 + (u * kThreads + 64 * wave + lane) / kCPR;
       const int ch = lane % kCPR;
-      const int64_t phys = tab[min(kw / BS, jlast)];
+      const int64_t phys = clamp_blk(tab[min(kw / BS, jlast)]);
       k[u] = *reinterpret_cast<const u32x4*>(kpool + phys * blk_stride + head_off +
                                              static_cast<int64_t>(key % BS) * kRowBytes + ch * 16);
     }
@@ -125,14 +129,14 @@ struct TileLoader {
 
   __device__ __forceinline__ void load_v(const char* vpool, const int32_t* tab, int64_t blk_stride, int64_t head_off,
                                          int key0, int n_keys, int wave, int lane) {
-    const int jlast = (n_keys - 1) / BS;
+    const int jlast = min((n_keys - 1) / BS, max_blocks - 1);
 #pragma unroll
     for (int u = 0; u < kVU; ++u) {
       const int g16 = (W / 2) * u + (wave >> 1);              // 16-key group of the tile
       const int dim = 64 * (wave & 1) + lane;
       const int kg = key0 + 16 * g16;                   // first key of the group
       if constexpr (BS >= 16) {
-        const int64_t phys = tab[min(kg / BS, jlast)];
+        const int64_t phys = clamp_blk(tab[min(kg / BS, jlast)]);
         const char* row = vpool + phys * blk_stride + head_off + static_cast<int64_t>(dim) * BS * kE +
                           (kg % BS) * kE;
 #pragma unroll
@@ -144,7 +148,7 @@ struct TileLoader {
         // two 8-key blocks
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-          const int64_t phys = tab[min(kg / 8 + hb, jlast)];
+          const int64_t phys = clamp_blk(tab[min(kg / 8 + hb, jlast)]);
           const char* row = vpool + phys * blk_stride + head_off + static_cast<int64_t>(dim) * 8 * kE;
           if constexpr (kE == 1) {
             const uint2 w = *reinterpret_cast<const uint2*>(row);
@@ -165,7 +169,7 @@ struct TileLoader {
   int pk[kKU];
   int pvb[kVU][kVB];
   __device__ __forceinline__ void fetch_k(const int32_t* tab, int key0, int n_keys, int wave) {
-    const int jlast = (n_keys - 1) / BS;
+    const int jlast = min((n_keys - 1) / BS, max_blocks - 1);
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
       const int kw = key0 + (u * kThreads + 64 * wave) / kCPR;
@@ -173,7 +177,7 @@ struct TileLoader {
     }
   }
   __device__ __forceinline__ void fetch_v(const int32_t* tab, int key0, int n_keys, int wave) {
-    const int jlast = (n_keys - 1) / BS;
+    const int jlast = min((n_keys - 1) / BS, max_blocks - 1);
 #pragma unroll
     for (int u = 0; u < kVU; ++u) {
       const int kg = key0 + 16 * ((W / 2) * u + (wave >> 1));
@@ -397,6 +401,8 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) prefill_kernel(Prefill
   char* const vbuf1 = smem + 2 * kKBytes + kVBytes;
   const int last = n_tiles - 1;
   TileLoader<KV, BS, W> ld;
+  ld.max_blocks = a.max_blocks;
+  ld.pool_blocks = a.num_blocks;
 
   // S^T = K Q^T of the tile whose K rows are in kb, as two 32-key halves.
   auto scores = [&](const char* kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
@@ -621,7 +627,7 @@ __global__ void __launch_bounds__(64 * W, 1) prefill_pipe_kernel(PrefillArgs a, 
     // the table entries of this workgroup's keys, into LDS (ready after the prologue's first barrier)
     const int32_t* tab_g = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
     const int nblk = min((n_keys + BS - 1) / BS, a.max_blocks);
-    for (int i = threadIdx.x; i < nblk; i += 64 * W) tab_s[i] = tab_g[i];
+    for (int i = threadIdx.x; i < nblk; i += 64 * W) tab_s[i] = min(max(tab_g[i], 0), a.num_blocks - 1);
   }
   const int32_t* const tab = tab_s;
 
@@ -640,6 +646,8 @@ __global__ void __launch_bounds__(64 * W, 1) prefill_pipe_kernel(PrefillArgs a, 
   char* const vbuf1 = smem + 2 * kKBytes + kVBytes;
   const int last = n_tiles - 1;
   TileLoader<KV, BS, W> ld;
+  ld.max_blocks = a.max_blocks;
+  ld.pool_blocks = a.num_blocks;
 
   // One step; on entry: sc = S(t); pp = P(t - 1) (bf16 pairs); LDS holds K(t + 1) and V(t - 1);
   // the register stage holds K(t + 2) and V(t).

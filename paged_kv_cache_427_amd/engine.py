@@ -13,7 +13,7 @@ import torch
 from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3
 from .allocator import BlockAllocator
 from .ops import (make_pool_desc, pa_cache_write, pa_copy_blocks, pa_decode, pa_decode_workspace_size,
-                  pa_prefill_chunk)
+                  pa_prefill_chunk, validate_decode, validate_pairs, validate_prefill, validate_slots)
 
 _PA = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 _CODE_TORCH = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8}
@@ -69,8 +69,12 @@ class StepInputs:
 class PagedKVEngine:
     """Owns the two pools of one layer and the host allocator of a workload (package `synth`)."""
 
-    def __init__(self, wl, device: str = "cuda", poison: Optional[int] = None, allocate_pools: bool = True):
+    def __init__(self, wl, device: str = "cuda", poison: Optional[int] = None, allocate_pools: bool = True,
+                 validate: bool = False):
         self.wl = wl
+        # validate: check every step's slots, copy pairs, tables and lengths on the host before they
+        # go to the device (pa_validate_*)
+        self.validate = validate
         self.device = torch.device(device)
         self.pool = make_pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
                                    _PA[wl.kv_dtype], wl.k_scale, wl.v_scale)
@@ -147,6 +151,9 @@ class PagedKVEngine:
         step_slots = slots[s0:s1].copy()
         dev = self.device
         cow = np.asarray(cows, np.int32).reshape(-1, 2)
+        if self.validate:
+            validate_slots(self.pool, step_slots)
+            validate_pairs(self.pool, self.pool, cow)
         si = StepInputs(cow_pairs=torch.as_tensor(cow, device=dev),
                         slots=torch.as_tensor(step_slots, device=dev),
                         k_new=self.k_tok[s0:s1], v_new=self.v_tok[s0:s1],
@@ -158,6 +165,8 @@ class PagedKVEngine:
             tabs = [len(self.alloc.table(s)) for s in wl.decode_seqs]
             mb = max(max(tabs), -(-max_len // wl.block_size), 1)
             host_tabs = self.alloc.fill_tables(wl.decode_seqs, mb)
+            if self.validate:
+                validate_decode(self.pool, host_tabs, lens, max_len)
             si.dec_tables = torch.as_tensor(host_tabs, device=dev)
             si.dec_lens = torch.as_tensor(lens, device=dev)
             shared = leading_shared_blocks(host_tabs, np.asarray(lens), wl.block_size)
@@ -173,8 +182,12 @@ class PagedKVEngine:
             chunk = np.asarray(wl.prefill_chunk, np.int32)
             tabs = [len(self.alloc.table(s)) for s in wl.prefill_seqs]
             mb = max(max(tabs), 1)
-            si.pre_tables = torch.as_tensor(self.alloc.fill_tables(wl.prefill_seqs, mb), device=dev)
-            si.pre_qsl = torch.as_tensor(np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32), device=dev)
+            pre_tabs = self.alloc.fill_tables(wl.prefill_seqs, mb)
+            qsl = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+            if self.validate:
+                validate_prefill(self.pool, pre_tabs, qsl, prior, int(chunk.max()), int(wl.q_prefill.shape[0]))
+            si.pre_tables = torch.as_tensor(pre_tabs, device=dev)
+            si.pre_qsl = torch.as_tensor(qsl, device=dev)
             si.pre_prior = torch.as_tensor(prior, device=dev)
             si.pre_q = wl.q_prefill.to(dev)
             si.pre_out = torch.empty_like(si.pre_q)

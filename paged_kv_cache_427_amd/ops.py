@@ -7,9 +7,10 @@ a GPU, these calls raise.
 import ctypes
 from typing import Optional
 
+import numpy as np
 import torch
 
-from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3, PoolDesc, check, lib
+from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3, PoolDesc, check, lib, _I32P, _I64P
 
 _TORCH_TO_PA = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
                 torch.float8_e4m3fn: PA_FP8_E4M3}
@@ -229,3 +230,40 @@ def pa_prefill_chunk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
 def pa_fp8_decode_table(out: torch.Tensor, stream=None) -> None:
     """out (float32 [256], device) <- the device's decoding of every e4m3 code."""
     check(lib().pa_fp8_decode_table(_dev(out, "out"), _stream(stream)))
+
+
+# ---- host checks of device-resident inputs (pa_validate_*): numpy arrays, before they are sent ----
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def validate_decode(pool: PoolDesc, tables, lens, max_context_len: int) -> None:
+    """Raise PaError unless every table entry a sequence uses lies in the pool and every length is in
+    [0, max_context_len] and fits its row."""
+    t, l = _i32(tables), _i32(lens)
+    check(lib().pa_validate_decode(ctypes.byref(pool), t.ctypes.data_as(_I32P), int(t.shape[1]),
+                                   l.ctypes.data_as(_I32P), len(l), int(max_context_len)))
+
+
+def validate_prefill(pool: PoolDesc, tables, query_start_loc, prior_lens, max_chunk_len: int, total_q: int) -> None:
+    """Raise PaError unless the chunks are ordered, bounded by max_chunk_len and total_q, and every table
+    entry of each sequence's prior context plus chunk lies in the pool."""
+    t, q, p = _i32(tables), _i32(query_start_loc), _i32(prior_lens)
+    check(lib().pa_validate_prefill(ctypes.byref(pool), t.ctypes.data_as(_I32P), int(t.shape[1]),
+                                    q.ctypes.data_as(_I32P), p.ctypes.data_as(_I32P), len(p), int(max_chunk_len),
+                                    int(total_q)))
+
+
+def validate_slots(pool: PoolDesc, slots) -> None:
+    """Raise PaError unless every non-negative slot lies in the pool and no two tokens share one."""
+    s = np.ascontiguousarray(slots, dtype=np.int64)
+    check(lib().pa_validate_slots(ctypes.byref(pool), s.ctypes.data_as(_I64P), len(s)))
+
+
+def validate_pairs(src_pool: PoolDesc, dst_pool: PoolDesc, pairs, in_place: bool = True) -> None:
+    """Raise PaError unless every (source, destination) pair lies in its pool, destinations are distinct
+    and, for copies within one pool, no destination is also a source."""
+    pr = _i32(np.asarray(pairs).reshape(-1, 2))
+    check(lib().pa_validate_pairs(ctypes.byref(src_pool), ctypes.byref(dst_pool), pr.ctypes.data_as(_I32P), len(pr),
+                                  1 if in_place else 0))

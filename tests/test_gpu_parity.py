@@ -28,7 +28,7 @@ def _say(*a):
 
 
 def _run(wl, partition=None):
-    eng = _engine()(wl, poison=poison_code(wl.kv_dtype))
+    eng = _engine()(wl, poison=poison_code(wl.kv_dtype), validate=True)
     eng.build_history()
     si = eng.prepare_step(partition)
     eng.run_step(si)
