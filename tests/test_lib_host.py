@@ -15,6 +15,7 @@ from paged_kv_cache_427_amd._lib import PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_UNSUP
 from paged_kv_cache_427_amd.allocator import BlockAllocator, OutOfBlocks, PaError, move_seq
 from oracle import RefAllocator, AllocError, move_seq as ref_move_seq
 from oracle import OutOfBlocks as RefOOM
+from tests.native import san_host
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -41,11 +42,30 @@ def test_version_and_status_strings():
 
 # ---- allocator: differential against the oracle's RefAllocator ---------------------------------
 
-def _both(nblocks, b, order):
-    return BlockAllocator(nblocks, b, order), RefAllocator(nblocks, b, order)
+@pytest.fixture(scope="session")
+def san_driver(tmp_path_factory):
+    """The host code built with -fsanitize=address,undefined, as a child process (tests/native)."""
+    if san_host.compiler() is None:
+        pytest.skip("g++ is not installed")
+    d = san_host.Driver(san_host.build(str(tmp_path_factory.mktemp("san"))))
+    yield d
+    d.close()                         # fails on a sanitizer report or a leak at exit
 
 
-def _same_state(c: BlockAllocator, r: RefAllocator, live):
+@pytest.fixture(scope="module", params=["lib", "asan"])
+def backend(request):
+    """(allocator class, move function): the shared library through ctypes, or the sanitized build."""
+    if request.param == "lib":
+        return BlockAllocator, move_seq
+    d = request.getfixturevalue("san_driver")
+    return (lambda *a: san_host.SanAllocator(d, *a)), san_host.san_move_seq
+
+
+def _both(backend, nblocks, b, order):
+    return backend[0](nblocks, b, order), RefAllocator(nblocks, b, order)
+
+
+def _same_state(c, r: RefAllocator, live):
     assert c.free_list() == r.free_list()
     for blk in range(r.num_blocks):
         assert c.refcount(blk) == r.refcount(blk)
@@ -64,9 +84,9 @@ _op = st.one_of(
 
 @settings(max_examples=300, deadline=None)
 @given(st.lists(_op, max_size=60), st.sampled_from([8, 16, 32]), st.integers(4, 30), st.integers(0, 2**31))
-def test_cpp_allocator_matches_reference(ops, b, nblocks, seed):
+def test_cpp_allocator_matches_reference(backend, ops, b, nblocks, seed):
     order = np.random.default_rng(seed).permutation(nblocks).astype(np.int32)
-    c, r = _both(nblocks, b, order)
+    c, r = _both(backend, nblocks, b, order)
     for op in ops:
         ref_exc = None
         try:
@@ -115,7 +135,7 @@ _pop = st.one_of(
 )
 
 
-def _same_cache(c: BlockAllocator, r: RefAllocator):
+def _same_cache(c, r: RefAllocator):
     assert c.evictable_list() == r.evictable_list()
     assert c.num_cached() == r.num_cached()
     assert c.available() == r.available()
@@ -123,9 +143,9 @@ def _same_cache(c: BlockAllocator, r: RefAllocator):
 
 @settings(max_examples=300, deadline=None)
 @given(st.lists(_pop, max_size=50), st.sampled_from([4, 8]), st.integers(3, 24), st.integers(0, 2**31))
-def test_cpp_prefix_cache_matches_reference(ops, b, nblocks, seed):
+def test_cpp_prefix_cache_matches_reference(backend, ops, b, nblocks, seed):
     order = np.random.default_rng(seed).permutation(nblocks).astype(np.int32)
-    c, r = _both(nblocks, b, order)
+    c, r = _both(backend, nblocks, b, order)
     c.enable_prefix_cache()
     r.enable_prefix_cache()
     content = {}                      # sid -> the token ids the sequence holds
@@ -264,10 +284,11 @@ _sop = st.one_of(
 @settings(max_examples=300, deadline=None)
 @given(st.lists(_sop, max_size=50), st.sampled_from([4, 16]), st.integers(2, 20), st.integers(1, 20),
        st.integers(0, 2**31), st.booleans())
-def test_cpp_swap_matches_reference(ops, b, n_dev, n_host, seed, caching):
+def test_cpp_swap_matches_reference(backend, ops, b, n_dev, n_host, seed, caching):
     order = np.random.default_rng(seed).permutation(n_dev).astype(np.int32)
-    cd, rd = _both(n_dev, b, order)
-    ch, rh = _both(n_host, b, None)
+    cd, rd = _both(backend, n_dev, b, order)
+    ch, rh = _both(backend, n_host, b, None)
+    move = backend[1]
     if caching:
         cd.enable_prefix_cache()
         rd.enable_prefix_cache()
@@ -303,7 +324,7 @@ def test_cpp_swap_matches_reference(ops, b, n_dev, n_host, seed, caching):
                 side[loc or "dev"][0].free_seq(op[1])
             else:
                 src, dst = ("dev", "host") if op[0] == "out" else ("host", "dev")
-                out_c = move_seq(side[src][0], side[dst][0], op[1])
+                out_c = move(side[src][0], side[dst][0], op[1])
             assert ref_exc is None, f"C++ accepted {op} that the reference refused: {ref_exc}"
         except OutOfBlocks:
             assert isinstance(ref_exc, RefOOM)
@@ -688,3 +709,73 @@ def test_validate_pairs():
     _invalid(validate_pairs, p, p, [(1, 2), (3, 2)], match="appears twice")
     _invalid(validate_pairs, p, q, [(7, 3)], False, match="destination block 3")
     _invalid(validate_pairs, p, q, [(8, 0)], False, match="source block 8")
+
+
+# ---- the host validators and planners under the sanitizers, on random and malformed inputs ------
+
+def _status(fn, *a):
+    try:
+        return 0, fn(*a)
+    except PaError as e:
+        return e.status, None
+
+
+_ints = lambda lo, hi, n: st.lists(st.integers(lo, hi), min_size=n, max_size=n)   # noqa: E731
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.data(), st.integers(0, 12), st.sampled_from([1, 8, 16]), st.integers(0, 5), st.integers(0, 6))
+def test_sanitized_validators_agree_with_library(san_driver, data, nb, bs, n, mb):
+    from paged_kv_cache_427_amd.ops import validate_decode, validate_pairs, validate_prefill, validate_slots
+    pool = PoolDesc(nb, bs, 1, 64, 1, 1.0, 1.0)
+    tabs = np.asarray(data.draw(_ints(-2, nb + 2, n * mb)), np.int32).reshape(n, mb)
+    lens = data.draw(_ints(-3, mb * bs + 5, n))
+    mx = data.draw(st.integers(-1, mb * bs + 5))
+    want = _status(validate_decode, pool, tabs, lens, mx)[0]
+    got = _status(san_driver.call, "vdecode", nb, bs, mb, san_host.arr(tabs), san_host.arr(lens), mx)[0]
+    assert got == want
+    qsl = np.cumsum([0] + data.draw(_ints(-2, 2 * bs, n))).tolist()
+    prior = data.draw(_ints(-1, mb * bs, n))
+    mc, tq = data.draw(st.integers(0, 3 * bs)), data.draw(st.integers(0, 8 * bs))
+    want = _status(validate_prefill, pool, tabs, qsl, prior, mc, tq)[0]
+    got = _status(san_driver.call, "vprefill", nb, bs, mb, san_host.arr(tabs), san_host.arr(qsl),
+                  san_host.arr(prior), mc, tq)[0]
+    assert got == want
+    slots = data.draw(st.lists(st.integers(-2, nb * bs + 2), max_size=12))
+    assert _status(san_driver.call, "vslots", nb, bs, san_host.arr(slots))[0] == \
+        _status(validate_slots, pool, slots)[0]
+    nd = data.draw(st.integers(0, 12))
+    pairs = data.draw(st.lists(st.tuples(st.integers(-1, nb + 1), st.integers(-1, nd + 1)), max_size=6))
+    in_place = data.draw(st.booleans())
+    dpool = PoolDesc(nd, 16, 1, 64, 1, 1.0, 1.0)
+    spool = PoolDesc(nb, 16, 1, 64, 1, 1.0, 1.0)
+    want = _status(validate_pairs, spool, dpool, np.asarray(pairs, np.int32).reshape(-1, 2), in_place)[0]
+    got = _status(san_driver.call, "vpairs", nb, nd, san_host.arr(pairs), int(in_place))[0]
+    assert got == want
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.data(), st.sampled_from([1, 2, 4]), st.integers(0, 3), st.sampled_from([4, 8]), st.integers(1, 6))
+def test_sanitized_beam_tails_agree_with_library(san_driver, data, width, groups, bs, mb):
+    from paged_kv_cache_427_amd.cascade import plan_beam_tails, plan_shared_blocks
+    n = width * groups
+    tabs = np.asarray(data.draw(_ints(0, 3, n * mb)), np.int32).reshape(n, mb)
+    lens = np.asarray(data.draw(_ints(-1, mb * bs + 2, n)), np.int32)
+    shared = data.draw(st.one_of(st.just([]), _ints(-1, mb + 1, groups)))
+    st_k, k = _status(plan_shared_blocks, tabs, lens, bs, width)
+    if st_k == 0 and shared:
+        k = np.asarray(shared, np.int32)
+    want = st_k if st_k else _status(plan_beam_tails, tabs, lens, bs, width, k)
+    try:
+        v = san_driver.call("tails", mb, san_host.arr(tabs), san_host.arr(lens), bs, width, san_host.arr(shared))
+    except PaError as e:
+        assert e.status == (want if isinstance(want, int) else want[0])
+        return
+    assert not isinstance(want, int) and want[0] == 0
+    tt, tl = want[1]
+    ks, i = san_host._take(v, 0)
+    assert ks == k.tolist()
+    cap = v[i]
+    flat, i = san_host._take(v, i + 1)
+    assert np.asarray(flat, np.int32).reshape(n, cap).tolist() == tt.tolist()
+    assert san_host._take(v, i)[0] == tl.tolist()
