@@ -52,6 +52,19 @@
 #include "pa_internal.h"
 
 namespace pa {
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return n;
+}
+
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -867,18 +880,6 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_b
   }
   store_out(a.out, oi, lsum > 0.f ? o / lsum * a.v_scale : 0.f, out_bf16 != 0);
   if (a.lse && d == 0) a.lse[orow / D] = (mm + __log2f(lsum)) * 0.6931471805599453f;
-}
-
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
-  return n;
 }
 
 // Workgroups of the persistent grid: one per CU.  Measured on MI355X against three (what the

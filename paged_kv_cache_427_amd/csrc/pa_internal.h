@@ -91,6 +91,8 @@ size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t hea
                               int64_t waves);
 // Waves of one decode launch on the current device (an upper bound for any dtype).
 int decode_max_waves();
+// Compute units of the current device (cached per device; 256 when the query fails).
+int device_cus();
 // Sets the workspace pointers of `a` (num_seqs set) inside a workspace of decode_workspace_bytes().
 void decode_workspace_carve(DecodeArgs& a, void* workspace);
 // The current device's copy of the library's static decode workspace (PA_DECODE_STATIC_WORKSPACE_BYTES):

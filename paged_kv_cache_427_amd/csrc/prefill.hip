@@ -35,6 +35,7 @@
 //    XCD so that they share its L2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "pa_device.h"
@@ -57,6 +58,8 @@ constexpr int kKStride = kD * 2 + 16;    // bytes per K row in LDS (the padding 
 constexpr int kVStride = kKT * 2 + 16;   // bytes per V^T row in LDS
 constexpr int kKBytes = kKT * kKStride;
 constexpr int kVBytes = kD * kVStride;
+constexpr int kOStride = kD * 2 + 16;    // bytes per bf16 output row staged in LDS (8 waves x 32 rows fit the tiles)
+static_assert(8 * 32 * kOStride <= 2 * (kKBytes + kVBytes), "output staging fits the tile buffers");
 constexpr float kRescaleSlack = 8.0f;    // log2 of the largest unrescaled growth
 constexpr int kMaxRanked = 64;           // sequences ordered by length when there are at most this many
 constexpr int kMaxLdsTable = 16384;      // table entries the pipelined kernel holds in LDS (64 KiB)
@@ -304,19 +307,42 @@ struct TileLoader {
   }
 };
 
-// Sequence of length rank r (0 = most keys; ties by index), for num_seqs <= kMaxRanked.  Every wave
-// computes it on its own: lane s ranks sequence s against all others.
-__device__ __forceinline__ int seq_of_rank(const PrefillArgs& a, int r, int lane) {
+// The sequence a workgroup of rank r serves, with its chunk's first query row, chunk length and prior
+// context.  With at most kMaxRanked sequences, rank 0 is the one with the most keys (ties by index):
+// lane s loads sequence s's sizes once and the ranking compares registers across lanes, so the
+// lookup is one round trip to memory.  Larger batches are served in index order.
+struct SeqInfo {
+  int seq, q_base, C, P;
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const PrefillArgs& a, int r, int lane) {
   const int n = a.num_seqs;
-  int mine = -1;
-  if (lane < n) mine = a.prior[lane] + a.qsl[lane + 1] - a.qsl[lane];
-  int rank = 0;
-  for (int s = 0; s < n; ++s) {
-    const int other = a.prior[s] + a.qsl[s + 1] - a.qsl[s];
-    rank += (other > mine) || (other == mine && s < lane);
+  SeqInfo si;
+  if (n <= kMaxRanked) {
+    int q0 = 0, q1 = 0, pr = 0;
+    if (lane < n) {
+      q0 = a.qsl[lane];
+      q1 = a.qsl[lane + 1];
+      pr = a.prior[lane];
+    }
+    const int mine = lane < n ? pr + q1 - q0 : -1;
+    int rank = 0;
+    for (int s = 0; s < n; ++s) {
+      const int other = __builtin_amdgcn_readlane(mine, s);
+      rank += (other > mine) || (other == mine && s < lane);
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < n && rank == r);
+    si.seq = hit ? static_cast<int>(__builtin_ctzll(hit)) : 0;
+    si.q_base = __builtin_amdgcn_readlane(q0, si.seq);
+    si.C = __builtin_amdgcn_readlane(q1, si.seq) - si.q_base;
+    si.P = __builtin_amdgcn_readlane(pr, si.seq);
+  } else {
+    si.seq = r;
+    si.q_base = a.qsl[r];
+    si.C = a.qsl[r + 1] - si.q_base;
+    si.P = a.prior[r];
   }
-  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < n && rank == r);
-  return hit ? static_cast<int>(__builtin_ctzll(hit)) : 0;
+  return si;
 }
 
 template <int KV, int BS, int G, int W>
@@ -348,12 +374,10 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) prefill_kernel(Prefill
     kvh = rr % a.num_kv_heads;
   }
   if (rank >= a.num_seqs) return;
-  const int seq = a.num_seqs <= kMaxRanked ? seq_of_rank(a, rank, lane) : rank;
-  const int q_base = a.qsl[seq];
-  const int C = a.qsl[seq + 1] - q_base;
+  const SeqInfo si = seq_info(a, rank, lane);
+  const int seq = si.seq, q_base = si.q_base, C = si.C, P = si.P;
   const int q0 = qt * QT;
   if (q0 >= C) return;
-  const int P = a.prior[seq];
   const int q_end = min(q0 + QT, C);
   const int n_keys = P + q_end;
   const int n_tiles = (n_keys + kKT - 1) / kKT;
@@ -573,28 +597,60 @@ __global__ void __launch_bounds__(64 * W, 1) prefill_pipe_kernel(PrefillArgs a, 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  int rank, kvh, qt;
-  if (xcd_remap) {
-    const int x = blockIdx.x % 8;
-    const int j = blockIdx.x / 8;
-    qt = num_qtiles - 1 - j % num_qtiles;
-    const int rr = j / num_qtiles;
-    const int hpx = a.num_kv_heads / 8;
-    rank = rr / hpx;
-    kvh = (rr % hpx) * 8 + x;
-  } else {
-    qt = num_qtiles - 1 - blockIdx.x % num_qtiles;
-    const int rr = blockIdx.x / num_qtiles;
-    rank = rr / a.num_kv_heads;
-    kvh = rr % a.num_kv_heads;
+  // Lane s of every wave holds sequence s's chunk start, chunk end, prior context and, for a batch
+  // of at most kMaxRanked sequences, its rank by key count (0 = most keys, ties by index): one round
+  // trip to memory for the whole workgroup, and each item's lookup is then register-only.
+  const int n_seqs = a.num_seqs;
+  const bool ranked = n_seqs <= kMaxRanked;
+  int s_q0 = 0, s_q1 = 0, s_pr = 0, s_rank = -1;
+  if (ranked) {
+    if (lane < n_seqs) {
+      s_q0 = a.qsl[lane];
+      s_q1 = a.qsl[lane + 1];
+      s_pr = a.prior[lane];
+    }
+    const int mine = lane < n_seqs ? s_pr + s_q1 - s_q0 : -1;
+    int rk = 0;
+    for (int s2 = 0; s2 < n_seqs; ++s2) {
+      const int other = __builtin_amdgcn_readlane(mine, s2);
+      rk += (other > mine) || (other == mine && s2 < lane);
+    }
+    s_rank = lane < n_seqs ? rk : -1;
   }
-  if (rank >= a.num_seqs) return;
-  const int seq = a.num_seqs <= kMaxRanked ? seq_of_rank(a, rank, lane) : rank;
-  const int q_base = a.qsl[seq];
-  const int C = a.qsl[seq + 1] - q_base;
+  // The item list (rank, KV head, query tile), ranks in order and the longest query tile first: with
+  // the XCD remap, workgroup i serves the KV heads congruent to i % 8 (the XCD it runs on), so the
+  // items of one (sequence, KV head) share that XCD's L2.  The nb workgroups of a list take its
+  // items in snake order: round R gives item R nb + b to workgroup b (R even) or to nb - 1 - b (R
+  // odd), which evens out the decreasing sizes along the list without any shared counter.
+  const int xq = xcd_remap ? static_cast<int>(blockIdx.x % 8) : 0;
+  const int nb = xcd_remap ? static_cast<int>(gridDim.x / 8) : static_cast<int>(gridDim.x);
+  const int wb = xcd_remap ? static_cast<int>(blockIdx.x / 8) : static_cast<int>(blockIdx.x);
+  const int heads = xcd_remap ? a.num_kv_heads / 8 : a.num_kv_heads;
+  const int64_t n_items = static_cast<int64_t>(n_seqs) * heads * num_qtiles;
+
+#pragma unroll 1
+  for (int R = 0;; ++R) {
+  const int64_t item = static_cast<int64_t>(R) * nb + ((R & 1) ? nb - 1 - wb : wb);
+  if (item >= n_items) break;
+  const int qt = num_qtiles - 1 - static_cast<int>(item % num_qtiles);
+  const int64_t grp = item / num_qtiles;   // (rank, KV head of the list)
+  const int rank = static_cast<int>(grp / heads);
+  const int kvh = xcd_remap ? static_cast<int>(grp % heads) * 8 + xq : static_cast<int>(grp % heads);
+  int seq, q_base, C, P;
+  if (ranked) {
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(s_rank == rank);
+    seq = hit ? static_cast<int>(__builtin_ctzll(hit)) : 0;
+    q_base = __builtin_amdgcn_readlane(s_q0, seq);
+    C = __builtin_amdgcn_readlane(s_q1, seq) - q_base;
+    P = __builtin_amdgcn_readlane(s_pr, seq);
+  } else {
+    seq = rank;
+    q_base = a.qsl[rank];
+    C = a.qsl[rank + 1] - q_base;
+    P = a.prior[rank];
+  }
   const int q0 = qt * QT;
-  if (q0 >= C) return;
-  const int P = a.prior[seq];
+  if (q0 >= C) continue;
   const int q_end = min(q0 + QT, C);
   const int n_keys = P + q_end;
   const int n_tiles = (n_keys + kKT - 1) / kKT;
@@ -775,14 +831,22 @@ __global__ void __launch_bounds__(64 * W, 1) prefill_pipe_kernel(PrefillArgs a, 
   };
 
   // Prologue: S(0) from K(0); K(1) in kbuf1; V(-1) = zeros in vbuf1 with P(-1) = 0 (O(-1) adds 0);
-  // the register stage then holds K(2) and V(0).
+  // the register stage then holds K(2) and V(0).  K(0), V(0) and K(1) are loaded together (K(1)
+  // through a second register stage), then K(2), so the prologue waits on memory twice.
   __syncthreads();   // the table in LDS
-  ld.load_k(kpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
-  ld.load_v(vpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
-  ld.store_k(kbuf0, wave, lane);
-  ld.load_k(kpool, tab, blk_stride, head_off, min(1, last) * kKT, n_keys, wave, lane);
-  for (int i = threadIdx.x; i < kVBytes / 16; i += 64 * W)
-    reinterpret_cast<uint4*>(vbuf1)[i] = make_uint4(0, 0, 0, 0);
+  {
+    TileLoader<KV, BS, W> ld1;
+    ld1.max_blocks = a.max_blocks;
+    ld1.pool_blocks = a.num_blocks;
+    ld.load_k(kpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+    ld.load_v(vpool, tab, blk_stride, head_off, 0, n_keys, wave, lane);
+    ld1.load_k(kpool, tab, blk_stride, head_off, min(1, last) * kKT, n_keys, wave, lane);
+    for (int i = threadIdx.x; i < kVBytes / 16; i += 64 * W)
+      reinterpret_cast<uint4*>(vbuf1)[i] = make_uint4(0, 0, 0, 0);
+    ld.store_k(kbuf0, wave, lane);
+    ld.load_k(kpool, tab, blk_stride, head_off, min(2, last) * kKT, n_keys, wave, lane);
+    ld1.store_k(kbuf1, wave, lane);
+  }
   __syncthreads();
   f32x16 sa[2], sb2[2];
 #pragma unroll
@@ -795,9 +859,7 @@ __global__ void __launch_bounds__(64 * W, 1) prefill_pipe_kernel(PrefillArgs a, 
       sa[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(krow + 32 * c), qb[c],
                                                        sa[sb], 0, 0, 0);
   }
-  ld.store_k(kbuf1, wave, lane);
-  ld.load_k(kpool, tab, blk_stride, head_off, min(2, last) * kKT, n_keys, wave, lane);
-  __syncthreads();
+  __syncthreads();   // every wave's S(0) has read kbuf0 before the first step overwrites it
 
   uint32_t pA[4][4], pB[4][4];
 #pragma unroll
@@ -838,25 +900,48 @@ __global__ void __launch_bounds__(64 * W, 1) prefill_pipe_kernel(PrefillArgs a, 
     }
   }
 
-  if (!row_ok) return;
   const float l = half_sum(l_lane);
   const float inv = l > 0.f ? a.v_scale / l : 0.f;
-  const int64_t obase = (static_cast<int64_t>(q_base + qi) * a.num_q_heads + head) * kD;
+  if (out_bf16) {
+    // bf16 rows leave through LDS so that every store writes whole rows: wave w stages its 32 rows
+    // [row][dim] (stride kOStride) in its own slice of the tile buffers, once every wave's last
+    // products have read them, and stores 4 rows x 256 B per instruction.
+    __syncthreads();
+    char* const ost = smem + wave * (32 * kOStride);
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int d = dt * 32 + 8 * rr + 4 * h;
-      const float x0 = o[dt][4 * rr] * inv, x1 = o[dt][4 * rr + 1] * inv;
-      const float x2 = o[dt][4 * rr + 2] * inv, x3 = o[dt][4 * rr + 3] * inv;
-      if (out_bf16) {
-        uint16_t* op = static_cast<uint16_t*>(a.out) + obase + d;
-        *reinterpret_cast<uint2*>(op) = make_uint2(f32_to_bf16_bits(x0) | (f32_to_bf16_bits(x1) << 16),
-                                                   f32_to_bf16_bits(x2) | (f32_to_bf16_bits(x3) << 16));
-      } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d) = make_float4(x0, x1, x2, x3);
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d = dt * 32 + 8 * rr + 4 * h;
+        *reinterpret_cast<uint2*>(ost + (lane & 31) * kOStride + 2 * d) =
+            make_uint2(f32_to_bf16_bits(o[dt][4 * rr] * inv) | (f32_to_bf16_bits(o[dt][4 * rr + 1] * inv) << 16),
+                       f32_to_bf16_bits(o[dt][4 * rr + 2] * inv) | (f32_to_bf16_bits(o[dt][4 * rr + 3] * inv) << 16));
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int wr = 4 * j + (lane >> 4);            // row of the wave
+      const int srow = wave * 32 + wr;
+      const int sq = q0 + srow % QT;
+      const uint4 w = *reinterpret_cast<const uint4*>(ost + wr * kOStride + 16 * (lane & 15));
+      if (sq < C) {
+        uint16_t* op = static_cast<uint16_t*>(a.out) +
+                       (static_cast<int64_t>(q_base + sq) * a.num_q_heads + kvh * G + srow / QT) * kD;
+        *reinterpret_cast<uint4*>(op + 8 * (lane & 15)) = w;
       }
     }
+  } else if (row_ok) {
+    const int64_t obase = (static_cast<int64_t>(q_base + qi) * a.num_q_heads + head) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d = dt * 32 + 8 * rr + 4 * h;
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d) =
+            make_float4(o[dt][4 * rr] * inv, o[dt][4 * rr + 1] * inv, o[dt][4 * rr + 2] * inv,
+                        o[dt][4 * rr + 3] * inv);
+      }
+  }
+  }   // items
 }
 
 template <int KV, int BS, int G, int W>
@@ -874,14 +959,28 @@ int launch_g(const PrefillArgs& a, int out_bf16, hipStream_t s) {
   // and its bf16 instances spill.
   if constexpr (W == 8) {
     if (a.max_blocks <= kMaxLdsTable) {
-      static bool attr_set = false;
-      if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pipe_kernel<KV, BS, G, W>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsTable * 4);
+      constexpr int kMaxDevices = 64;
+      static bool attr_set[kMaxDevices] = {};
+      int dev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return static_cast<int>(e);
+      if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pipe_kernel<KV, BS, G, W>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsTable * 4);
         if (e != hipSuccess) return static_cast<int>(e);
-        attr_set = true;
+        if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
       }
-      hipLaunchKernelGGL((prefill_pipe_kernel<KV, BS, G, W>), dim3(static_cast<unsigned>(wgs)), dim3(64 * W),
+      // persistent: one workgroup per compute unit (what the registers allow), each walking its
+      // share of the item list; never more workgroups than items
+      const int64_t cus = device_cus();
+      int64_t grid;
+      if (xcd_remap) {
+        const int64_t per_list = static_cast<int64_t>(a.num_seqs) * (a.num_kv_heads / 8) * num_qtiles;
+        grid = 8 * std::max<int64_t>(1, std::min<int64_t>(cus / 8, per_list));
+      } else {
+        grid = std::max<int64_t>(1, std::min<int64_t>(cus, wgs));
+      }
+      hipLaunchKernelGGL((prefill_pipe_kernel<KV, BS, G, W>), dim3(static_cast<unsigned>(grid)), dim3(64 * W),
                          tab_bytes, s, a, out_bf16, num_qtiles, xcd_remap);
       return static_cast<int>(hipGetLastError());
     }
