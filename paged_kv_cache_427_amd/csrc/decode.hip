@@ -766,120 +766,124 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
   }
 }
 
-// Merge of the partial records of every (sequence, query head) whose segment was split into
-// pieces: out = sum_r o_r 2^(m_r - M) / sum_r l_r 2^(m_r - M) * v_scale, M = max_r m_r.  Segments
-// served by one piece were written by the stream kernel; empty sequences (L = 0) get zeros here.
-// The records of partition k are those of the shares v0(k)..v1(k) that overlap it.  The workgroup
-// lists them in LDS (a scan of per-partition counts), reads every (m, l) at once, and then each
-// thread (one output dim) sums its dim over the records with many loads in flight.
-constexpr int kMergeMaxRec = 1024;
+// Merge of the partial records of the segments that were split into pieces:
+// out = sum_r o_r 2^(m_r - M) / sum_r l_r 2^(m_r - M) * v_scale, M = max_r m_r.  One wave per
+// (sequence, query head) row, four rows per workgroup: a row whose segment was served by one piece
+// (written by the stream kernel) leaves after reading the plan; an empty one gets zeros (and a -inf
+// log-sum-exp); a split one is merged with its records loaded across the lanes, 64 at a time (the
+// maximum and weighted sum are wave reductions), and each lane then adds its slice of the output
+// dims over the records with many loads in flight.  The records of partition k are those of the
+// shares v0(k)..v1(k) that overlap it, read in that order, so results do not depend on timing.
+constexpr int kMergeThreads = 256;
 
 template <int D>
-__global__ void __launch_bounds__(D) decode_merge_kernel(DecodeArgs a, int out_bf16) {
-  __shared__ int64_t rec_s[kMergeMaxRec];   // record offsets (floats into ws_part)
-  __shared__ float w_s[kMergeMaxRec];       // 2^(m_r - M)
-  __shared__ int scan_s[D];
-  __shared__ float red_s[D];
+__global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a, int out_bf16) {
+  constexpr int DPL = D / 64;   // output dims per lane
+  const int lane = threadIdx.x & 63;
+  // workgroup i serves stream i % streams (with 8 streams, the XCD whose stream kernel workgroups
+  // wrote that stream's records, so they are read from its L2); its rows are numbered
+  // (head slot, sequence, head in the group) with the head fastest
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int h = blockIdx.x % a.num_q_heads;
-  const int seq = blockIdx.x / a.num_q_heads;
-  const int kvh = h / G, g = h % G;
-  const int d = threadIdx.x;
+  const int x = static_cast<int>(blockIdx.x % a.streams);
+  const int64_t q = static_cast<int64_t>(blockIdx.x / a.streams) * (kMergeThreads / 64) + (threadIdx.x >> 6);
+  const int hpx = a.num_kv_heads / a.streams;
+  if (q >= static_cast<int64_t>(hpx) * a.num_seqs * G) return;
+  const int g = static_cast<int>(q % G);
+  const int seq = static_cast<int>((q / G) % a.num_seqs);
+  const int hh = static_cast<int>(q / (static_cast<int64_t>(G) * a.num_seqs));
+  const int kvh = hh * a.streams + x;
   const ro_i32 pref = ro(a.ws_pref);
   const int n = a.num_seqs;
   const int nj = pref[seq + 1] - pref[seq];
   const int64_t orow = seq * a.o_sseq + kvh * a.o_skv + g * a.o_sg;
-  const int64_t oi = orow + d;
   if (nj == 0) {
-    store_out(a.out, oi, 0.f, out_bf16 != 0);
-    if (a.lse && d == 0) a.lse[orow / D] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) store_out(a.out, orow + DPL * lane + e, 0.f, out_bf16 != 0);
+    if (a.lse && lane == 0) a.lse[orow / D] = -INFINITY;
     return;
   }
-  const int x = kvh % a.streams, hh = kvh / a.streams;
   Sched sc;
   sc.S = ro(a.ws_sched)[0];
   sc.V = ro(a.ws_sched)[1];
   const int P0 = hh * pref[n] + pref[seq];   // stream position of the segment's first unit
   const int PU = a.part_tokens / kUnit;
   const int nparts = (nj + PU - 1) / PU;
-  if (nparts == 1 && sc.share_of(P0) == sc.share_of(P0 + nj - 1)) return;
+  if (nparts == 1 && sc.share_of(P0) == sc.share_of(P0 + nj - 1)) return;   // one piece
   const int64_t seg = (static_cast<int64_t>(hh) * n + seq) * a.max_parts + x * a.stream_slots;
-  auto rec_of = [&](int k, int v) { return ((seg + k + v) * G + g) * (D + 4); };
-
-  // ---- list the records: thread t owns partitions [t * ch, (t + 1) * ch) ----
-  const int ch = (nparts + D - 1) / D;
-  const int k0 = min(d * ch, nparts), k1 = min(k0 + ch, nparts);
-  int cnt = 0;
-  for (int k = k0; k < k1; ++k)
-    cnt += sc.share_of(P0 + min((k + 1) * PU, nj) - 1) - sc.share_of(P0 + k * PU) + 1;
-  scan_s[d] = cnt;
-  __syncthreads();
-  for (int off = 1; off < D; off *= 2) {
-    const int v = d >= off ? scan_s[d - off] : 0;
-    __syncthreads();
-    scan_s[d] += v;
-    __syncthreads();
+  auto rec_of = [&](int k, int vv) { return ((seg + k + vv) * G + g) * (D + 4); };
+  float M = -INFINITY, lsum = 0.f, o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  // pieces in order, walked without divisions: piece (k, vv) ends at the nearer of partition k's
+  // end pe and share vv's end nb
+  int k = 0, vv = sc.share_of(P0);
+  int pe = P0 + min(PU, nj), nb = (vv + 1) * sc.S;
+  const int seg_end = P0 + nj;
+  while (k < nparts) {
+    int64_t my_off = 0;
+    int cnt = 0;
+    for (; cnt < 64 && k < nparts; ++cnt) {
+      if (lane == cnt) my_off = rec_of(k, vv);
+      const int e = min(pe, nb);
+      if (e == nb) {
+        ++vv;
+        nb += sc.S;
+      }
+      if (e == pe) {
+        ++k;
+        pe = min(pe + PU, seg_end);
+      }
+    }
+    const float m_r = lane < cnt ? a.ws_part[my_off] : -INFINITY;
+    const float l_r = lane < cnt ? a.ws_part[my_off + 1] : 0.f;
+    float mb = m_r;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mb = fmaxf(mb, shfl_xor(mb, off));
+    const float Mn = fmaxf(M, mb);
+    const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    const float w_r = lane < cnt ? __builtin_amdgcn_exp2f(m_r - Mn) : 0.f;
+    float ls = l_r * w_r;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ls += shfl_xor(ls, off);
+    lsum = lsum * alpha + ls;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] *= alpha;
+    const uint32_t off_lo = static_cast<uint32_t>(my_off), off_hi = static_cast<uint32_t>(my_off >> 32);
+    const uint32_t w_bits = __builtin_bit_cast(uint32_t, w_r);
+    // up to kFly records' loads in flight at a time (slots past cnt load nothing)
+    constexpr int kFly = 16;
+    for (int c0 = 0; c0 < cnt; c0 += kFly) {
+      float val[kFly][DPL], wt[kFly];
+#pragma unroll
+      for (int j = 0; j < kFly; ++j) {
+        wt[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) val[j][e] = 0.f;
+        if (c0 + j < cnt) {
+          const int c = c0 + j;
+          const int64_t r = (static_cast<int64_t>(__builtin_amdgcn_readlane(off_hi, c)) << 32) |
+                            __builtin_amdgcn_readlane(off_lo, c);
+          wt[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(w_bits, c));
+          if constexpr (DPL == 2) {
+            const float2 t = *reinterpret_cast<const float2*>(a.ws_part + r + 4 + 2 * lane);
+            val[j][0] = t.x;
+            val[j][1] = t.y;
+          } else {
+            val[j][0] = a.ws_part[r + 4 + lane];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kFly; ++j)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] += val[j][e] * wt[j];
+    }
+    M = Mn;
   }
-  const int R = scan_s[D - 1];
-  if (R <= kMergeMaxRec) {
-    int r = scan_s[d] - cnt;
-    for (int k = k0; k < k1; ++k) {
-      const int v0 = sc.share_of(P0 + k * PU), v1 = sc.share_of(P0 + min((k + 1) * PU, nj) - 1);
-      for (int v = v0; v <= v1; ++v) rec_s[r++] = rec_of(k, v);
-    }
-    __syncthreads();
-    // ---- maximum and weighted sum of the partial sums ----
-    float mm = -INFINITY;
-    for (int q = d; q < R; q += D) {
-      const float m = a.ws_part[rec_s[q]];
-      w_s[q] = m;
-      mm = fmaxf(mm, m);
-    }
-    red_s[d] = mm;
-    __syncthreads();
-    for (int off = D / 2; off > 0; off /= 2) {
-      if (d < off) red_s[d] = fmaxf(red_s[d], red_s[d + off]);
-      __syncthreads();
-    }
-    const float M = red_s[0];
-    __syncthreads();
-    float ls = 0.f;
-    for (int q = d; q < R; q += D) {
-      const float w = __builtin_amdgcn_exp2f(w_s[q] - M);
-      w_s[q] = w;
-      ls += a.ws_part[rec_s[q] + 1] * w;
-    }
-    red_s[d] = ls;
-    __syncthreads();
-    for (int off = D / 2; off > 0; off /= 2) {
-      if (d < off) red_s[d] += red_s[d + off];
-      __syncthreads();
-    }
-    const float lsum = red_s[0];
-    // ---- this thread's output dim ----
-    float o = 0.f;
-#pragma unroll 8
-    for (int q = 0; q < R; ++q) o += a.ws_part[rec_s[q] + 4 + d] * w_s[q];
-    store_out(a.out, oi, lsum > 0.f ? o / lsum * a.v_scale : 0.f, out_bf16 != 0);
-    if (a.lse && d == 0) a.lse[orow / D] = (M + __log2f(lsum)) * 0.6931471805599453f;
-    return;
-  }
-  // more records than the LDS list holds: one pass with a running maximum
-  float mm = -INFINITY, lsum = 0.f, o = 0.f;
-  for (int k = 0; k < nparts; ++k) {
-    const int v0 = sc.share_of(P0 + k * PU), v1 = sc.share_of(P0 + min((k + 1) * PU, nj) - 1);
-    for (int v = v0; v <= v1; ++v) {
-      const float* rec = a.ws_part + rec_of(k, v);
-      const float m = rec[0], l = rec[1], y = rec[4 + d];
-      const float mn = fmaxf(mm, m);
-      const float fo = __builtin_amdgcn_exp2f(mm - mn), fn = __builtin_amdgcn_exp2f(m - mn);
-      lsum = lsum * fo + l * fn;
-      o = o * fo + y * fn;
-      mm = mn;
-    }
-  }
-  store_out(a.out, oi, lsum > 0.f ? o / lsum * a.v_scale : 0.f, out_bf16 != 0);
-  if (a.lse && d == 0) a.lse[orow / D] = (mm + __log2f(lsum)) * 0.6931471805599453f;
+  const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) store_out(a.out, orow + DPL * lane + e, o[e] * inv, out_bf16 != 0);
+  if (a.lse && lane == 0) a.lse[orow / D] = (M + __log2f(lsum)) * 0.6931471805599453f;
 }
 
 // Workgroups of the persistent grid: one per CU.  Measured on MI355X against three (what the
@@ -918,8 +922,10 @@ int launch_one(const DecodeArgs& a0, int out_bf16, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return static_cast<int>(e);
   if (a.fill_empty) return 0;
-  const int64_t rw = static_cast<int64_t>(a.num_q_heads) * a.num_seqs;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<unsigned>(rw)), dim3(D), 0, s, a, out_bf16);
+  const int64_t rows = static_cast<int64_t>(a.num_q_heads / a.streams) * a.num_seqs;   // per stream
+  const int64_t mw = a.streams * ((rows + kMergeThreads / 64 - 1) / (kMergeThreads / 64));   // a wave per row
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<unsigned>(mw)), dim3(kMergeThreads), 0, s, a,
+                     out_bf16);
   return static_cast<int>(hipGetLastError());
 }
 
