@@ -95,9 +95,10 @@ def test_batches_at_the_plan_limits(n):
 
 
 @pytest.mark.parametrize("partition", [32, 512])
-def test_more_pieces_than_the_merge_lists_in_lds(partition):
-    """Two long contexts cut every 32 tokens: over 1024 pieces per (sequence, head), merged by the
-    merge kernel's one-pass fallback (and, for comparison, the same contexts cut every 512)."""
+def test_rows_of_many_pieces(partition):
+    """Two long contexts cut every 32 tokens: over 1024 pieces per (sequence, head), which the merge
+    kernel combines 64 records at a time with a running maximum across the batches (and, for
+    comparison, the same contexts cut every 512: about 70 pieces, two batches)."""
     rng = np.random.Generator(np.random.PCG64(4272))
     gen = torch.Generator().manual_seed(4272)
     hq, hkv, b, d = 2, 1, 16, 128

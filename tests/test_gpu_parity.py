@@ -219,6 +219,27 @@ def test_prefill_variants(kv, hq, hkv, b):
     assert _out_err(si.dec_out, ref.decode_out) <= TOL[kv]
 
 
+def test_prefill_persistent_item_walk():
+    """256-row prefill tiles walked by the persistent workgroups: more sequences (70) than the ranked
+    order takes, so items go in index order; 16 KV heads, two per XCD's list; groups of 8; ragged
+    chunks and priors; about 17 items per workgroup."""
+    from synth.workloads import mixed_workload
+    rng = np.random.Generator(np.random.PCG64(11))
+    gen = torch.Generator().manual_seed(11)
+    n = 70
+    prior = rng.integers(0, 90, n).tolist()
+    chunk = rng.integers(1, 129, n).tolist()
+    chunk[0] = 128                                  # 128 queries x 8 heads fill 1024 rows: 8-wave tiles
+    wl = mixed_workload("mixed_fp8", "small", rng, gen, "cpu", hq=128, hkv=16, d=128, b=16, kv="fp8",
+                        prior=prior, chunk=chunk, dlens=[9])
+    _say("prefill persistent walk", n, "sequences")
+    ref = run_paged(wl)
+    eng, si = _run(wl)
+    err = _out_err(si.pre_out, ref.prefill_out)
+    _say("prefill persistent walk max err", err)
+    assert err <= TOL["fp8"]
+
+
 # ---- full-size workloads against the pool-free dense oracle --------------------------------------
 
 FULL = [("llama7b_bf16", None), ("shared_prefix_bf16", None), ("gqa_long_bf16", None), ("mixed_fp8", None),
