@@ -1,8 +1,8 @@
 """GPU parity of pa_decode at the edges of its work plan: the largest batch the stream kernel plans
 itself (4096 sequences), the smallest one planned by the plan kernel (4097, prefix searched in LDS),
-more sequences than the plan kernel ranks in LDS (more than 8192), and more pieces per (sequence,
-head) than the merge kernel lists in LDS (1024), each against the fp64 oracle on sampled or all
-outputs (bf16 tolerance 2e-2)."""
+more sequences than the plan kernel ranks in LDS (more than 8192), and rows of over 1024 pieces per
+(sequence, head), which the merge kernel combines in several batches of records, each against the
+fp64 oracle on sampled or all outputs (bf16 tolerance 2e-2)."""
 import numpy as np
 import pytest
 import torch
