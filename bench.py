@@ -486,11 +486,27 @@ def copy_probe(args, dev, res) -> None:
     gbs = 2 * n * 4 / (float(np.median(times[1:])) * 1e-3) / 1e9
     res["hbm_achievable"] = {"GBps": round(gbs, 1), "kernel": "device copy (torch copy_), read + write bytes",
                              "bytes_per_copy": 2 * n * 4, "copies_timed": len(times) - 1}
+    # read-only probe: the library's streaming read of the same buffer (16-byte loads, nothing written)
+    from paged_kv_cache_427_amd.ops import pa_hbm_read_probe
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    rtimes = []
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pa_hbm_read_probe(src, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rtimes.append(e0.elapsed_time(e1))
+    rgbs = n * 4 / (float(np.median(rtimes[1:])) * 1e-3) / 1e9
+    res["hbm_read_achievable"] = {"GBps": round(rgbs, 1), "kernel": "pa_hbm_read_probe (streaming 16-byte loads), bytes read",
+                                  "bytes_per_read": n * 4, "reads_timed": len(rtimes) - 1}
     for key in ("roofline",):
         r = res.get(key)
         if r and r.get("bound") == "hbm":
             r["achievable_peak"] = round(gbs, 1)
             r["frac_of_achievable"] = round(r["achieved"] / gbs, 4)
+            r["read_achievable_peak"] = round(rgbs, 1)
+            r["frac_of_read_achievable"] = round(r["achieved"] / rgbs, 4)
     del src, dst
 
 

@@ -275,6 +275,18 @@ pa_status pa_decode_noalloc(const void* q, int32_t q_dtype, const int64_t* q_str
                             const int32_t* shared_blocks, pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * pa_plan_cache_hint (host) -- the shared_blocks hint of pa_decode_ex for a batch: for each
+ * sequence, the length of the leading run of its table entries (within its ceil(lens[s] /
+ * block_size) used ones) whose physical block another used entry of the batch also names, i.e.
+ * the blocks of a shared prefix that several rows read ([day28] §六 question 3; [exp]
+ * 「PagedAttention：向操作系统借思路」 on sharing blocks between sequences).  tables host int32
+ * [num_seqs][max_blocks], lens host int32 [num_seqs], shared_blocks host int32 [num_seqs] (out).
+ * PA_ERR_INVALID on a negative size or length, or a length needing more than max_blocks entries.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_plan_cache_hint(const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t num_seqs,
+                             int32_t block_size, int32_t* shared_blocks);
+
+/* ---------------------------------------------------------------------------------------------
  * pa_plan_shared_blocks (host) -- for a decode batch laid out as groups of `width` consecutive
  * sequences (the branches of one request), the number of leading blocks every member of group g
  * shares: shared_blocks[g] = the longest k such that all members have the same first k table
@@ -343,6 +355,19 @@ pa_status pa_validate_pairs(const pa_pool_desc* src_pool, const pa_pool_desc* ds
  * the same conversion the attention kernels use (NaN codes give NaN).  out: device float [256].
  * ------------------------------------------------------------------------------------------- */
 pa_status pa_fp8_decode_table(float* out, pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_hbm_read_probe -- measurement aid: streams `bytes` of device memory at buf once with 16-byte
+ * non-temporal loads (32 workgroups per compute unit, four loads in flight per thread), so that
+ * its time gives the read bandwidth this device reaches with plain streaming loads: the practical
+ * ceiling against which a bandwidth-bound kernel's achieved GB/s is read (the pages expect paged
+ * attention to cost little against a contiguous layout: [day28] §七).  buf: device pointer,
+ * 16-byte aligned; bytes: a positive multiple of 16.  sink: device pointer to one uint32 that the
+ * kernel writes only if the data folds to a value it never takes in practice (it keeps the loads
+ * from being removed; its content afterwards is unspecified).  PA_ERR_INVALID on a null pointer,
+ * misalignment or a size that is not a positive multiple of 16.
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_hbm_read_probe(const void* buf, size_t bytes, void* sink, pa_stream stream);
 
 /* =============================================================================================
  * Host block allocator (no GPU).  [ch7] 7.1 「三个关键机制」; [exp] PagedAttention section;

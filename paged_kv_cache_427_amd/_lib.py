@@ -47,6 +47,7 @@ _PROTOS = {
     "pa_merge_states": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_int32,
                                   c_void_p, c_void_p]),
     "pa_plan_shared_blocks": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, c_int32, _I32P]),
+    "pa_plan_cache_hint": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, _I32P]),
     "pa_plan_beam_tails": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, c_int32, _I32P, _I32P, c_int32, _I32P,
                                      _I32P]),
     "pa_validate_decode": (c_int32, [POINTER(PoolDesc), _I32P, c_int32, _I32P, c_int32, c_int32]),
@@ -66,6 +67,7 @@ _PROTOS = {
                                    c_int32, c_void_p, c_void_p, c_int32, c_int32, c_float, c_int32,
                                    c_void_p, c_int32, c_void_p]),
     "pa_fp8_decode_table": (c_int32, [c_void_p, c_void_p]),
+    "pa_hbm_read_probe": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "pa_alloc_create": (c_int32, [c_int32, c_int32, _I32P, POINTER(c_void_p)]),
     "pa_alloc_destroy": (None, [c_void_p]),
     "pa_alloc_add_seq": (c_int32, [c_void_p, c_int64]),

@@ -415,6 +415,31 @@ pa_status pa_alloc_move_seq(pa_allocator* src, pa_allocator* dst, int64_t id, in
   return pa_ok();
 }
 
+pa_status pa_plan_cache_hint(const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t num_seqs,
+                             int32_t block_size, int32_t* shared_blocks) {
+  if (num_seqs < 0 || max_blocks < 0 || block_size < 1)
+    return pa_fail(PA_ERR_INVALID, "pa_plan_cache_hint: negative size or block_size < 1");
+  if (num_seqs == 0) return pa_ok();
+  if (!tables || !lens || !shared_blocks) return pa_fail(PA_ERR_INVALID, "pa_plan_cache_hint: null argument");
+  // used entries of every row, then how many times each physical block is named
+  std::unordered_map<int32_t, int32_t> uses;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (lens[s] < 0) return pa_fail(PA_ERR_INVALID, "pa_plan_cache_hint: negative length");
+    const int64_t nb = (static_cast<int64_t>(lens[s]) + block_size - 1) / block_size;
+    if (nb > max_blocks) return pa_fail(PA_ERR_INVALID, "pa_plan_cache_hint: a length needs more than max_blocks entries");
+    const int32_t* row = tables + static_cast<int64_t>(s) * max_blocks;
+    for (int64_t j = 0; j < nb; ++j) ++uses[row[j]];
+  }
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t nb = (static_cast<int64_t>(lens[s]) + block_size - 1) / block_size;
+    const int32_t* row = tables + static_cast<int64_t>(s) * max_blocks;
+    int64_t k = 0;
+    while (k < nb && uses[row[k]] > 1) ++k;
+    shared_blocks[s] = static_cast<int32_t>(k);
+  }
+  return pa_ok();
+}
+
 pa_status pa_plan_shared_blocks(const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t num_seqs,
                                 int32_t block_size, int32_t width, int32_t* shared_blocks) {
   if (!shared_blocks || (num_seqs > 0 && (!tables || !lens)))

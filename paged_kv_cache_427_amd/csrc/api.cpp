@@ -438,4 +438,13 @@ pa_status pa_fp8_decode_table(float* out, pa_stream stream) {
   return launch_status(pa::launch_fp8_table(out, stream), "pa_fp8_decode_table");
 }
 
+pa_status pa_hbm_read_probe(const void* buf, size_t bytes, void* sink, pa_stream stream) {
+  if (!buf || !sink) return pa_fail(PA_ERR_INVALID, "pa_hbm_read_probe: null pointer");
+  if (bytes == 0 || bytes % 16 != 0) return pa_fail(PA_ERR_INVALID, "pa_hbm_read_probe: bytes must be a positive multiple of 16");
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return pa_fail(PA_ERR_INVALID, "pa_hbm_read_probe: buf is not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return pa_fail(PA_ERR_INVALID, "pa_hbm_read_probe: sink is not 4-byte aligned");
+  return launch_status(pa::launch_read_probe(buf, static_cast<int64_t>(bytes / 16), static_cast<uint32_t*>(sink), stream),
+                       "pa_hbm_read_probe");
+}
+
 }  // extern "C"

@@ -11,6 +11,8 @@
 // that the tokens of one block land side by side in each dim row.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -213,6 +215,39 @@ int launch_copy_blocks(const CopyBlocksArgs& a, void* stream) {
   if (splits > 64) splits = 64;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.num_pairs, 2 * a.num_layers, splits), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
+}
+
+namespace {
+// Streaming read of n16 16-byte pieces: each thread takes four pieces per round (grid-stride,
+// non-temporal loads), XORs them into a register, and stores only if the fold hits a value it
+// practically never takes.  Measured on MI355X over 2 GiB: 8 workgroups per CU 5.4 TB/s with
+// ordinary loads, 5.8 non-temporal; 32 per CU (four times what fits at once) 6.1-6.3.
+__global__ void __launch_bounds__(kThreads) read_probe_kernel(const uint4* p, int64_t n16, uint32_t* sink) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    u32x4 r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = __builtin_nontemporal_load(q + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc ^= r[k].x ^ r[k].y ^ r[k].z ^ r[k].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = __builtin_nontemporal_load(q + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+}  // namespace
+
+int launch_read_probe(const void* buf, int64_t n16, uint32_t* sink, void* stream) {
+  const int64_t wgs = std::min<int64_t>(static_cast<int64_t>(device_cus()) * 32, (n16 + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(std::max<int64_t>(wgs, 1))), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf), n16, sink);
   return static_cast<int>(hipGetLastError());
 }
 

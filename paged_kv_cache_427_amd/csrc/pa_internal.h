@@ -138,5 +138,6 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, int q_dtype, int out_dtype,
 int launch_prefill(const PrefillArgs& a, int kv_dtype, int out_dtype, int block_size, int head_dim,
                    void* stream);
 int launch_fp8_table(float* out, void* stream);
+int launch_read_probe(const void* buf, int64_t n16, uint32_t* sink, void* stream);
 
 }  // namespace pa

@@ -10,7 +10,7 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3
+from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3, _I32P, check, lib
 from .allocator import BlockAllocator
 from .ops import (make_pool_desc, pa_cache_write, pa_copy_blocks, pa_decode, pa_decode_workspace_size,
                   pa_prefill_chunk, validate_decode, validate_pairs, validate_prefill, validate_slots)
@@ -26,19 +26,17 @@ def _signed(code: int, bits: int) -> int:
 
 def leading_shared_blocks(tables: np.ndarray, lens: np.ndarray, block_size: int) -> np.ndarray:
     """For each row, how many leading entries of its table (within its length) are physical blocks
-    that another row of the same batch also reads: the pa_decode `shared_blocks` hint."""
-    tables = np.asarray(tables)
-    nblk = -(-np.asarray(lens, np.int64) // block_size)
-    if tables.shape[1] == 0:
-        return np.zeros(len(nblk), dtype=np.int32)
-    valid = np.arange(tables.shape[1])[None, :] < nblk[:, None]
-    blocks = tables[valid]
-    uniq, counts = np.unique(blocks, return_counts=True)
-    multi = np.zeros(tables.shape, dtype=bool)
-    multi[valid] = counts[np.searchsorted(uniq, blocks)] > 1
-    # length of the leading run of shared entries in each row
-    run = np.where(multi.all(axis=1), tables.shape[1], np.argmin(multi, axis=1))
-    return np.minimum(run, nblk).astype(np.int32)
+    that another row of the same batch also reads: the pa_decode_ex `shared_blocks` hint (host,
+    pa_plan_cache_hint)."""
+    t = np.ascontiguousarray(tables, dtype=np.int32)
+    l = np.ascontiguousarray(lens, dtype=np.int32)
+    out = np.zeros(len(l), dtype=np.int32)
+    if len(l) == 0:
+        return out
+    width = int(t.shape[1]) if t.ndim == 2 else 0
+    check(lib().pa_plan_cache_hint(t.ctypes.data_as(_I32P), width, l.ctypes.data_as(_I32P), len(l),
+                                   int(block_size), out.ctypes.data_as(_I32P)))
+    return out
 
 
 @dataclass

@@ -232,6 +232,14 @@ def pa_fp8_decode_table(out: torch.Tensor, stream=None) -> None:
     check(lib().pa_fp8_decode_table(_dev(out, "out"), _stream(stream)))
 
 
+def pa_hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Streams buf (a contiguous device tensor, a multiple of 16 bytes) once with 16-byte loads;
+    sink is a device tensor of at least 4 bytes (a measurement aid: time it to read the device's
+    streaming read bandwidth)."""
+    check(lib().pa_hbm_read_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"),
+                                  _stream(stream)))
+
+
 # ---- host checks of device-resident inputs (pa_validate_*): numpy arrays, before they are sent ----
 
 def _i32(a):

@@ -275,6 +275,17 @@ std::string run(const std::string& cmd, Line& l) {
                                    in_place),
                  o);
   }
+  if (cmd == "hint") {              // hint max_blocks [tables] [lens] block_size
+    const int32_t mb = static_cast<int32_t>(l.i());
+    auto t = l.arr<int32_t>();
+    auto lens = l.arr<int32_t>();
+    const int32_t bs = static_cast<int32_t>(l.i());
+    if (t.size() != lens.size() * mb) throw std::runtime_error("table size");
+    auto out = buf<int32_t>(lens.size());
+    const pa_status st = pa_plan_cache_hint(t.data(), mb, lens.data(), static_cast<int32_t>(lens.size()), bs, out.data());
+    put(o, out, st == PA_OK ? lens.size() : 0);
+    return reply(st, o);
+  }
   if (cmd == "tails") {             // tails max_blocks [tables] [lens] block_size width [shared]
     const int32_t mb = static_cast<int32_t>(l.i());
     auto t = l.arr<int32_t>();

@@ -219,6 +219,17 @@ def test_prefill_variants(kv, hq, hkv, b):
     assert _out_err(si.dec_out, ref.decode_out) <= TOL[kv]
 
 
+def test_read_probe_streams_and_leaves_memory_alone():
+    from paged_kv_cache_427_amd.ops import pa_hbm_read_probe
+    buf = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    before = buf.clone()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    pa_hbm_read_probe(buf, sink)
+    pa_hbm_read_probe(buf[:(1 << 20) - 12], sink)     # a size that is not a multiple of 64 pieces
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+
+
 def test_prefill_persistent_item_walk():
     """256-row prefill tiles walked by the persistent workgroups: more sequences (70) than the ranked
     order takes, so items go in index order; 16 KV heads, two per XCD's list; groups of 8; ragged
