@@ -492,9 +492,10 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) prefill_kernel(Prefill
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c / 2][8 * (c % 2) + e], c2, nm));
-        lsum += p;
-        pb[c][e] = static_cast<__bf16>(p);
+        // the row sum adds the bf16-rounded probability that the P.V product uses
+        const __bf16 p = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[c / 2][8 * (c % 2) + e], c2, nm)));
+        lsum += static_cast<float>(p);
+        pb[c][e] = p;
       }
     l_run += half_sum(lsum);
     ld.store_v(odd ? vbuf0 : vbuf1, min(t + 1, last) * kKT, n_keys, wave, lane);
@@ -705,8 +706,6 @@ __global__ void __launch_bounds__(64 * W, 1) prefill_pipe_kernel(PrefillArgs a, 
   ld.max_blocks = a.max_blocks;
   ld.pool_blocks = a.num_blocks;
 
-  // One step; on entry: sc = S(t); pp = P(t - 1) (bf16 pairs); LDS holds K(t + 1) and V(t - 1);
-  // the register stage holds K(t + 2) and V(t).
   // One step; on entry: sc = S(t); pp = P(t - 1) (bf16 pairs); LDS holds K(t + 1) and V(t - 1);
   // the register stage holds K(t + 2) and V(t).
   auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], uint32_t (&pp)[4][4], uint32_t (&pn)[4][4])

@@ -2,7 +2,9 @@
 itself (4096 sequences), the smallest one planned by the plan kernel (4097, prefix searched in LDS),
 more sequences than the plan kernel ranks in LDS (more than 8192), and rows of over 1024 pieces per
 (sequence, head), which the merge kernel combines in several batches of records, each against the
-fp64 oracle on sampled or all outputs (bf16 tolerance 2e-2)."""
+fp64 oracle on sampled or all outputs (bf16 tolerance 2e-2); and one workspace reused by decodes of
+different shapes, each bit-identical to the same decode on a fresh workspace (every call rewrites
+the plan and records it reads)."""
 import numpy as np
 import pytest
 import torch
@@ -51,7 +53,7 @@ def _oracle_rows(kpool, vpool, tabs, lens, q, scale, seqs):
     return out
 
 
-def _decode(q, kpool, vpool, tabs, lens, scale, max_ctx, partition):
+def _decode(q, kpool, vpool, tabs, lens, scale, max_ctx, partition, workspace=None):
     from paged_kv_cache_427_amd.ops import pa_decode, make_pool_desc
     from paged_kv_cache_427_amd._lib import PA_BF16
     num_blocks, hkv, b, d = kpool.shape
@@ -59,7 +61,8 @@ def _decode(q, kpool, vpool, tabs, lens, scale, max_ctx, partition):
     dev = torch.device("cuda")
     out = torch.full(q.shape, 3.0, dtype=torch.bfloat16, device=dev)
     pa_decode(q.to(dev), kpool.to(dev), vpool.to(dev), pool, torch.as_tensor(tabs).to(dev),
-              torch.as_tensor(np.asarray(lens, np.int32)).to(dev), scale, out, max_ctx, partition)
+              torch.as_tensor(np.asarray(lens, np.int32)).to(dev), scale, out, max_ctx, partition,
+              workspace=workspace)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 
@@ -94,11 +97,13 @@ def test_batches_at_the_plan_limits(n):
     assert err <= TOL_BF16
 
 
-@pytest.mark.parametrize("partition", [32, 512])
+@pytest.mark.parametrize("partition", [0, 32, 512])
 def test_rows_of_many_pieces(partition):
     """Two long contexts cut every 32 tokens: over 1024 pieces per (sequence, head), which the merge
     kernel combines 64 records at a time with a running maximum across the batches (and, for
-    comparison, the same contexts cut every 512: about 70 pieces, two batches)."""
+    comparison, the same contexts cut every 512: about 70 pieces, two batches).  Without partitions
+    the two contexts are cut only by the waves' shares (a few units each, so again over 1000 pieces
+    per row)."""
     rng = np.random.Generator(np.random.PCG64(4272))
     gen = torch.Generator().manual_seed(4272)
     hq, hkv, b, d = 2, 1, 16, 128
@@ -113,5 +118,44 @@ def test_rows_of_many_pieces(partition):
     got = _decode(q, kpool, vpool, tabs, lens, scale, 36000, partition)
     ref = _oracle_rows(kpool, vpool, tabs, lens, q, scale, [0, 1])
     err = max(float(np.max(np.abs(got[s] - ref[s]))) for s in (0, 1))
+    _say("max err", err)
+    assert err <= TOL_BF16
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace for decodes of three shapes, then the first shape again, starting from bytes
+    that are not zero: every result equals the same decode on a fresh workspace bit for bit (the
+    plan and the records a call reads are the ones it wrote, whatever an earlier call left)."""
+    from paged_kv_cache_427_amd.ops import pa_decode_workspace_size
+    rng = np.random.Generator(np.random.PCG64(4273))
+    gen = torch.Generator().manual_seed(4273)
+    shapes = [(64, 8, 8, 600), (5, 16, 4, 3000), (200, 4, 4, 200)]
+    d, b = 128, 16
+    cases = []
+    need = 0
+    for n, hq, hkv, lmax in shapes:
+        lens = rng.integers(1, lmax + 1, size=n).astype(np.int32)
+        lens[n // 3] = 0
+        num_blocks = sum(-(-int(L) // b) for L in lens) + 8
+        kpool, vpool = _pools(gen, num_blocks, hkv, b, d)
+        tabs = _tables(rng, lens, b, num_blocks)
+        q = torch.randn((n, hq, d), generator=gen).to(torch.bfloat16)
+        cases.append((q, kpool, vpool, tabs, lens, int(lens.max())))
+        need = max(need, pa_decode_workspace_size(n, hq, d, int(lens.max()), 0))
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    shared = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    for k in [0, 1, 2, 0]:
+        q, kpool, vpool, tabs, lens, mx = cases[k]
+        _say("shape", shapes[k], "on the shared workspace")
+        got = _decode(q, kpool, vpool, tabs, lens, scale, mx, 0, workspace=shared)
+        fresh = _decode(q, kpool, vpool, tabs, lens, scale, mx, 0,
+                        workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
+        assert np.array_equal(got, fresh)
+    # and against the oracle on a few rows of the longest shape
+    q, kpool, vpool, tabs, lens, mx = cases[1]
+    got = _decode(q, kpool, vpool, tabs, lens, scale, mx, 0, workspace=shared)
+    rows = [s for s in range(len(lens)) if lens[s] > 0]
+    ref = _oracle_rows(kpool, vpool, tabs, lens, q, scale, rows)
+    err = max(float(np.max(np.abs(got[s] - ref[s]))) for s in rows)
     _say("max err", err)
     assert err <= TOL_BF16
