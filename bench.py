@@ -46,13 +46,22 @@ from synth import make_workload, poison_code, elem_bytes  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_427_amd", "csrc", "decode.hip")
+# the sources of every decode launch (the stream and merge kernels; the beam decode's tail merge)
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_427_amd", "csrc", f) for f in ("decode.hip", "cascade.hip")]
+
+
+def decode_source_hash() -> str:
+    """First 16 hex digits of the sha256 of the decode sources, concatenated in DECODE_SRCS order."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(config: str, block_size):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary of this workload, or
-    None when there is none or the decode source changed since the counters were taken."""
-    import hashlib
+    None when there is none or the decode sources changed since the counters were taken."""
     import re
     if block_size not in (None, 16):
         return None
@@ -64,8 +73,7 @@ def measured_traffic(config: str, block_size):
     m_h = re.search(r"decode_source_sha256_16: ([0-9a-f]+)", text)
     if not (m_t and m_h):
         return None
-    cur = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
-    return int(m_t.group(1)) if cur == m_h.group(1) else None
+    return int(m_t.group(1)) if decode_source_hash() == m_h.group(1) else None
 
 
 def decode_bytes(wl, tables: np.ndarray):
@@ -580,19 +588,23 @@ def step_bench(args, dev, config, block_size, steps, warmup, partition=None, con
           f"tokens {wl.num_tokens}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    nev = 5
+    nev = 6
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
 
     def step(ev=None):
+        # a beam decode's shared part goes first (the step's copies and writes cannot change it); its
+        # time counts as decode time
         if ev: ev[0].record(stream)
-        eng.copy_step(si)
+        eng.early_decode_step(si)
         if ev: ev[1].record(stream)
-        eng.write_step(si)
+        eng.copy_step(si)
         if ev: ev[2].record(stream)
-        eng.prefill_step(si)
+        eng.write_step(si)
         if ev: ev[3].record(stream)
-        eng.decode_step(si)
+        eng.prefill_step(si)
         if ev: ev[4].record(stream)
+        eng.decode_step(si)
+        if ev: ev[5].record(stream)
 
     for _ in range(warmup):
         step()
@@ -615,8 +627,10 @@ def step_bench(args, dev, config, block_size, steps, warmup, partition=None, con
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    parts = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(nev - 1)]
-                      for i in range(steps)])
+    raw = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(nev - 1)]
+                    for i in range(steps)])
+    # columns: copy, write, prefill, decode (the early part of a beam decode added to the decode)
+    parts = np.stack([raw[:, 1], raw[:, 2], raw[:, 3], raw[:, 0] + raw[:, 4]], axis=1)
     ms_copy, ms_write, ms_prefill, ms_decode = parts.mean(axis=0)
 
     res = {"metric": "paged decode KV-read GB/s (% of MI355X HBM peak); decode tokens/s per layer",
@@ -638,11 +652,11 @@ def step_bench(args, dev, config, block_size, steps, warmup, partition=None, con
         res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": measured_traffic(config, block_size),
-                           "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of this decode source, scaled by "
+                           "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of these decode sources, scaled by "
                                              "a device copy of known size, read from the committed profile "
                                              "(null when the source changed since)",
-                           "kernel": ("beam decode: pa_decode_ex over shared blocks + over private tails + "
-                                      "pa_merge_states" if getattr(si, "cascade", None) is not None else
+                           "kernel": ("beam decode: pa_decode_ex over shared blocks + pa_decode_tail_merge "
+                                      "(private tails merged in)" if getattr(si, "cascade", None) is not None else
                                       "pa_decode (stream + merge kernels)"),
                            "algorithmic_bytes_per_launch": int(uniq + other)}
         res["decode_logical_kv_GBps"] = round(logical / (ms_decode * 1e-3) / 1e9, 1)

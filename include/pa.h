@@ -83,7 +83,8 @@ const char* pa_status_str(int32_t status);
 /* Detail of the last failure on this thread (static thread-local buffer; "" after success). */
 const char* pa_last_error(void);
 /* ABI version: (major << 16) | minor (2.0: pa_decode without the cache hint, pa_decode_noalloc;
- * 2.1: pa_validate_*, pa_plan_beam_tails, device-side clamping of block ids). */
+ * 2.1: pa_validate_*, pa_plan_beam_tails, device-side clamping of block ids; 2.2:
+ * pa_decode_tail_merge). */
 int32_t pa_version(void);
 
 /* ---------------------------------------------------------------------------------------------
@@ -323,6 +324,36 @@ pa_status pa_plan_beam_tails(const int32_t* tables, int32_t max_blocks, const in
 pa_status pa_merge_states(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
                           int64_t rows, int32_t head_dim, void* out, int32_t out_dtype, float* lse_out,
                           pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_decode_tail_merge -- the private tails of a beam decode and the merge with the shared part, in
+ * one launch, for tails of at most 32 keys ([day28] §六 question 3: branches read their common
+ * prompt blocks once; each branch then has only the few tokens it generated since the fork).  For
+ * sequence s and query head h (KV head g = h / (num_q_heads / num_kv_heads)), with the tail's
+ * keys T_s[j] = pool[tail_tables[s][j / b]][g][j % b], 0 <= j < tail_lens[s]:
+ *     lse_t = ln sum_j exp(scale q[s,h,:] . K_T[j]),  o_t = softmax_j(...) V_T
+ *     out[s,h,:] = (o_prev[s,h,:] e^(lse_prev[s,h] - M) + o_t e^(lse_t - M)) / (e^(lse_prev - M) + e^(lse_t - M))
+ * with M the larger of the two log-sum-exps: what pa_decode_ex over the tails (with lse_out)
+ * followed by pa_merge_states computes.  A row with no tail keys gets o_prev; a row with neither
+ * gets zeros.
+ *   q            device bf16 [num_seqs][num_q_heads][128], 16-byte aligned; the pool bf16 or fp8
+ *                (PA_ERR_UNSUPPORTED otherwise, and for head_dim other than 128)
+ *   tail_tables  device int32 [num_seqs][max_blocks_per_seq]; tail_lens device int32 [num_seqs],
+ *                each clamped to [0, max_tail_len] on the device
+ *   max_tail_len a bound of every tail length, at most 32 (PA_ERR_UNSUPPORTED above: decode such
+ *                tails with pa_decode_ex and combine them with pa_merge_states)
+ *   o_prev       device float [num_seqs][num_q_heads][128], 8-byte aligned, and lse_prev device
+ *                float [num_seqs][num_q_heads] (natural log; -inf for no keys): the other part's
+ *                result, as pa_decode_ex writes it with lse_out
+ *   out          device [num_seqs][num_q_heads][128] of out_dtype (PA_F32 or PA_BF16), aligned to
+ *                two elements; it must not overlap o_prev
+ * The tail's P.V products run in fp32 (the probabilities are not rounded to bf16).
+ * ------------------------------------------------------------------------------------------- */
+pa_status pa_decode_tail_merge(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
+                               const pa_pool_desc* pool, const int32_t* tail_tables, int32_t max_blocks_per_seq,
+                               const int32_t* tail_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                               int32_t max_tail_len, const float* o_prev, const float* lse_prev, void* out,
+                               int32_t out_dtype, pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Host checks of device-resident inputs (no GPU).  The kernels use these values as given; out of

@@ -46,6 +46,9 @@ _PROTOS = {
                                c_void_p, c_int32, _I64P, c_void_p, c_void_p, c_void_p]),
     "pa_merge_states": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_int32,
                                   c_void_p, c_void_p]),
+    "pa_decode_tail_merge": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_int32,
+                                       c_void_p, c_int32, c_int32, c_float, c_int32, c_void_p, c_void_p, c_void_p,
+                                       c_int32, c_void_p]),
     "pa_plan_shared_blocks": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, c_int32, _I32P]),
     "pa_plan_cache_hint": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, _I32P]),
     "pa_plan_beam_tails": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, c_int32, _I32P, _I32P, c_int32, _I32P,

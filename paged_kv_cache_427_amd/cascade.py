@@ -5,15 +5,18 @@ decode reads each shared block once per branch.  Here one pa_decode_ex call read
 of each request once, with the W branches' queries of a KV head as its W query heads (the strides
 pick them out of the batch's q, and write the outputs back to the branches' rows), a second call
 reads each branch's private tail, and pa_merge_states combines the two results by their
-log-sum-exps.  Needs one query head per KV head (the branches then fill the group) and W in
-{2, 4, 8}; the batch is laid out as requests x W consecutive branches.
+log-sum-exps.  Tails of at most 32 tokens (a beam's tokens since the fork) are decoded and merged
+in one launch instead, pa_decode_tail_merge.  Needs one query head per KV head (the branches then
+fill the group) and W in {2, 4, 8}; the batch is laid out as requests x W consecutive branches.
 """
 import numpy as np
 import torch
 
-from ._lib import check, lib
+from ._lib import PA_F32, check, lib
 from ._lib import _I32P
-from .ops import pa_decode_ex, pa_decode_workspace_size, pa_merge_states
+
+TAIL_MERGE_MAX = 32     # longest tail pa_decode_tail_merge takes
+from .ops import pa_decode_ex, pa_decode_tail_merge, pa_decode_workspace_size, pa_merge_states
 
 
 def plan_shared_blocks(tables: np.ndarray, lens: np.ndarray, block_size: int, width: int) -> np.ndarray:
@@ -62,6 +65,8 @@ class CascadeDecode:
         lens = np.asarray(lens, np.int64)
         # shared part: group g reads the table row of its first branch, k_g blocks
         self.tables = torch.as_tensor(np.ascontiguousarray(tables, dtype=np.int32), device=dev)
+        self.tables_host = np.ascontiguousarray(tables, dtype=np.int32)
+        self.block_size = b
         self.pre_lens = torch.as_tensor((k * b).astype(np.int32), device=dev)
         self.pre_max = int((k * b).max()) if self.groups else 0
         # private tails: each branch's blocks from its group's k on
@@ -78,13 +83,33 @@ class CascadeDecode:
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
         self.max_blocks = int(tables.shape[1])
 
+    def shared_blocks(self) -> np.ndarray:
+        """Physical ids of the blocks the shared part reads (host)."""
+        tabs = self.tables_host
+        ids = [tabs[g * self.width, :int(k)] for g, k in enumerate(self.shared_tokens // self.block_size)]
+        return np.unique(np.concatenate(ids)) if ids else np.zeros(0, np.int32)
+
     def run(self, q: torch.Tensor, k_pool, v_pool, pool, scale: float, out: torch.Tensor, stream=None) -> None:
+        self.run_shared(q, k_pool, v_pool, pool, scale, stream)
+        self.run_tails(q, k_pool, v_pool, pool, scale, out, stream)
+
+    def run_shared(self, q: torch.Tensor, k_pool, v_pool, pool, scale: float, stream=None) -> None:
+        """The shared part: each request's shared blocks once, for all its branches (into o_pre, l_pre)."""
         W, hq, d = self.width, self.hq, self.d
         # rows of group g: sequence stride W*hq*d; KV head stride d; branch (head in the group) stride hq*d
         strides = (W * hq * d, d, hq * d)
         pa_decode_ex(q, strides, self.groups, W * hq, k_pool, v_pool, pool, self.tables.data_ptr(),
                      W * self.max_blocks, self.pre_lens, scale, self.o_pre, strides, max(self.pre_max, 1),
                      self.l_pre, self.workspace, stream=stream)
+
+    def run_tails(self, q: torch.Tensor, k_pool, v_pool, pool, scale: float, out: torch.Tensor, stream=None) -> None:
+        """The private tails, merged with the shared part's result into out."""
+        hq, d = self.hq, self.d
+        if self.tail_max <= TAIL_MERGE_MAX and pool.dtype != PA_F32 and d == 128:
+            # short tails: their attention and the merge with the shared part in one launch
+            pa_decode_tail_merge(q, k_pool, v_pool, pool, self.tail_tables, self.tail_lens, scale, self.tail_max,
+                                 self.o_pre, self.l_pre, out, stream=stream)
+            return
         pa_decode_ex(q, None, self.n, hq, k_pool, v_pool, pool, self.tail_tables.data_ptr(),
                      int(self.tail_tables.shape[1]), self.tail_lens, scale, self.o_tail, None,
                      max(self.tail_max, 1), self.l_tail, self.workspace, stream=stream)

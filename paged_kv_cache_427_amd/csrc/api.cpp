@@ -387,6 +387,62 @@ pa_status pa_merge_states(const float* o_a, const float* lse_a, const float* o_b
   return launch_status(pa::launch_merge_states(a, out_dtype, stream), "pa_merge_states");
 }
 
+pa_status pa_decode_tail_merge(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
+                               const pa_pool_desc* pool, const int32_t* tail_tables, int32_t max_blocks,
+                               const int32_t* tail_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                               int32_t max_tail_len, const float* o_prev, const float* lse_prev, void* out,
+                               int32_t out_dtype, pa_stream stream) {
+  pa_status st = check_pool(pool, "pa_decode_tail_merge");
+  if (st != PA_OK) return st;
+  if (num_seqs < 0) return pa_fail(PA_ERR_INVALID, "pa_decode_tail_merge: negative num_seqs");
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_tail_merge: num_q_heads must be a positive multiple of num_kv_heads");
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_tail_merge: group size must be 1, 2, 4 or 8");
+  if (q_dtype != PA_BF16 || pool->dtype == PA_F32)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_tail_merge: needs bf16 q and a bf16 or fp8 pool");
+  if (pool->head_dim != 128) return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_tail_merge: head_dim must be 128");
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_tail_merge: bad out_dtype");
+  if (!std::isfinite(scale)) return pa_fail(PA_ERR_INVALID, "pa_decode_tail_merge: scale is not finite");
+  if (max_tail_len < 0) return pa_fail(PA_ERR_INVALID, "pa_decode_tail_merge: negative max_tail_len");
+  if (max_tail_len > 32)
+    return pa_fail(PA_ERR_UNSUPPORTED,
+                   "pa_decode_tail_merge: tails of more than 32 keys (use pa_decode_ex and pa_merge_states)");
+  if (max_blocks < (max_tail_len + pool->block_size - 1) / pool->block_size || max_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_tail_merge: max_blocks_per_seq < ceil(max_tail_len / block_size)");
+  if (num_seqs == 0) return pa_ok();
+  if (!q || !k_pool || !v_pool || !tail_tables || !tail_lens || !o_prev || !lse_prev || !out)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_tail_merge: null pointer");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_tail_merge: q must start at a 16-byte boundary");
+  if (reinterpret_cast<uintptr_t>(o_prev) % 8 != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_tail_merge: o_prev must start at an 8-byte boundary");
+  if (reinterpret_cast<uintptr_t>(out) % (2 * elem_bytes(out_dtype)) != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_tail_merge: out must start at a boundary of 2 elements");
+  pa::TailMergeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.tables = tail_tables;
+  a.max_blocks = max_blocks;
+  a.lens = tail_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_blocks = pool->num_blocks;
+  const float kscale = pool->dtype == PA_FP8_E4M3 ? pool->k_scale : 1.0f;
+  a.qk_scale = static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
+  a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+  a.max_tail = max_tail_len;
+  a.o_prev = o_prev;
+  a.lse_prev = lse_prev;
+  a.out = out;
+  return launch_status(pa::launch_tail_merge(a, pool->dtype, pool->block_size, pool->head_dim, out_dtype, stream),
+                       "pa_decode_tail_merge: no kernel for this combination");
+}
+
 pa_status pa_prefill_chunk(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
                            const pa_pool_desc* pool, const int32_t* tables, int32_t max_blocks,
                            const int32_t* qsl, const int32_t* prior, int32_t num_seqs,

@@ -1,11 +1,17 @@
-// Merge of two attention results over disjoint key sets of the same query rows.
+// Merge of two attention results over disjoint key sets of the same query rows, and the attention of
+// short private tails folded into such a merge.
 //
 // Beam branches share their prompt's blocks («GPU 学习日报 Day 28：vLLM 与 PagedAttention：GPU
 // Memory 管理的艺术», §六 question 3).  A decode can then read the shared blocks once, for the
 // queries of every branch (one pa_decode_ex call over the shared part, the branches' queries as the
 // query heads of each KV head), read each private tail on its own, and combine the two results of
 // every row with their log-sum-exps: the same rescaled combination as the merge of split pieces.
-// One thread per 4 dims of a row: an HBM-bound elementwise pass.
+//  * merge_states_kernel: one thread per 4 dims of a row, an HBM-bound elementwise pass;
+//  * tail_merge_kernel: the tail of at most 32 keys and the merge in one pass, one wave per
+//    (sequence, KV head).  Lane j and lane j + 32 dot key j's two halves of the dims with the G query
+//    heads (packed bf16 dots, fp32 sums); the softmax is a reduction over 32 lanes; each lane then adds
+//    two output dims over the keys, the probabilities read from their lanes as scalars, in fp32;
+//    and the shared part's (output, log-sum-exp) is folded in before the row is written.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -46,7 +52,229 @@ __global__ void __launch_bounds__(kThreads) merge_states_kernel(MergeStatesArgs 
   if (a.lse_out && d == 0) a.lse_out[r] = m == -INFINITY ? -INFINITY : m + __logf(sum);
 }
 
+constexpr int kTailMax = 32;   // keys of a tail this kernel takes (lanes 0..31)
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot_bf16x2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc,
+                                         false);
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+template <int KV, int BS, int G>
+__global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, int out_bf16) {
+  constexpr int D = 128;
+  constexpr int E = KV == kBF16 ? 2 : 1;
+  constexpr int TILE = BS * D * E;                 // bytes of one (block, KV head) tile
+  constexpr int NB = (kTailMax + BS - 1) / BS;     // blocks a tail can touch
+  constexpr int NP = BS / 8;                       // 8-token pieces of a V^T row of one block
+  constexpr int PW = 2 * E;                        // dwords of one piece (bf16 4, fp8 2)
+  const int lane = threadIdx.x & 63;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (w >= static_cast<int64_t>(a.num_seqs) * a.num_kv_heads) return;
+  const int seq = static_cast<int>(w / a.num_kv_heads);
+  const int kvh = static_cast<int>(w % a.num_kv_heads);
+  // a length outside [0, max_tail] is clamped, and a block id outside the pool is clamped into it
+  const int L = __builtin_amdgcn_readfirstlane(min(max(a.lens[seq], 0), a.max_tail));
+  const int32_t* tab = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+  int64_t phys[NB];
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+    phys[q] = q * BS < L ? min(max(tab[q], 0), a.num_blocks - 1) : 0;
+  const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * TILE;
+  const char* kbase = static_cast<const char*>(a.k_pool) + static_cast<int64_t>(kvh) * TILE;
+  const char* vbase = static_cast<const char*>(a.v_pool) + static_cast<int64_t>(kvh) * TILE;
+  const int64_t row0 = static_cast<int64_t>(seq) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
+  const int j = lane & 31, half = lane >> 5;
+
+  // ---- every load first, so that the wave waits on memory once ----
+  // K: key j's dims 64 half .. +64 (lane j and lane j + 32); zeros past the tail
+  uint32_t kraw[16 * E];   // 64 dims: 32 dwords of bf16, 16 of fp8
+#pragma unroll
+  for (int c = 0; c < 16 * E; ++c) kraw[c] = 0u;
+  if (j < L) {
+    const char* krow = kbase + phys[j / BS] * blk_stride + (j % BS) * (D * E) + half * 64 * E;
+#pragma unroll
+    for (int c = 0; c < 4 * E; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(krow + 16 * c);
+      kraw[4 * c] = v.x; kraw[4 * c + 1] = v.y; kraw[4 * c + 2] = v.z; kraw[4 * c + 3] = v.w;
+    }
+  }
+  // V^T rows of dims 2 lane and 2 lane + 1, the 8-token pieces that hold tail keys
+  uint32_t vraw[NB][NP][2][PW];
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int c = 0; c < NP; ++c)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int k = 0; k < PW; ++k) vraw[q][c][r][k] = 0u;
+        if (q * BS + 8 * c < L) {
+          const char* src = vbase + phys[q] * blk_stride + static_cast<int64_t>(2 * lane + r) * BS * E + 8 * E * c;
+          if constexpr (E == 2) {
+            const uint4 u = *reinterpret_cast<const uint4*>(src);
+            vraw[q][c][r][0] = u.x; vraw[q][c][r][1] = u.y; vraw[q][c][r][2] = u.z; vraw[q][c][r][3] = u.w;
+          } else {
+            const uint2 u = *reinterpret_cast<const uint2*>(src);
+            vraw[q][c][r][0] = u.x; vraw[q][c][r][1] = u.y;
+          }
+        }
+      }
+  uint4 qraw[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const char* qrow = static_cast<const char*>(a.q) + ((row0 + g) * D + half * 64) * 2;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qraw[g][c] = *reinterpret_cast<const uint4*>(qrow + 16 * c);
+  }
+  float2 po[G];
+  float lp[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    po[g] = *reinterpret_cast<const float2*>(a.o_prev + (row0 + g) * D + 2 * lane);
+    lp[g] = a.lse_prev[row0 + g];
+  }
+
+  // ---- base-2 logits of key j for each head (-inf past the tail) ----
+  uint32_t kw[32];   // bf16 pairs of the 64 dims
+  if constexpr (E == 2) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) kw[c] = kraw[c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      kw[2 * c] = fp8x2_bf16<false>(kraw[c]);
+      kw[2 * c + 1] = fp8x2_bf16<true>(kraw[c]);
+    }
+  }
+  float x[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      acc = dot_bf16x2(kw[4 * c], qraw[g][c].x, acc);
+      acc = dot_bf16x2(kw[4 * c + 1], qraw[g][c].y, acc);
+      acc = dot_bf16x2(kw[4 * c + 2], qraw[g][c].z, acc);
+      acc = dot_bf16x2(kw[4 * c + 3], qraw[g][c].w, acc);
+    }
+    acc += shfl_xor(acc, 32);                      // the other half of the dims
+    x[g] = j < L ? acc * a.qk_scale : -INFINITY;
+  }
+  // ---- softmax statistics over the 32 keys (both halves hold the same values) ----
+  float p[G], m[G], l[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mx = x[g];
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+    m[g] = mx;
+    p[g] = L > 0 ? __builtin_amdgcn_exp2f(x[g] - mx) : 0.f;   // 0 past the tail
+    float sm = p[g];
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) sm += shfl_xor(sm, off);
+    l[g] = sm;
+  }
+  // ---- sum over the keys of p v, dims 2 lane and 2 lane + 1; values past the tail (any bits) are
+  // skipped, never multiplied ----
+  float o[G][2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) o[g][0] = o[g][1] = 0.f;
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int c = 0; c < NP; ++c) {
+      const int t0 = q * BS + 8 * c;
+      if (t0 >= L) continue;   // wave-uniform
+      float v0[8], v1[8];
+#pragma unroll
+      for (int k = 0; k < PW; ++k) {
+        if constexpr (E == 2) {
+          v0[2 * k] = bf16_lo(vraw[q][c][0][k]); v0[2 * k + 1] = bf16_hi(vraw[q][c][0][k]);
+          v1[2 * k] = bf16_lo(vraw[q][c][1][k]); v1[2 * k + 1] = bf16_hi(vraw[q][c][1][k]);
+        } else {
+          fp8x2_to_f32<false>(vraw[q][c][0][k], v0[4 * k], v0[4 * k + 1]);
+          fp8x2_to_f32<true>(vraw[q][c][0][k], v0[4 * k + 2], v0[4 * k + 3]);
+          fp8x2_to_f32<false>(vraw[q][c][1][k], v1[4 * k], v1[4 * k + 1]);
+          fp8x2_to_f32<true>(vraw[q][c][1][k], v1[4 * k + 2], v1[4 * k + 3]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t0 + t >= L) continue;   // wave-uniform
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[g]), t0 + t));
+          o[g][0] += pj * v0[t];
+          o[g][1] += pj * v1[t];
+        }
+      }
+    }
+  // ---- fold in the prior (output, natural log-sum-exp) and write the row ----
+  constexpr float kLog2e = 1.4426950408889634f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t r = row0 + g;
+    const float lpb = lp[g] * kLog2e;                           // base 2
+    const float lt = L > 0 ? m[g] + __log2f(l[g]) : -INFINITY;
+    const float M = fmaxf(lpb, lt);
+    float r0v = 0.f, r1v = 0.f;
+    if (M != -INFINITY) {
+      const float wp = __builtin_amdgcn_exp2f(lpb - M);         // 0 when the prior is empty
+      const float wt = L > 0 ? __builtin_amdgcn_exp2f(m[g] - M) : 0.f;   // weight of the sums o
+      const float inv = 1.f / (wp + wt * l[g]);
+      r0v = (po[g].x * wp + o[g][0] * wt * a.v_scale) * inv;
+      r1v = (po[g].y * wp + o[g][1] * wt * a.v_scale) * inv;
+    }
+    if (out_bf16) {
+      static_cast<uint32_t*>(a.out)[r * (D / 2) + lane] = f32_to_bf16_bits(r0v) | (f32_to_bf16_bits(r1v) << 16);
+    } else {
+      *reinterpret_cast<float2*>(static_cast<float*>(a.out) + r * D + 2 * lane) = make_float2(r0v, r1v);
+    }
+  }
+}
+
+template <int KV, int BS>
+int launch_tail_g(const TailMergeArgs& a, int ob, hipStream_t s, unsigned blocks) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 1>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 2: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 2>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 4: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 4>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 8: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 8>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    default: return -1;
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
+template <int KV>
+int launch_tail_bs(const TailMergeArgs& a, int block_size, int ob, hipStream_t s, unsigned blocks) {
+  switch (block_size) {
+    case 8: return launch_tail_g<KV, 8>(a, ob, s, blocks);
+    case 16: return launch_tail_g<KV, 16>(a, ob, s, blocks);
+    case 32: return launch_tail_g<KV, 32>(a, ob, s, blocks);
+    default: return -1;
+  }
+}
+
 }  // namespace
+
+int launch_tail_merge(const TailMergeArgs& a, int kv_dtype, int block_size, int head_dim, int out_dtype,
+                      void* stream) {
+  if (head_dim != 128 || a.max_tail > kTailMax) return -1;
+  const int64_t waves = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads;
+  if (waves == 0) return 0;
+  const int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
+  if (blocks > 0x7fffffff) return -1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int ob = out_dtype == kBF16 ? 1 : 0;
+  if (kv_dtype == kBF16) return launch_tail_bs<kBF16>(a, block_size, ob, s, static_cast<unsigned>(blocks));
+  if (kv_dtype == kFP8) return launch_tail_bs<kFP8>(a, block_size, ob, s, static_cast<unsigned>(blocks));
+  return -1;
+}
 
 int launch_merge_states(const MergeStatesArgs& a, int out_dtype, void* stream) {
   const int64_t total = a.rows * (a.head_dim / 4);

@@ -132,6 +132,27 @@ struct MergeStatesArgs {
   float* lse_out;
 };
 int launch_merge_states(const MergeStatesArgs& a, int out_dtype, void* stream);
+struct TailMergeArgs {
+  const void* q;         // bf16 [num_seqs][num_q_heads][128]
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tables; // [num_seqs][max_blocks]: the tail's blocks, key j in block j / block_size
+  int32_t max_blocks;
+  const int32_t* lens;   // [num_seqs] tail keys, clamped to [0, max_tail]
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;    // pool blocks: a table entry outside [0, num_blocks) is clamped into it
+  float qk_scale;        // scale * k_scale * log2(e)
+  float v_scale;
+  int32_t max_tail;      // at most 32
+  const float* o_prev;   // [num_seqs][num_q_heads][128] normalised output over the other keys
+  const float* lse_prev; // [num_seqs][num_q_heads] their natural log-sum-exp
+  void* out;             // [num_seqs][num_q_heads][128] of out dtype
+};
+// Returns 0 on success, -1 when no kernel exists for the combination, else a hipError_t.
+int launch_tail_merge(const TailMergeArgs& a, int kv_dtype, int block_size, int head_dim, int out_dtype,
+                      void* stream);
 // Returns 0 on success, -1 when no kernel exists for the combination, else a hipError_t.
 int launch_decode(const DecodeArgs& a, int kv_dtype, int q_dtype, int out_dtype, int block_size,
                   int head_dim, void* stream);

@@ -200,18 +200,38 @@ class PagedKVEngine:
         pa_cache_write(si.k_new, si.v_new, si.slots, self.k_pool, self.v_pool, self.pool, stream)
 
     def use_cascade(self, si: StepInputs, width: int) -> None:
-        """Decode the batch (requests x `width` branches) reading each request's shared blocks once."""
+        """Decode the batch (requests x `width` branches) reading each request's shared blocks once.
+        The shared part reads only full blocks that every branch still shares; when none of them is a
+        copy destination or receives a token this step (always so: copies and writes go to a
+        branch's last, private block), early_decode_step() runs it before the step's copies, so that
+        it does not stream beside their write-back."""
         from .cascade import CascadeDecode
         wl = self.wl
         si.cascade = CascadeDecode(si.dec_tables.cpu().numpy(), np.asarray(wl.decode_lens, np.int32), wl.block_size,
                                    width, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, self.device)
+        touched = set(si.host_cow[:, 1].tolist()) if len(si.host_cow) else set()
+        if len(si.host_slots):
+            touched |= set((si.host_slots[si.host_slots >= 0] // wl.block_size).tolist())
+        si.cascade_early = not (touched & set(si.cascade.shared_blocks().tolist()))
+        si.cascade_shared_done = False
+
+    def early_decode_step(self, si: StepInputs, stream=None) -> None:
+        """The part of the decode that this step's copies and writes cannot change (the beam decode's
+        shared blocks), issued first; nothing for other decodes."""
+        if si.dec_q is None or getattr(si, "cascade", None) is None or not si.cascade_early:
+            return
+        si.cascade.run_shared(si.dec_q, self.k_pool, self.v_pool, self.pool, self.wl.scale, stream)
+        si.cascade_shared_done = True
 
     def decode_step(self, si: StepInputs, stream=None, out: Optional[torch.Tensor] = None) -> None:
         if si.dec_q is None:
             return
         if getattr(si, "cascade", None) is not None:
-            si.cascade.run(si.dec_q, self.k_pool, self.v_pool, self.pool, self.wl.scale,
-                           si.dec_out if out is None else out, stream)
+            if not si.cascade_shared_done:
+                si.cascade.run_shared(si.dec_q, self.k_pool, self.v_pool, self.pool, self.wl.scale, stream)
+            si.cascade.run_tails(si.dec_q, self.k_pool, self.v_pool, self.pool, self.wl.scale,
+                                 si.dec_out if out is None else out, stream)
+            si.cascade_shared_done = False
             return
         pa_decode(si.dec_q, self.k_pool, self.v_pool, self.pool, si.dec_tables, si.dec_lens, self.wl.scale,
                   si.dec_out if out is None else out, si.dec_max_len, si.dec_partition, si.dec_workspace, stream,
@@ -224,7 +244,9 @@ class PagedKVEngine:
                          self.wl.scale, si.pre_max_chunk, si.pre_out, stream)
 
     def run_step(self, si: StepInputs, stream=None) -> None:
-        """One step: CoW copies, then the new tokens' cache write, then prefill and decode."""
+        """One step: CoW copies, then the new tokens' cache write, then prefill and decode (a beam
+        decode's shared part first, before the copies)."""
+        self.early_decode_step(si, stream)
         self.copy_step(si, stream)
         self.write_step(si, stream)
         self.prefill_step(si, stream)

@@ -213,6 +213,26 @@ def pa_merge_states(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, l
                                 None if lse_out is None else _dev(lse_out, "lse_out"), _stream(stream)))
 
 
+def pa_decode_tail_merge(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc,
+                         tail_tables: torch.Tensor, tail_lens: torch.Tensor, scale: float, max_tail_len: int,
+                         o_prev: torch.Tensor, lse_prev: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """out[s, h] = the merge of (o_prev, lse_prev)[s, h] with attention over sequence s's tail of at
+    most 32 keys (tail_tables int32 [num_seqs, max_blocks], tail_lens int32 [num_seqs]); q bf16
+    [num_seqs, num_q_heads, 128], o_prev float [same], lse_prev float [num_seqs, num_q_heads]."""
+    num_seqs, num_q_heads, head_dim = q.shape
+    if tail_tables.dtype != torch.int32 or tail_lens.dtype != torch.int32:
+        raise TypeError("tail_tables and tail_lens must be int32")
+    if o_prev.dtype != torch.float32 or lse_prev.dtype != torch.float32:
+        raise TypeError("o_prev and lse_prev must be float32")
+    if o_prev.numel() != q.numel() or out.numel() != q.numel() or lse_prev.numel() != num_seqs * num_q_heads:
+        raise ValueError("shapes disagree")
+    check(lib().pa_decode_tail_merge(_dev(q, "q"), pa_dtype(q), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                     ctypes.byref(pool), _dev(tail_tables, "tail_tables"), int(tail_tables.shape[1]),
+                                     _dev(tail_lens, "tail_lens"), int(num_seqs), int(num_q_heads), float(scale),
+                                     int(max_tail_len), _dev(o_prev, "o_prev"), _dev(lse_prev, "lse_prev"),
+                                     _dev(out, "out"), pa_dtype(out), _stream(stream)))
+
+
 def pa_prefill_chunk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc,
                      block_tables: torch.Tensor, query_start_loc: torch.Tensor,
                      prior_context_lens: torch.Tensor, scale: float, max_chunk_len: int, out: torch.Tensor,

@@ -153,3 +153,85 @@ def test_cascade_decode_of_beam_branches(size):
         _say(size, "cascade sampled oracle err", worst)
         assert worst <= TOL_BF16
     assert diff <= TOL_BF16
+
+
+@pytest.mark.parametrize("kv,bs,group", [("bf16", 16, 1), ("bf16", 8, 4), ("bf16", 32, 8), ("fp8", 16, 1),
+                                         ("fp8", 8, 2), ("fp8", 32, 4)])
+def test_tail_merge_against_the_oracle(kv, bs, group):
+    """pa_decode_tail_merge: tails of 0..32 keys (every block boundary and the empty tail) merged into
+    a prior (output, log-sum-exp) that is sometimes empty, against the fp64 oracle (the tail's
+    attention by ref_decode and ref_lse, the merge written out), and against pa_decode_ex over the
+    tails followed by pa_merge_states."""
+    from paged_kv_cache_427_amd.ops import (make_pool_desc, pa_decode_ex, pa_decode_tail_merge,
+                                            pa_decode_workspace_size, pa_merge_states)
+    from paged_kv_cache_427_amd._lib import PA_BF16, PA_FP8_E4M3
+    from oracle import decode_pool, e4m3_encode, pool_shape
+    rng = np.random.default_rng(4274 + bs + group)
+    lens = np.array([0, 1, 7, 8, 9, 15, 16, 17, 24, 31, 32, 5, 0, 32, 12], dtype=np.int32)
+    n, hkv, d = len(lens), 2, 128
+    hq = hkv * group
+    mb = -(-32 // bs)
+    nblk = n * mb + 3
+    perm = rng.permutation(nblk)
+    tabs = np.zeros((n, mb), dtype=np.int32)
+    for s in range(n):
+        tabs[s] = perm[s * mb:(s + 1) * mb]
+    if kv == "bf16":
+        kvals = rng.normal(size=pool_shape(nblk, hkv, bs, d, "k"))
+        vvals = rng.normal(size=pool_shape(nblk, hkv, bs, d, "v"))
+        kt = torch.as_tensor(kvals, dtype=torch.float32).to(torch.bfloat16)
+        vt = torch.as_tensor(vvals, dtype=torch.float32).to(torch.bfloat16)
+        kd, vd = kt.double().numpy(), vt.double().numpy()
+        ks = vs = 1.0
+        pool = make_pool_desc(nblk, bs, hkv, d, PA_BF16)
+    else:
+        ks, vs = 0.5, 0.25                                # N(0, 1) values stored as e4m3 codes of x / scale
+        codes = [e4m3_encode(rng.normal(size=pool_shape(nblk, hkv, bs, d, w)) / sc).astype(np.uint8)
+                 for w, sc in (("k", ks), ("v", vs))]
+        kt, vt = torch.as_tensor(codes[0]), torch.as_tensor(codes[1])
+        kd, vd = decode_pool(codes[0], "fp8", ks), decode_pool(codes[1], "fp8", vs)
+        pool = make_pool_desc(nblk, bs, hkv, d, PA_FP8_E4M3, k_scale=ks, v_scale=vs)
+    q = torch.as_tensor(rng.normal(size=(n, hq, d)), dtype=torch.float32).to(torch.bfloat16)
+    o_prev = torch.as_tensor(rng.normal(size=(n, hq, d)), dtype=torch.float32)
+    lse_prev = torch.as_tensor(rng.normal(size=(n, hq)) * 3, dtype=torch.float32)
+    lse_prev[1, :] = -np.inf                              # no prior keys, one tail key
+    lse_prev[0, 0] = -np.inf                              # neither: zeros
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    dev = torch.device("cuda")
+    qd, kp, vp = q.to(dev), kt.to(dev), vt.to(dev)
+    td, ld = torch.as_tensor(tabs).to(dev), torch.as_tensor(lens).to(dev)
+    op, lp = o_prev.to(dev), lse_prev.to(dev)
+    out = torch.full((n, hq, d), 5.0, dtype=torch.bfloat16, device=dev)
+    _say("tail merge", kv, "b", bs, "G", group)
+    pa_decode_tail_merge(qd, kp, vp, pool, td, ld, scale, 32, op, lp, out)
+    # the two-call path
+    o_t = torch.empty((n, hq, d), dtype=torch.float32, device=dev)
+    l_t = torch.empty((n, hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(pa_decode_workspace_size(n, hq, d, 32, 0), 1), dtype=torch.uint8, device=dev)
+    pa_decode_ex(qd, None, n, hq, kp, vp, pool, td.data_ptr(), mb, ld, scale, o_t, None, 32, l_t, ws)
+    two = torch.empty((n, hq, d), dtype=torch.float32, device=dev)
+    pa_merge_states(op, lp, o_t, l_t, two)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    qn, on, ln = q.double().numpy(), o_prev.double().numpy(), lse_prev.double().numpy()
+    want = np.zeros((n, hq, d))
+    for s in range(n):
+        L = int(lens[s])
+        k = gather_seq(kd, tabs[s], L, "k")
+        v = gather_seq(vd, tabs[s], L, "v")
+        ot = ref_decode(qn[s:s + 1], [(k, v)], scale)[0]
+        for h in range(hq):
+            lt = ref_lse(qn[s, h], k[:, h // group, :], scale)
+            m = max(ln[s, h], lt)
+            if m == -np.inf:
+                continue
+            wa, wb = np.exp(ln[s, h] - m), np.exp(lt - m)
+            want[s, h] = (on[s, h] * wa + ot[h] * wb) / (wa + wb)
+    tol = TOL_BF16 if kv == "bf16" else 6e-2
+    err = float(np.max(np.abs(got - want)))
+    err2 = float(np.max(np.abs(got - two.double().cpu().numpy())))
+    _say("max err vs oracle", err, "vs decode + merge", err2)
+    assert err <= tol and err2 <= tol
+    assert np.all(got[0, 0] == 0.0)
+    # the empty tail (row 12) keeps the prior output (to bf16)
+    assert np.max(np.abs(got[12] - on[12])) <= 1e-2

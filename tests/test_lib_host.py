@@ -28,7 +28,7 @@ def _header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _header_functions()
-    assert len(names) == 42
+    assert len(names) == 43
     handle = lib()
     for n in names:
         assert hasattr(handle, n), n
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lib().pa_version() >> 16 == 2 and lib().pa_version() & 0xffff >= 1
+    assert lib().pa_version() >> 16 == 2 and lib().pa_version() & 0xffff >= 2
     assert lib().pa_status_str(PA_ERR_OOM) == b"PA_ERR_OOM"
 
 
@@ -805,3 +805,31 @@ def test_read_probe_argument_checks():
     assert L.pa_hbm_read_probe(FAKE, 24, FAKE, None) == PA_ERR_INVALID
     assert L.pa_hbm_read_probe(ctypes.c_void_p(0x10008), 16, FAKE, None) == PA_ERR_INVALID
     assert L.pa_hbm_read_probe(FAKE, 16, ctypes.c_void_p(0x10002), None) == PA_ERR_INVALID
+
+
+def test_tail_merge_argument_checks():
+    """pa_decode_tail_merge takes tails of at most 32 keys (longer ones: pa_decode_ex and
+    pa_merge_states), bf16 q over a bf16 or fp8 pool of head_dim 128, and refuses null or misaligned
+    arguments before any launch."""
+    L = lib()
+
+    def call(q=FAKE, q_dtype=1, pool=None, max_blocks=2, n=1, hq=2, max_tail=20, o_prev=FAKE, out=FAKE,
+             out_dtype=1, tables=FAKE):
+        pool = pool or _pool()
+        return L.pa_decode_tail_merge(q, q_dtype, FAKE, FAKE, ctypes.byref(pool), tables, max_blocks, FAKE, n, hq,
+                                      0.1, max_tail, o_prev, FAKE, out, out_dtype, None)
+
+    assert call(max_tail=33) == PA_ERR_UNSUPPORTED
+    assert "32" in L.pa_last_error().decode()
+    assert call(max_tail=-1) == PA_ERR_INVALID
+    assert call(pool=_pool(dtype=0), q_dtype=0) == PA_ERR_UNSUPPORTED       # f32 pool
+    assert call(pool=_pool(head_dim=64)) == PA_ERR_UNSUPPORTED
+    assert call(hq=3) == PA_ERR_INVALID                                      # not a multiple of the KV heads
+    assert call(hq=32) == PA_ERR_UNSUPPORTED                                 # group of 16
+    assert call(max_blocks=1, max_tail=20) == PA_ERR_INVALID                # 20 keys need 2 blocks of 16
+    assert call(tables=None) == PA_ERR_INVALID
+    assert call(q=ctypes.c_void_p(0x1008)) == PA_ERR_INVALID                # q base 8 bytes past 16
+    assert call(o_prev=ctypes.c_void_p(0x1004)) == PA_ERR_INVALID           # o_prev float2 rows
+    assert call(out=ctypes.c_void_p(0x1002)) == PA_ERR_INVALID              # bf16 pairs
+    assert call(out_dtype=3) == PA_ERR_INVALID
+    assert call(n=0) == 0                                                    # nothing to do
