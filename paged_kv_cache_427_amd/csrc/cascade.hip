@@ -73,24 +73,47 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
   constexpr int NP = BS / 8;                       // 8-token pieces of a V^T row of one block
   constexpr int PW = 2 * E;                        // dwords of one piece (bf16 4, fp8 2)
   const int lane = threadIdx.x & 63;
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) +
+                    __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar reads below
   if (w >= static_cast<int64_t>(a.num_seqs) * a.num_kv_heads) return;
   const int seq = static_cast<int>(w / a.num_kv_heads);
   const int kvh = static_cast<int>(w % a.num_kv_heads);
-  // a length outside [0, max_tail] is clamped, and a block id outside the pool is clamped into it
-  const int L = __builtin_amdgcn_readfirstlane(min(max(a.lens[seq], 0), a.max_tail));
+  // the length and the row's first table entries are read together (the entries before the length
+  // is known, inside the row); a length outside [0, max_tail] is clamped, and a block id outside
+  // the pool is clamped into it
   const int32_t* tab = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
-  int64_t phys[NB];
+  const int len_raw = a.lens[seq];
+  int32_t ent[NB];
 #pragma unroll
-  for (int q = 0; q < NB; ++q)
-    phys[q] = q * BS < L ? min(max(tab[q], 0), a.num_blocks - 1) : 0;
+  for (int q = 0; q < NB; ++q) ent[q] = q < a.max_blocks ? tab[q] : 0;
   const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * TILE;
   const char* kbase = static_cast<const char*>(a.k_pool) + static_cast<int64_t>(kvh) * TILE;
   const char* vbase = static_cast<const char*>(a.v_pool) + static_cast<int64_t>(kvh) * TILE;
   const int64_t row0 = static_cast<int64_t>(seq) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
   const int j = lane & 31, half = lane >> 5;
 
-  // ---- every load first, so that the wave waits on memory once ----
+  // ---- every load first, so that the wave waits on memory once: q (for one head; a larger group
+  // reads each head's q when it dots it, so as not to hold them all) and the prior state, which need
+  // no table entry, then K and V ----
+  auto q_row = [&](int g) __attribute__((always_inline)) {
+    return static_cast<const char*>(a.q) + ((row0 + g) * D + half * 64) * 2;
+  };
+  uint4 q1[8];
+  if constexpr (G == 1) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) q1[c] = *reinterpret_cast<const uint4*>(q_row(0) + 16 * c);
+  }
+  float2 po[G];
+  float lp[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    po[g] = *reinterpret_cast<const float2*>(a.o_prev + (row0 + g) * D + 2 * lane);
+    lp[g] = a.lse_prev[row0 + g];
+  }
+  const int L = __builtin_amdgcn_readfirstlane(min(max(len_raw, 0), a.max_tail));
+  int64_t phys[NB];
+#pragma unroll
+  for (int q = 0; q < NB; ++q) phys[q] = q * BS < L ? min(max(ent[q], 0), a.num_blocks - 1) : 0;
   // K: key j's dims 64 half .. +64 (lane j and lane j + 32); zeros past the tail
   uint32_t kraw[16 * E];   // 64 dims: 32 dwords of bf16, 16 of fp8
 #pragma unroll
@@ -124,20 +147,6 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
           }
         }
       }
-  uint4 qraw[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const char* qrow = static_cast<const char*>(a.q) + ((row0 + g) * D + half * 64) * 2;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qraw[g][c] = *reinterpret_cast<const uint4*>(qrow + 16 * c);
-  }
-  float2 po[G];
-  float lp[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    po[g] = *reinterpret_cast<const float2*>(a.o_prev + (row0 + g) * D + 2 * lane);
-    lp[g] = a.lse_prev[row0 + g];
-  }
 
   // ---- base-2 logits of key j for each head (-inf past the tail) ----
   uint32_t kw[32];   // bf16 pairs of the 64 dims
@@ -157,10 +166,11 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
     float acc = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      acc = dot_bf16x2(kw[4 * c], qraw[g][c].x, acc);
-      acc = dot_bf16x2(kw[4 * c + 1], qraw[g][c].y, acc);
-      acc = dot_bf16x2(kw[4 * c + 2], qraw[g][c].z, acc);
-      acc = dot_bf16x2(kw[4 * c + 3], qraw[g][c].w, acc);
+      const uint4 qv = G == 1 ? q1[c] : *reinterpret_cast<const uint4*>(q_row(g) + 16 * c);
+      acc = dot_bf16x2(kw[4 * c], qv.x, acc);
+      acc = dot_bf16x2(kw[4 * c + 1], qv.y, acc);
+      acc = dot_bf16x2(kw[4 * c + 2], qv.z, acc);
+      acc = dot_bf16x2(kw[4 * c + 3], qv.w, acc);
     }
     acc += shfl_xor(acc, 32);                      // the other half of the dims
     x[g] = j < L ? acc * a.qk_scale : -INFINITY;
