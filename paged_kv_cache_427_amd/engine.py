@@ -24,6 +24,16 @@ def _signed(code: int, bits: int) -> int:
     return code - (1 << bits) if code >= (1 << (bits - 1)) else code
 
 
+def untouched_by_step(blocks: np.ndarray, cow_pairs: np.ndarray, slots: np.ndarray, block_size: int) -> bool:
+    """True when none of `blocks` is a copy destination of the step (cow_pairs rows are (source,
+    destination)) or receives one of its tokens (slot // block_size, slots < 0 unused): a decode
+    that reads only those blocks then gives the same result before the step's copies and writes."""
+    touched = set(np.asarray(cow_pairs).reshape(-1, 2)[:, 1].tolist())
+    slots = np.asarray(slots)
+    touched |= set((slots[slots >= 0] // block_size).tolist())
+    return not (touched & set(np.asarray(blocks).tolist()))
+
+
 def leading_shared_blocks(tables: np.ndarray, lens: np.ndarray, block_size: int) -> np.ndarray:
     """For each row, how many leading entries of its table (within its length) are physical blocks
     that another row of the same batch also reads: the pa_decode_ex `shared_blocks` hint (host,
@@ -209,10 +219,7 @@ class PagedKVEngine:
         wl = self.wl
         si.cascade = CascadeDecode(si.dec_tables.cpu().numpy(), np.asarray(wl.decode_lens, np.int32), wl.block_size,
                                    width, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, self.device)
-        touched = set(si.host_cow[:, 1].tolist()) if len(si.host_cow) else set()
-        if len(si.host_slots):
-            touched |= set((si.host_slots[si.host_slots >= 0] // wl.block_size).tolist())
-        si.cascade_early = not (touched & set(si.cascade.shared_blocks().tolist()))
+        si.cascade_early = untouched_by_step(si.cascade.shared_blocks(), si.host_cow, si.host_slots, wl.block_size)
         si.cascade_shared_done = False
 
     def early_decode_step(self, si: StepInputs, stream=None) -> None:
