@@ -571,8 +571,9 @@ PREFILL_WARMUP_MS = 150.0
 
 def step_bench(args, dev, config, block_size, steps, warmup, partition=None, contiguous=False,
                plain_decode=False, with_cpu=False, prefill_warmup_ms=0.0):
-    """Time `steps` whole steps of one workload (copy-on-write copies, cache write, prefill, decode)
-    after `warmup` untimed ones, each launch bracketed by HIP events on the launch stream."""
+    """Time `steps` whole steps of one workload (copy-on-write copies, cache write, prefill, decode;
+    a beam decode's shared part before the copies) after `warmup` untimed ones, each launch
+    bracketed by HIP events on the launch stream."""
     from paged_kv_cache_427_amd.engine import PagedKVEngine
     t_setup = time.time()
     wl = make_workload(config, "full", device=dev, block_size=block_size)

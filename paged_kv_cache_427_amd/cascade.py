@@ -14,9 +14,9 @@ import torch
 
 from ._lib import PA_F32, check, lib
 from ._lib import _I32P
+from .ops import pa_decode_ex, pa_decode_tail_merge, pa_decode_workspace_size, pa_merge_states
 
 TAIL_MERGE_MAX = 32     # longest tail pa_decode_tail_merge takes
-from .ops import pa_decode_ex, pa_decode_tail_merge, pa_decode_workspace_size, pa_merge_states
 
 
 def plan_shared_blocks(tables: np.ndarray, lens: np.ndarray, block_size: int, width: int) -> np.ndarray:
