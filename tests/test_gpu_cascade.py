@@ -155,9 +155,11 @@ def test_cascade_decode_of_beam_branches(size):
     assert diff <= TOL_BF16
 
 
-@pytest.mark.parametrize("kv,bs,group", [("bf16", 16, 1), ("bf16", 8, 4), ("bf16", 32, 8), ("fp8", 16, 1),
-                                         ("fp8", 8, 2), ("fp8", 32, 4)])
-def test_tail_merge_against_the_oracle(kv, bs, group):
+@pytest.mark.parametrize("kv,bs,group,out_f32", [("bf16", 16, 1, False), ("bf16", 8, 4, False),
+                                                 ("bf16", 32, 8, False), ("fp8", 16, 1, False),
+                                                 ("fp8", 8, 2, False), ("fp8", 32, 4, False),
+                                                 ("bf16", 16, 2, True), ("fp8", 16, 8, True)])
+def test_tail_merge_against_the_oracle(kv, bs, group, out_f32):
     """pa_decode_tail_merge: tails of 0..32 keys (every block boundary and the empty tail) merged into
     a prior (output, log-sum-exp) that is sometimes empty, against the fp64 oracle (the tail's
     attention by ref_decode and ref_lse, the merge written out), and against pa_decode_ex over the
@@ -201,8 +203,8 @@ def test_tail_merge_against_the_oracle(kv, bs, group):
     qd, kp, vp = q.to(dev), kt.to(dev), vt.to(dev)
     td, ld = torch.as_tensor(tabs).to(dev), torch.as_tensor(lens).to(dev)
     op, lp = o_prev.to(dev), lse_prev.to(dev)
-    out = torch.full((n, hq, d), 5.0, dtype=torch.bfloat16, device=dev)
-    _say("tail merge", kv, "b", bs, "G", group)
+    out = torch.full((n, hq, d), 5.0, dtype=torch.float32 if out_f32 else torch.bfloat16, device=dev)
+    _say("tail merge", kv, "b", bs, "G", group, "f32 out" if out_f32 else "bf16 out")
     pa_decode_tail_merge(qd, kp, vp, pool, td, ld, scale, 32, op, lp, out)
     # the two-call path
     o_t = torch.empty((n, hq, d), dtype=torch.float32, device=dev)
@@ -232,6 +234,9 @@ def test_tail_merge_against_the_oracle(kv, bs, group):
     err2 = float(np.max(np.abs(got - two.double().cpu().numpy())))
     _say("max err vs oracle", err, "vs decode + merge", err2)
     assert err <= tol and err2 <= tol
+    if out_f32 and kv == "bf16":
+        # fp32 probabilities, sums and output over the exact bf16 inputs: only fp32 rounding remains
+        assert err <= 1e-4
     assert np.all(got[0, 0] == 0.0)
     # the empty tail (row 12) keeps the prior output (to bf16)
     assert np.max(np.abs(got[12] - on[12])) <= 1e-2
