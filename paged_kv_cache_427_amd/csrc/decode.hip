@@ -768,38 +768,45 @@ __global__ void __launch_bounds__(kThreads, (Pipe<KV, D>::kOcc)) decode_stream_k
 
 // Merge of the partial records of the segments that were split into pieces:
 // out = sum_r o_r 2^(m_r - M) / sum_r l_r 2^(m_r - M) * v_scale, M = max_r m_r.  One wave per
-// (sequence, query head) row, four rows per workgroup: a row whose segment was served by one piece
-// (written by the stream kernel) leaves after reading the plan; an empty one gets zeros (and a -inf
-// log-sum-exp); a split one is merged with its records loaded across the lanes, 64 at a time (the
-// maximum and weighted sum are wave reductions), and each lane then adds its slice of the output
-// dims over the records with many loads in flight.  The records of partition k are those of the
-// shares v0(k)..v1(k) that overlap it, read in that order, so results do not depend on timing.
+// (sequence, KV head) segment and HW of its G query heads (they share the segment's pieces), four
+// waves per workgroup: a segment served by one piece (written by the stream kernel) leaves after
+// reading the plan; an empty one gets zeros (and a -inf log-sum-exp); a split one is merged with its
+// records' (max, sum) loaded across the lanes, 64 pieces at a time, for the wave's HW heads at once
+// (the maximum and weighted sum of each head are wave reductions), and each lane then adds its
+// slice of the output dims of every head over the records with many loads in flight.  The records
+// of partition k are those of the shares v0(k)..v1(k) that overlap it, read in that order, so
+// results do not depend on timing (nor on how many heads a wave serves).
 constexpr int kMergeThreads = 256;
 
-template <int D>
+template <int D, int HW>
 __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a, int out_bf16) {
   constexpr int DPL = D / 64;   // output dims per lane
+  constexpr int kRec = D + 4;   // floats of one head's record
   const int lane = threadIdx.x & 63;
   // workgroup i serves stream i % streams (with 8 streams, the XCD whose stream kernel workgroups
-  // wrote that stream's records, so they are read from its L2); its rows are numbered
-  // (head slot, sequence, head in the group) with the head fastest
+  // wrote that stream's records, so they are read from its L2); its waves are numbered (head slot,
+  // sequence, slice of HW heads in the group) with the slice fastest
   const int G = a.num_q_heads / a.num_kv_heads;
+  const int slices = G / HW;
   const int x = static_cast<int>(blockIdx.x % a.streams);
   const int64_t q = static_cast<int64_t>(blockIdx.x / a.streams) * (kMergeThreads / 64) + (threadIdx.x >> 6);
   const int hpx = a.num_kv_heads / a.streams;
-  if (q >= static_cast<int64_t>(hpx) * a.num_seqs * G) return;
-  const int g = static_cast<int>(q % G);
-  const int seq = static_cast<int>((q / G) % a.num_seqs);
-  const int hh = static_cast<int>(q / (static_cast<int64_t>(G) * a.num_seqs));
+  if (q >= static_cast<int64_t>(hpx) * a.num_seqs * slices) return;
+  const int g0 = static_cast<int>(q % slices) * HW;
+  const int seq = static_cast<int>((q / slices) % a.num_seqs);
+  const int hh = static_cast<int>(q / (static_cast<int64_t>(slices) * a.num_seqs));
   const int kvh = hh * a.streams + x;
   const ro_i32 pref = ro(a.ws_pref);
   const int n = a.num_seqs;
   const int nj = pref[seq + 1] - pref[seq];
-  const int64_t orow = seq * a.o_sseq + kvh * a.o_skv + g * a.o_sg;
+  const int64_t orow0 = seq * a.o_sseq + kvh * a.o_skv + g0 * a.o_sg;
   if (nj == 0) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) store_out(a.out, orow + DPL * lane + e, 0.f, out_bf16 != 0);
-    if (a.lse && lane == 0) a.lse[orow / D] = -INFINITY;
+    for (int g = 0; g < HW; ++g) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) store_out(a.out, orow0 + g * a.o_sg + DPL * lane + e, 0.f, out_bf16 != 0);
+      if (a.lse && lane == 0) a.lse[(orow0 + g * a.o_sg) / D] = -INFINITY;
+    }
     return;
   }
   Sched sc;
@@ -810,10 +817,15 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
   const int nparts = (nj + PU - 1) / PU;
   if (nparts == 1 && sc.share_of(P0) == sc.share_of(P0 + nj - 1)) return;   // one piece
   const int64_t seg = (static_cast<int64_t>(hh) * n + seq) * a.max_parts + x * a.stream_slots;
-  auto rec_of = [&](int k, int vv) { return ((seg + k + vv) * G + g) * (D + 4); };
-  float M = -INFINITY, lsum = 0.f, o[DPL];
+  auto rec_of = [&](int k, int vv) { return ((seg + k + vv) * G + g0) * kRec; };   // head g0 of piece (k, vv)
+  float M[HW], lsum[HW], o[HW][DPL];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  for (int g = 0; g < HW; ++g) {
+    M[g] = -INFINITY;
+    lsum[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[g][e] = 0.f;
+  }
   // pieces in order, walked without divisions: piece (k, vv) ends at the nearer of partition k's
   // end pe and share vv's end nb
   int k = 0, vv = sc.share_of(P0);
@@ -834,56 +846,76 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
         pe = min(pe + PU, seg_end);
       }
     }
-    const float m_r = lane < cnt ? a.ws_part[my_off] : -INFINITY;
-    const float l_r = lane < cnt ? a.ws_part[my_off + 1] : 0.f;
-    float mb = m_r;
+    float m_r[HW], l_r[HW];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mb = fmaxf(mb, shfl_xor(mb, off));
-    const float Mn = fmaxf(M, mb);
-    const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-    const float w_r = lane < cnt ? __builtin_amdgcn_exp2f(m_r - Mn) : 0.f;
-    float ls = l_r * w_r;
+    for (int g = 0; g < HW; ++g) {
+      m_r[g] = lane < cnt ? a.ws_part[my_off + g * kRec] : -INFINITY;
+      l_r[g] = lane < cnt ? a.ws_part[my_off + g * kRec + 1] : 0.f;
+    }
+    uint32_t w_bits[HW];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ls += shfl_xor(ls, off);
-    lsum = lsum * alpha + ls;
+    for (int g = 0; g < HW; ++g) {
+      float mb = m_r[g];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] *= alpha;
+      for (int off = 32; off > 0; off >>= 1) mb = fmaxf(mb, shfl_xor(mb, off));
+      const float Mn = fmaxf(M[g], mb);
+      const float alpha = M[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[g] - Mn);
+      const float w_r = lane < cnt ? __builtin_amdgcn_exp2f(m_r[g] - Mn) : 0.f;
+      float ls = l_r[g] * w_r;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) ls += shfl_xor(ls, off);
+      lsum[g] = lsum[g] * alpha + ls;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[g][e] *= alpha;
+      w_bits[g] = __builtin_bit_cast(uint32_t, w_r);
+      M[g] = Mn;
+    }
     const uint32_t off_lo = static_cast<uint32_t>(my_off), off_hi = static_cast<uint32_t>(my_off >> 32);
-    const uint32_t w_bits = __builtin_bit_cast(uint32_t, w_r);
-    // up to kFly records' loads in flight at a time (slots past cnt load nothing)
-    constexpr int kFly = 16;
+    // up to 16 records' loads in flight at a time over the HW heads (slots past cnt load nothing)
+    constexpr int kFly = HW >= 16 ? 1 : 16 / HW;
     for (int c0 = 0; c0 < cnt; c0 += kFly) {
-      float val[kFly][DPL], wt[kFly];
+      float val[kFly][HW][DPL], wt[kFly][HW];
 #pragma unroll
       for (int j = 0; j < kFly; ++j) {
-        wt[j] = 0.f;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) val[j][e] = 0.f;
+        for (int g = 0; g < HW; ++g) {
+          wt[j][g] = 0.f;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) val[j][g][e] = 0.f;
+        }
         if (c0 + j < cnt) {
           const int c = c0 + j;
           const int64_t r = (static_cast<int64_t>(__builtin_amdgcn_readlane(off_hi, c)) << 32) |
                             __builtin_amdgcn_readlane(off_lo, c);
-          wt[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(w_bits, c));
-          if constexpr (DPL == 2) {
-            const float2 t = *reinterpret_cast<const float2*>(a.ws_part + r + 4 + 2 * lane);
-            val[j][0] = t.x;
-            val[j][1] = t.y;
-          } else {
-            val[j][0] = a.ws_part[r + 4 + lane];
+#pragma unroll
+          for (int g = 0; g < HW; ++g) {
+            wt[j][g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(w_bits[g], c));
+            if constexpr (DPL == 2) {
+              const float2 t = *reinterpret_cast<const float2*>(a.ws_part + r + g * kRec + 4 + 2 * lane);
+              val[j][g][0] = t.x;
+              val[j][g][1] = t.y;
+            } else {
+              val[j][g][0] = a.ws_part[r + g * kRec + 4 + lane];
+            }
           }
         }
       }
 #pragma unroll
       for (int j = 0; j < kFly; ++j)
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[e] += val[j][e] * wt[j];
-    }
-    M = Mn;
-  }
-  const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
+        for (int g = 0; g < HW; ++g)
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) store_out(a.out, orow + DPL * lane + e, o[e] * inv, out_bf16 != 0);
-  if (a.lse && lane == 0) a.lse[orow / D] = (M + __log2f(lsum)) * 0.6931471805599453f;
+          for (int e = 0; e < DPL; ++e) o[g][e] += val[j][g][e] * wt[j][g];
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < HW; ++g) {
+    const int64_t orow = orow0 + g * a.o_sg;
+    const float inv = lsum[g] > 0.f ? a.v_scale / lsum[g] : 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) store_out(a.out, orow + DPL * lane + e, o[g][e] * inv, out_bf16 != 0);
+    if (a.lse && lane == 0) a.lse[orow / D] = (M[g] + __log2f(lsum[g])) * 0.6931471805599453f;
+  }
 }
 
 // Workgroups of the persistent grid: one per CU.  Measured on MI355X against three (what the
@@ -922,10 +954,15 @@ int launch_one(const DecodeArgs& a0, int out_bf16, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return static_cast<int>(e);
   if (a.fill_empty) return 0;
-  const int64_t rows = static_cast<int64_t>(a.num_q_heads / a.streams) * a.num_seqs;   // per stream
-  const int64_t mw = a.streams * ((rows + kMergeThreads / 64 - 1) / (kMergeThreads / 64));   // a wave per row
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<unsigned>(mw)), dim3(kMergeThreads), 0, s, a,
-                     out_bf16);
+  // A wave merges all G heads of a segment when its rows are not partitioned (a few pieces each, at
+  // share boundaries: the beam decode's shared part, G = 8, 20.8 -> 10.7 us), one head when they are
+  // (rows of tens of pieces: whole groups per wave left too few waves for the long GQA decode, whose
+  // decode launch went 564 -> 575 us).
+  const int HW = a.max_parts == 1 ? G : 1;
+  const int64_t waves = static_cast<int64_t>(a.num_kv_heads / a.streams) * a.num_seqs * (G / HW);   // per stream
+  const int64_t mw = a.streams * ((waves + kMergeThreads / 64 - 1) / (kMergeThreads / 64));
+  auto merge = HW == 1 ? decode_merge_kernel<D, 1> : decode_merge_kernel<D, G>;
+  hipLaunchKernelGGL(merge, dim3(static_cast<unsigned>(mw)), dim3(kMergeThreads), 0, s, a, out_bf16);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -97,16 +97,16 @@ def test_batches_at_the_plan_limits(n):
     assert err <= TOL_BF16
 
 
-@pytest.mark.parametrize("partition", [0, 32, 512])
-def test_rows_of_many_pieces(partition):
+@pytest.mark.parametrize("partition,group", [(0, 2), (32, 2), (512, 2), (0, 8)])
+def test_rows_of_many_pieces(partition, group):
     """Two long contexts cut every 32 tokens: over 1024 pieces per (sequence, head), which the merge
     kernel combines 64 records at a time with a running maximum across the batches (and, for
     comparison, the same contexts cut every 512: about 70 pieces, two batches).  Without partitions
     the two contexts are cut only by the waves' shares (a few units each, so again over 1000 pieces
-    per row)."""
+    per row), and one merge wave takes all the heads of a group (2 or 8) through those batches."""
     rng = np.random.Generator(np.random.PCG64(4272))
     gen = torch.Generator().manual_seed(4272)
-    hq, hkv, b, d = 2, 1, 16, 128
+    hq, hkv, b, d = group, 1, 16, 128
     lens = np.array([36000, 33001], dtype=np.int32)
     need = sum(-(-int(L) // b) for L in lens)
     num_blocks = need + 16
@@ -114,7 +114,7 @@ def test_rows_of_many_pieces(partition):
     tabs = _tables(rng, lens, b, num_blocks)
     q = torch.randn((2, hq, d), generator=gen).to(torch.bfloat16)
     scale = float(np.float32(1.0 / np.sqrt(d)))
-    _say("decode, 2 long contexts, partition", partition)
+    _say("decode, 2 long contexts, partition", partition, "group", group)
     got = _decode(q, kpool, vpool, tabs, lens, scale, 36000, partition)
     ref = _oracle_rows(kpool, vpool, tabs, lens, q, scale, [0, 1])
     err = max(float(np.max(np.abs(got[s] - ref[s]))) for s in (0, 1))
