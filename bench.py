@@ -47,7 +47,8 @@ from synth import make_workload, poison_code, elem_bytes  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 # the sources of every decode launch (the stream and merge kernels; the beam decode's tail merge)
-DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_427_amd", "csrc", f) for f in ("decode.hip", "cascade.hip")]
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_427_amd", "csrc", f)
+               for f in ("decode.hip", "cascade.hip", "decode_records.h")]
 
 
 def decode_source_hash() -> str:
@@ -656,8 +657,9 @@ def step_bench(args, dev, config, block_size, steps, warmup, partition=None, con
                            "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of these decode sources, scaled by "
                                              "a device copy of known size, read from the committed profile "
                                              "(null when the source changed since)",
-                           "kernel": ("beam decode: pa_decode_ex over shared blocks + pa_decode_tail_merge "
-                                      "(private tails merged in)" if getattr(si, "cascade", None) is not None else
+                           "kernel": ("beam decode: pa_decode_beam (shared blocks once, left as partial records; "
+                                      "then the private tails with the records folded in)"
+                                      if getattr(si, "cascade", None) is not None else
                                       "pa_decode (stream + merge kernels)"),
                            "algorithmic_bytes_per_launch": int(uniq + other)}
         res["decode_logical_kv_GBps"] = round(logical / (ms_decode * 1e-3) / 1e9, 1)

@@ -84,7 +84,7 @@ const char* pa_status_str(int32_t status);
 const char* pa_last_error(void);
 /* ABI version: (major << 16) | minor (2.0: pa_decode without the cache hint, pa_decode_noalloc;
  * 2.1: pa_validate_*, pa_plan_beam_tails, device-side clamping of block ids; 2.2:
- * pa_decode_tail_merge). */
+ * pa_decode_tail_merge; 2.3: pa_decode_beam). */
 int32_t pa_version(void);
 
 /* ---------------------------------------------------------------------------------------------
@@ -354,6 +354,46 @@ pa_status pa_decode_tail_merge(const void* q, int32_t q_dtype, const void* k_poo
                                const int32_t* tail_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                                int32_t max_tail_len, const float* o_prev, const float* lse_prev, void* out,
                                int32_t out_dtype, pa_stream stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * pa_decode_beam -- the whole beam decode in at most two launches ([day28] §六 question 3): the
+ * shared blocks of each request read once for all its branches, then every branch's private tail of
+ * at most 32 keys, folded into the shared part's partial results as it is read.  The batch is
+ * num_seqs sequences in groups of `width` consecutive branches (the members of one request), one
+ * query head per KV head (H = num_kv_heads of the pool).  For sequence s of group g = s / width and
+ * head h, the keys are those of pa_decode_ex over the shared part followed by those of the tail:
+ *     shared  pool[tables[g * width][j / b]][h][j % b], 0 <= j < shared_lens[g]
+ *     tail    pool[tail_tables[s][j / b]][h][j % b],    0 <= j < tail_lens[s]
+ * and out[s,h,:] = softmax over both key sets of scale q[s,h,:] . K, times V: what pa_decode_ex over
+ * the shared part (the branches as query heads) and pa_decode_tail_merge compute, without the
+ * shared part's output and log-sum-exp ever being written.  A row with neither shared nor tail keys
+ * gets zeros.
+ *   q              device bf16 [num_seqs][H][128], 16-byte aligned; the pool bf16 or fp8
+ *                  (PA_ERR_UNSUPPORTED otherwise, and for head_dim other than 128)
+ *   tables         device int32 [num_seqs][max_blocks_per_seq] (only the rows of each group's first
+ *                  member are read, for their shared blocks); shared_lens device int32 [num_seqs /
+ *                  width], clamped to [0, max_shared_len] on the device
+ *   tail_tables    device int32 [num_seqs][tail_max_blocks]; tail_lens device int32 [num_seqs],
+ *                  clamped to [0, max_tail_len]; max_tail_len at most 32 (PA_ERR_UNSUPPORTED above)
+ *                  (pa_plan_shared_blocks and pa_plan_beam_tails make these from the batch's tables)
+ *   width          2, 4 or 8, dividing num_seqs
+ *   workspace      device memory of at least pa_decode_workspace_size(num_seqs / width, width * H,
+ *                  128, max_shared_len, 0) bytes: the shared part's plan and partial records
+ *   out            device [num_seqs][H][128] of out_dtype (PA_F32 or PA_BF16), two-element aligned
+ *   phases         PA_BEAM_SHARED: the shared part only (it leaves its records in the workspace);
+ *                  PA_BEAM_TAILS: the tails and the output, reading the records that the last
+ *                  PA_BEAM_SHARED call with the same sizes, tables, lengths and workspace left;
+ *                  both: the two in order.  The split lets the shared part run before the step's
+ *                  cache writes and copy-on-write copies, which never touch a shared block; keep
+ *                  the workspace untouched between the two calls.
+ * ------------------------------------------------------------------------------------------- */
+enum { PA_BEAM_SHARED = 1, PA_BEAM_TAILS = 2 };
+pa_status pa_decode_beam(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
+                         const pa_pool_desc* pool, const int32_t* tables, int32_t max_blocks_per_seq,
+                         const int32_t* shared_lens, int32_t max_shared_len, const int32_t* tail_tables,
+                         int32_t tail_max_blocks, const int32_t* tail_lens, int32_t max_tail_len, int32_t num_seqs,
+                         int32_t width, float scale, void* workspace, size_t workspace_bytes, void* out,
+                         int32_t out_dtype, int32_t phases, pa_stream stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Host checks of device-resident inputs (no GPU).  The kernels use these values as given; out of

@@ -8,6 +8,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_HIP, PA_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_BEAM_SHARED, PA_BEAM_TAILS = 1, 2
 
 
 class PoolDesc(ctypes.Structure):
@@ -49,6 +50,9 @@ _PROTOS = {
     "pa_decode_tail_merge": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_int32,
                                        c_void_p, c_int32, c_int32, c_float, c_int32, c_void_p, c_void_p, c_void_p,
                                        c_int32, c_void_p]),
+    "pa_decode_beam": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(PoolDesc), c_void_p, c_int32,
+                                 c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_float,
+                                 c_void_p, c_size_t, c_void_p, c_int32, c_int32, c_void_p]),
     "pa_plan_shared_blocks": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, c_int32, _I32P]),
     "pa_plan_cache_hint": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, _I32P]),
     "pa_plan_beam_tails": (c_int32, [_I32P, c_int32, _I32P, c_int32, c_int32, c_int32, _I32P, _I32P, c_int32, _I32P,

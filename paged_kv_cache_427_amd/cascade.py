@@ -5,18 +5,19 @@ decode reads each shared block once per branch.  Here one pa_decode_ex call read
 of each request once, with the W branches' queries of a KV head as its W query heads (the strides
 pick them out of the batch's q, and write the outputs back to the branches' rows), a second call
 reads each branch's private tail, and pa_merge_states combines the two results by their
-log-sum-exps.  Tails of at most 32 tokens (a beam's tokens since the fork) are decoded and merged
-in one launch instead, pa_decode_tail_merge.  Needs one query head per KV head (the branches then
-fill the group) and W in {2, 4, 8}; the batch is laid out as requests x W consecutive branches.
+log-sum-exps.  Tails of at most 32 tokens (a beam's tokens since the fork) take pa_decode_beam
+instead: the shared part leaves its partial results in the workspace, and one tail launch folds
+them into each branch's row as it reads the tail.  Needs one query head per KV head (the branches
+then fill the group) and W in {2, 4, 8}; the batch is laid out as requests x W consecutive branches.
 """
 import numpy as np
 import torch
 
-from ._lib import PA_F32, check, lib
+from ._lib import PA_BEAM_SHARED, PA_BEAM_TAILS, PA_F32, check, lib
 from ._lib import _I32P
-from .ops import pa_decode_ex, pa_decode_tail_merge, pa_decode_workspace_size, pa_merge_states
+from .ops import pa_decode_beam, pa_decode_ex, pa_decode_workspace_size, pa_merge_states
 
-TAIL_MERGE_MAX = 32     # longest tail pa_decode_tail_merge takes
+TAIL_MERGE_MAX = 32     # longest tail pa_decode_beam takes
 
 
 def plan_shared_blocks(tables: np.ndarray, lens: np.ndarray, block_size: int, width: int) -> np.ndarray:
@@ -93,8 +94,21 @@ class CascadeDecode:
         self.run_shared(q, k_pool, v_pool, pool, scale, stream)
         self.run_tails(q, k_pool, v_pool, pool, scale, out, stream)
 
+    def beam_call(self, pool) -> bool:
+        """Whether pa_decode_beam serves this decode (tails of at most 32 tokens, bf16 or fp8 pool, head
+        dim 128); else pa_decode_ex over each part and pa_merge_states."""
+        return self.tail_max <= TAIL_MERGE_MAX and pool.dtype != PA_F32 and self.d == 128
+
+    def _beam(self, q, k_pool, v_pool, pool, scale, out, phases, stream):
+        pa_decode_beam(q, k_pool, v_pool, pool, self.tables, self.pre_lens, max(self.pre_max, 1), self.tail_tables,
+                       self.tail_lens, self.tail_max, self.width, scale, self.workspace, out, phases, stream)
+
     def run_shared(self, q: torch.Tensor, k_pool, v_pool, pool, scale: float, stream=None) -> None:
-        """The shared part: each request's shared blocks once, for all its branches (into o_pre, l_pre)."""
+        """The shared part: each request's shared blocks once, for all its branches (left as partial
+        results in the workspace, or written to o_pre, l_pre)."""
+        if self.beam_call(pool):
+            self._beam(q, k_pool, v_pool, pool, scale, self.o_pre, PA_BEAM_SHARED, stream)
+            return
         W, hq, d = self.width, self.hq, self.d
         # rows of group g: sequence stride W*hq*d; KV head stride d; branch (head in the group) stride hq*d
         strides = (W * hq * d, d, hq * d)
@@ -105,10 +119,9 @@ class CascadeDecode:
     def run_tails(self, q: torch.Tensor, k_pool, v_pool, pool, scale: float, out: torch.Tensor, stream=None) -> None:
         """The private tails, merged with the shared part's result into out."""
         hq, d = self.hq, self.d
-        if self.tail_max <= TAIL_MERGE_MAX and pool.dtype != PA_F32 and d == 128:
-            # short tails: their attention and the merge with the shared part in one launch
-            pa_decode_tail_merge(q, k_pool, v_pool, pool, self.tail_tables, self.tail_lens, scale, self.tail_max,
-                                 self.o_pre, self.l_pre, out, stream=stream)
+        if self.beam_call(pool):
+            # short tails: their attention and the fold of the shared part's partial results, one launch
+            self._beam(q, k_pool, v_pool, pool, scale, out, PA_BEAM_TAILS, stream)
             return
         pa_decode_ex(q, None, self.n, hq, k_pool, v_pool, pool, self.tail_tables.data_ptr(),
                      int(self.tail_tables.shape[1]), self.tail_lens, scale, self.o_tail, None,

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 
 #include "pa.h"
@@ -441,6 +442,112 @@ pa_status pa_decode_tail_merge(const void* q, int32_t q_dtype, const void* k_poo
   a.out = out;
   return launch_status(pa::launch_tail_merge(a, pool->dtype, pool->block_size, pool->head_dim, out_dtype, stream),
                        "pa_decode_tail_merge: no kernel for this combination");
+}
+
+pa_status pa_decode_beam(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
+                         const pa_pool_desc* pool, const int32_t* tables, int32_t max_blocks,
+                         const int32_t* shared_lens, int32_t max_shared_len, const int32_t* tail_tables,
+                         int32_t tail_max_blocks, const int32_t* tail_lens, int32_t max_tail_len, int32_t num_seqs,
+                         int32_t width, float scale, void* workspace, size_t workspace_bytes, void* out,
+                         int32_t out_dtype, int32_t phases, pa_stream stream) {
+  pa_status st = check_pool(pool, "pa_decode_beam");
+  if (st != PA_OK) return st;
+  if (phases != PA_BEAM_SHARED && phases != PA_BEAM_TAILS && phases != (PA_BEAM_SHARED | PA_BEAM_TAILS))
+    return pa_fail(PA_ERR_INVALID, "pa_decode_beam: phases must be PA_BEAM_SHARED, PA_BEAM_TAILS or both");
+  if (width != 2 && width != 4 && width != 8)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_beam: width must be 2, 4 or 8");
+  if (num_seqs < 0 || num_seqs % width != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_beam: num_seqs must be a non-negative multiple of width");
+  if (q_dtype != PA_BF16 || pool->dtype == PA_F32)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_beam: needs bf16 q and a bf16 or fp8 pool");
+  if (pool->head_dim != 128) return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_beam: head_dim must be 128");
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return pa_fail(PA_ERR_INVALID, "pa_decode_beam: bad out_dtype");
+  if (!std::isfinite(scale)) return pa_fail(PA_ERR_INVALID, "pa_decode_beam: scale is not finite");
+  if (max_shared_len < 0 || max_tail_len < 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_beam: negative max_shared_len or max_tail_len");
+  if (max_tail_len > 32)
+    return pa_fail(PA_ERR_UNSUPPORTED,
+                   "pa_decode_beam: tails of more than 32 keys (use pa_decode_ex and pa_merge_states)");
+  const int32_t b = pool->block_size;
+  if (max_blocks <= 0 || max_blocks < (static_cast<int64_t>(max_shared_len) + b - 1) / b)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_beam: max_blocks_per_seq < ceil(max_shared_len / block_size)");
+  if (static_cast<int64_t>(max_blocks) * width > INT32_MAX)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_beam: max_blocks_per_seq * width exceeds 2^31 - 1");
+  if (tail_max_blocks <= 0 || tail_max_blocks < (max_tail_len + b - 1) / b)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_beam: tail_max_blocks < ceil(max_tail_len / block_size)");
+  const int32_t groups = num_seqs / width;
+  const int32_t heads = pool->num_kv_heads;
+  if (groups > kMaxGridYZ || heads > kMaxGridYZ)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_beam: more than 65535 groups or KV heads in one call");
+  if (static_cast<int64_t>(heads) * groups * ((static_cast<int64_t>(max_shared_len) + 31) / 32) >= (int64_t(1) << 31))
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_beam: more than 2^31 32-key units of shared K/V in one call");
+  size_t need = 0;
+  st = pa_decode_workspace_size(groups, width * heads, pool->head_dim, max_shared_len, 0, &need);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return pa_ok();
+  if (!workspace || workspace_bytes < need)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_beam: workspace missing or smaller than pa_decode_workspace_size");
+  if (!q || !k_pool || !v_pool || !tables || !shared_lens || !tail_tables || !tail_lens || !out)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_beam: null pointer");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_beam: q must start at a 16-byte boundary");
+  if (reinterpret_cast<uintptr_t>(out) % (2 * elem_bytes(out_dtype)) != 0)
+    return pa_fail(PA_ERR_INVALID, "pa_decode_beam: out must start at a boundary of 2 elements");
+  const int64_t D = pool->head_dim;
+  const float kscale = pool->dtype == PA_FP8_E4M3 ? pool->k_scale : 1.0f;
+  const float qk_scale = static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
+  const float v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+  // The shared part: group g's width branches are the query heads of each KV head, over the table row
+  // of its first branch; every piece is left as a partial record in the workspace.
+  pa::DecodeArgs r{};
+  r.q = q;
+  r.k_pool = k_pool;
+  r.v_pool = v_pool;
+  r.tables = tables;
+  r.max_blocks = max_blocks * width;
+  r.lens = shared_lens;
+  r.num_seqs = groups;
+  r.num_q_heads = width * heads;
+  r.num_kv_heads = heads;
+  r.num_blocks = pool->num_blocks;
+  r.qk_scale = qk_scale;
+  r.v_scale = v_scale;
+  r.part_tokens = decode_partition(max_shared_len, 0);
+  r.max_parts = static_cast<int32_t>(decode_max_parts(max_shared_len, r.part_tokens));
+  r.max_ctx = max_shared_len;
+  r.records_only = 1;
+  pa::decode_workspace_carve(r, workspace);
+  r.q_sseq = width * heads * D;   // group
+  r.q_skv = D;                    // KV head
+  r.q_sg = heads * D;             // branch
+  pa::decode_launch_shape(r, pool->dtype);
+  if (phases & PA_BEAM_SHARED) {
+    st = launch_status(pa::launch_decode(r, pool->dtype, q_dtype, out_dtype, b, pool->head_dim, stream),
+                       "pa_decode_beam: no decode kernel for this combination");
+    if (st != PA_OK) return st;
+  }
+  if (phases & PA_BEAM_TAILS) {
+    pa::TailMergeArgs t{};
+    t.q = q;
+    t.k_pool = k_pool;
+    t.v_pool = v_pool;
+    t.tables = tail_tables;
+    t.max_blocks = tail_max_blocks;
+    t.lens = tail_lens;
+    t.num_seqs = num_seqs;
+    t.num_q_heads = heads;
+    t.num_kv_heads = heads;
+    t.num_blocks = pool->num_blocks;
+    t.qk_scale = qk_scale;
+    t.v_scale = v_scale;
+    t.max_tail = max_tail_len;
+    t.out = out;
+    t.width = width;
+    t.shared = r;
+    st = launch_status(pa::launch_tail_merge(t, pool->dtype, b, pool->head_dim, out_dtype, stream),
+                       "pa_decode_beam: no tail kernel for this combination");
+  }
+  return st;
 }
 
 pa_status pa_prefill_chunk(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,

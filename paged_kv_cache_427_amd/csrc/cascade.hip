@@ -11,11 +11,15 @@
 //    (sequence, KV head).  Lane j and lane j + 32 dot key j's two halves of the dims with the G query
 //    heads (packed bf16 dots, fp32 sums); the softmax is a reduction over 32 lanes; each lane then adds
 //    two output dims over the keys, the probabilities read from their lanes as scalars, in fp32;
-//    and the shared part's (output, log-sum-exp) is folded in before the row is written.
+//    and the shared part's (output, log-sum-exp) is folded in before the row is written.  In records
+//    mode (pa_decode_beam) the shared part is the partial records a records_only decode launch left
+//    in its workspace: the wave walks its row's pieces as the decode's merge kernel would and folds
+//    them in, so the shared part needs neither an output nor a merge launch.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 
+#include "decode_records.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -64,7 +68,7 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-template <int KV, int BS, int G>
+template <int KV, int BS, int G, bool REC>
 __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, int out_bf16) {
   constexpr int D = 128;
   constexpr int E = KV == kBF16 ? 2 : 1;
@@ -81,11 +85,40 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
   // the length and the row's first table entries are read together (the entries before the length
   // is known, inside the row); a length outside [0, max_tail] is clamped, and a block id outside
   // the pool is clamped into it
+  // records mode: the plan of this row's shared segment (sequence seq / width, KV head kvh), read
+  // first so that its loads are in flight beside the tail's (width and the stream count are powers
+  // of two)
+  int rec_nj = 0, rec_p0 = 0, rec_s = 1, rec_pu = 1, rec_grp = 0, rec_x = 0, rec_hh = 0;
+  int p_lo = 0, p_hi = 0, p_all = 0;
+  if constexpr (REC) {
+    const DecodeArgs& r = a.shared;
+    const int wl2 = __builtin_ctz(static_cast<unsigned>(a.width));
+    const int sl2 = __builtin_ctz(static_cast<unsigned>(r.streams));
+    rec_grp = seq >> wl2;
+    rec_x = kvh & (r.streams - 1);
+    rec_hh = kvh >> sl2;
+    const ro_i32 pref = ro(r.ws_pref);
+    p_lo = pref[rec_grp];
+    p_hi = pref[rec_grp + 1];
+    p_all = pref[r.num_seqs];
+    rec_s = ro(r.ws_sched)[0];
+    rec_pu = r.part_tokens / kDecodeUnit;
+  }
   const int32_t* tab = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   const int len_raw = a.lens[seq];
-  int32_t ent[NB];
+  int32_t ent[NB];   // entries past the row's width read its last entry again and are set to 0
 #pragma unroll
-  for (int q = 0; q < NB; ++q) ent[q] = q < a.max_blocks ? tab[q] : 0;
+  for (int q = 0; q < NB; ++q) {
+    const int32_t e = ro(tab)[min(q, a.max_blocks - 1)];
+    ent[q] = q < a.max_blocks ? e : 0;
+  }
+  if constexpr (REC) {
+    // the plan's loads complete with the table entries' (one wait before the K/V loads are issued),
+    // instead of being sunk to their first use after those loads
+    asm volatile("" ::"s"(p_lo), "s"(p_hi), "s"(p_all), "s"(rec_s), "s"(rec_pu));
+    rec_nj = p_hi - p_lo;
+    rec_p0 = rec_hh * p_all + p_lo;
+  }
   const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * TILE;
   const char* kbase = static_cast<const char*>(a.k_pool) + static_cast<int64_t>(kvh) * TILE;
   const char* vbase = static_cast<const char*>(a.v_pool) + static_cast<int64_t>(kvh) * TILE;
@@ -105,10 +138,12 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
   }
   float2 po[G];
   float lp[G];
+  if constexpr (!REC) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    po[g] = *reinterpret_cast<const float2*>(a.o_prev + (row0 + g) * D + 2 * lane);
-    lp[g] = a.lse_prev[row0 + g];
+    for (int g = 0; g < G; ++g) {
+      po[g] = *reinterpret_cast<const float2*>(a.o_prev + (row0 + g) * D + 2 * lane);
+      lp[g] = a.lse_prev[row0 + g];
+    }
   }
   const int L = __builtin_amdgcn_readfirstlane(min(max(len_raw, 0), a.max_tail));
   int64_t phys[NB];
@@ -147,6 +182,61 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
           }
         }
       }
+
+  // ---- records mode: fold the shared part's pieces of this row (usually one or two) into a base-2
+  // maximum ms, a sum ls and unnormalised dims os, a few pieces' loads in flight at a time ----
+  float ms = -INFINITY, ls = 0.f;
+  float2 os = make_float2(0.f, 0.f);
+  if constexpr (REC) {
+    static_assert(G == 1, "records mode serves one query head per KV head");
+    const DecodeArgs& r = a.shared;
+    if (rec_nj > 0) {
+      constexpr int kRec = D + 4;
+      constexpr int kB = 4;
+      const int gs = seq & (a.width - 1);
+      PieceWalk walk;
+      walk.init(segment_slot(r, rec_x, rec_hh, rec_grp), rec_p0, rec_nj, rec_pu, rec_s);
+      while (!walk.done()) {
+        // up to kB pieces; the loads of every slot are issued unconditionally (slots past cnt read
+        // piece 0 again and are then ignored), so no load waits on a branch
+        int64_t off[kB];
+        int cnt = 0;
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          if (b == 0 || !walk.done()) {
+            off[b] = (walk.next() * a.width + gs) * kRec;
+            cnt = b + 1;
+          } else {
+            off[b] = off[0];
+          }
+        }
+        float mj[kB], lj[kB];
+        float2 oj[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          const float2 ml = *reinterpret_cast<const float2*>(r.ws_part + off[b]);   // (max, sum)
+          oj[b] = *reinterpret_cast<const float2*>(r.ws_part + off[b] + 4 + 2 * lane);
+          mj[b] = b < cnt ? ml.x : -INFINITY;
+          lj[b] = ml.y;
+        }
+        float mn = ms;
+#pragma unroll
+        for (int b = 0; b < kB; ++b) mn = fmaxf(mn, mj[b]);
+        const float alpha = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - mn);
+        ls *= alpha;
+        os.x *= alpha;
+        os.y *= alpha;
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          const float wb = b < cnt && mj[b] != -INFINITY ? __builtin_amdgcn_exp2f(mj[b] - mn) : 0.f;
+          ls += lj[b] * wb;
+          os.x += oj[b].x * wb;
+          os.y += oj[b].y * wb;
+        }
+        ms = mn;
+      }
+    }
+  }
 
   // ---- base-2 logits of key j for each head (-inf past the tail) ----
   uint32_t kw[32];   // bf16 pairs of the 64 dims
@@ -224,21 +314,34 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
         }
       }
     }
-  // ---- fold in the prior (output, natural log-sum-exp) and write the row ----
+  // ---- fold in the prior (output, natural log-sum-exp; or, in records mode, its maximum, sum and
+  // unnormalised dims) and write the row ----
   constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int64_t r = row0 + g;
-    const float lpb = lp[g] * kLog2e;                           // base 2
-    const float lt = L > 0 ? m[g] + __log2f(l[g]) : -INFINITY;
-    const float M = fmaxf(lpb, lt);
     float r0v = 0.f, r1v = 0.f;
-    if (M != -INFINITY) {
-      const float wp = __builtin_amdgcn_exp2f(lpb - M);         // 0 when the prior is empty
-      const float wt = L > 0 ? __builtin_amdgcn_exp2f(m[g] - M) : 0.f;   // weight of the sums o
-      const float inv = 1.f / (wp + wt * l[g]);
-      r0v = (po[g].x * wp + o[g][0] * wt * a.v_scale) * inv;
-      r1v = (po[g].y * wp + o[g][1] * wt * a.v_scale) * inv;
+    if constexpr (REC) {
+      const float M = fmaxf(ms, L > 0 ? m[g] : -INFINITY);
+      if (M != -INFINITY) {
+        const float wp = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);   // weight of os, ls
+        const float wt = L > 0 ? __builtin_amdgcn_exp2f(m[g] - M) : 0.f;           // weight of o, l
+        const float den = ls * wp + l[g] * wt;
+        const float inv = den > 0.f ? a.v_scale / den : 0.f;
+        r0v = (os.x * wp + o[g][0] * wt) * inv;
+        r1v = (os.y * wp + o[g][1] * wt) * inv;
+      }
+    } else {
+      const float lpb = lp[g] * kLog2e;                           // base 2
+      const float lt = L > 0 ? m[g] + __log2f(l[g]) : -INFINITY;
+      const float M = fmaxf(lpb, lt);
+      if (M != -INFINITY) {
+        const float wp = __builtin_amdgcn_exp2f(lpb - M);         // 0 when the prior is empty
+        const float wt = L > 0 ? __builtin_amdgcn_exp2f(m[g] - M) : 0.f;   // weight of the sums o
+        const float inv = 1.f / (wp + wt * l[g]);
+        r0v = (po[g].x * wp + o[g][0] * wt * a.v_scale) * inv;
+        r1v = (po[g].y * wp + o[g][1] * wt * a.v_scale) * inv;
+      }
     }
     if (out_bf16) {
       static_cast<uint32_t*>(a.out)[r * (D / 2) + lane] = f32_to_bf16_bits(r0v) | (f32_to_bf16_bits(r1v) << 16);
@@ -250,11 +353,16 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
 
 template <int KV, int BS>
 int launch_tail_g(const TailMergeArgs& a, int ob, hipStream_t s, unsigned blocks) {
+  if (a.width > 0) {
+    if (a.num_q_heads != a.num_kv_heads) return -1;
+    hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 1, true>), dim3(blocks), dim3(kThreads), 0, s, a, ob);
+    return static_cast<int>(hipGetLastError());
+  }
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 1>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
-    case 2: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 2>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
-    case 4: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 4>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
-    case 8: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 8>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 1: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 1, false>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 2: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 2, false>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 4: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 4, false>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 8: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 8, false>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
     default: return -1;
   }
   return static_cast<int>(hipGetLastError());

@@ -48,6 +48,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "decode_records.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -72,7 +73,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kUnit = 32;          // keys per unit of one wave (two 16x16 S^T tiles)
+constexpr int kUnit = kDecodeUnit; // keys per unit of one wave (two 16x16 S^T tiles)
 constexpr float kSlack = 8.0f;     // log2 of the growth allowed before the accumulators are rescaled
 
 template <int KV>
@@ -110,12 +111,9 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float x, bool bf
     static_cast<float*>(out)[i] = x;
 }
 
-// Integer inputs that no kernel of a decode launch writes while it runs (tables, lengths, the
-// plan), read through the constant address space: the compiler keeps uniform reads of them on the
-// scalar unit even where the kernel also stores or counts atomically, so they never wait behind the
-// K/V loads in flight.
-typedef const int32_t __attribute__((address_space(4)))* ro_i32;
-__device__ __forceinline__ ro_i32 ro(const int32_t* p) { return (ro_i32)p; }
+// Tables, lengths and the plan are read through ro() (the constant address space): the compiler
+// keeps uniform reads of them on the scalar unit even where the kernel also stores or counts
+// atomically, so they never wait behind the K/V loads in flight.
 
 // Key order inside a unit.  Row i of the unit's S^T tile t is key 8*(i/4) + 4t + i%4, so the
 // accumulator rows 4kg..4kg+3 of both tiles -- what lane group kg holds -- are keys 8kg..8kg+7: the
@@ -552,7 +550,7 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs& a, int out_bf16, 
   l += shfl_xor(l, 32);
   const int kvh = x + a.streams * c.hh;
   if (i >= G) return;
-  if (c.j == 0 && np == c.nj) {
+  if (!a.records_only && c.j == 0 && np == c.nj) {
     const float inv = l > 0.f ? a.v_scale / l : 0.f;
     const int64_t base = c.seq * a.o_sseq + kvh * a.o_skv + i * a.o_sg;
     if (a.lse && kg == 0) a.lse[base / D] = (st.m + __log2f(l)) * 0.6931471805599453f;
@@ -568,8 +566,7 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs& a, int out_bf16, 
       }
     }
   } else {
-    const int64_t slot = x * a.stream_slots +
-                         (static_cast<int64_t>(c.hh) * a.num_seqs + c.seq) * a.max_parts + c.j / PU + share;
+    const int64_t slot = segment_slot(a, x, c.hh, c.seq) + c.j / PU + share;
     float* rec = a.ws_part + (slot * G + i) * (D + 4);
     if (kg == 0) *reinterpret_cast<float4*>(rec) = make_float4(st.m, l, 0.f, 0.f);
 #pragma unroll
@@ -816,8 +813,6 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
   const int PU = a.part_tokens / kUnit;
   const int nparts = (nj + PU - 1) / PU;
   if (nparts == 1 && sc.share_of(P0) == sc.share_of(P0 + nj - 1)) return;   // one piece
-  const int64_t seg = (static_cast<int64_t>(hh) * n + seq) * a.max_parts + x * a.stream_slots;
-  auto rec_of = [&](int k, int vv) { return ((seg + k + vv) * G + g0) * kRec; };   // head g0 of piece (k, vv)
   float M[HW], lsum[HW], o[HW][DPL];
 #pragma unroll
   for (int g = 0; g < HW; ++g) {
@@ -826,25 +821,14 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[g][e] = 0.f;
   }
-  // pieces in order, walked without divisions: piece (k, vv) ends at the nearer of partition k's
-  // end pe and share vv's end nb
-  int k = 0, vv = sc.share_of(P0);
-  int pe = P0 + min(PU, nj), nb = (vv + 1) * sc.S;
-  const int seg_end = P0 + nj;
-  while (k < nparts) {
-    int64_t my_off = 0;
+  PieceWalk walk;
+  walk.init(segment_slot(a, x, hh, seq), P0, nj, PU, sc.S);
+  while (!walk.done()) {
+    int64_t my_off = 0;   // head g0 of the lane's piece
     int cnt = 0;
-    for (; cnt < 64 && k < nparts; ++cnt) {
-      if (lane == cnt) my_off = rec_of(k, vv);
-      const int e = min(pe, nb);
-      if (e == nb) {
-        ++vv;
-        nb += sc.S;
-      }
-      if (e == pe) {
-        ++k;
-        pe = min(pe + PU, seg_end);
-      }
+    for (; cnt < 64 && !walk.done(); ++cnt) {
+      const int64_t slot = walk.next();
+      if (lane == cnt) my_off = (slot * G + g0) * kRec;
     }
     float m_r[HW], l_r[HW];
 #pragma unroll
@@ -934,15 +918,7 @@ int grid_workgroups(int per_cu) { return std::max(8, device_cus() * per_cu / 8 *
 template <int KV, int D, int BS, int G>
 int launch_one(const DecodeArgs& a0, int out_bf16, hipStream_t s) {
   DecodeArgs a = a0;
-  const int64_t wgs = grid_workgroups(a.max_ctx <= kShortCtx ? Pipe<KV, D>::kOcc : 1);   // resident, multiple of 8
-  a.streams = a.num_kv_heads % 8 == 0 ? 8 : 1;
-  a.stream_waves = static_cast<int32_t>(wgs / a.streams * kWaves);
-  a.max_shares = kSharesPerWave * a.stream_waves;   // bounds the share count V
-  a.self_plan = a.num_seqs <= kSelfPlanMax;
-  // One-unit contexts are never split, so no piece needs merging: the stream kernel then writes the
-  // zeros of empty sequences itself and the merge launch is left out.
-  a.fill_empty = a.self_plan && a.max_ctx <= kUnit;
-  a.stream_slots = static_cast<int64_t>(a.num_kv_heads / a.streams) * a.num_seqs * a.max_parts + a.max_shares;
+  const int64_t wgs = decode_launch_shape(a, KV);
   hipError_t e;
   if (!a.self_plan) {
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
@@ -953,7 +929,7 @@ int launch_one(const DecodeArgs& a0, int out_bf16, hipStream_t s) {
                      a, out_bf16);
   e = hipGetLastError();
   if (e != hipSuccess) return static_cast<int>(e);
-  if (a.fill_empty) return 0;
+  if (a.fill_empty || a.records_only) return 0;
   // A wave merges all G heads of a segment when its rows are not partitioned (a few pieces each, at
   // share boundaries: the beam decode's shared part, G = 8, 20.8 -> 10.7 us), one head when they are
   // (rows of tens of pieces: whole groups per wave left too few waves for the long GQA decode, whose
@@ -999,6 +975,20 @@ int pick_dim(const DecodeArgs& a, int bs, int d, int out_bf16, hipStream_t s) {
 }  // namespace
 
 int decode_max_waves() { return grid_workgroups(kMaxOcc) * kWaves; }
+
+int64_t decode_launch_shape(DecodeArgs& a, int kv_dtype) {
+  const int occ = kv_dtype == kF32 ? Pipe<kF32, 128>::kOcc : Pipe<kBF16, 128>::kOcc;
+  const int64_t wgs = grid_workgroups(a.max_ctx <= kShortCtx ? occ : 1);   // resident, multiple of 8
+  a.streams = a.num_kv_heads % 8 == 0 ? 8 : 1;
+  a.stream_waves = static_cast<int32_t>(wgs / a.streams * kWaves);
+  a.max_shares = kSharesPerWave * a.stream_waves;   // bounds the share count V
+  a.self_plan = a.num_seqs <= kSelfPlanMax;
+  // One-unit contexts are never split, so no piece needs merging: the stream kernel then writes the
+  // zeros of empty sequences itself and the merge launch is left out.
+  a.fill_empty = !a.records_only && a.self_plan && a.max_ctx <= kUnit;
+  a.stream_slots = static_cast<int64_t>(a.num_kv_heads / a.streams) * a.num_seqs * a.max_parts + a.max_shares;
+  return wgs;
+}
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 

@@ -72,6 +72,8 @@ struct DecodeArgs {
   int32_t max_shares;    // bound on the shares of one stream
   int32_t self_plan;     // 1: the stream kernel plans the launch itself (no plan kernel)
   int32_t fill_empty;    // 1: no merge launch; the stream kernel writes the zeros of empty sequences
+  int32_t records_only;  // 1: every piece, a whole segment too, is left as a partial record (no output,
+                         // no merge launch) for a later kernel to fold (the beam decode's tails)
   int64_t stream_slots;  // partial-record slots per stream
   int32_t* ws_pref;      // [num_seqs + 1] units (32 keys) of sequences before s, for one KV head
   int32_t* ws_sched;     // share size, share count
@@ -91,6 +93,10 @@ size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t hea
                               int64_t waves);
 // Waves of one decode launch on the current device (an upper bound for any dtype).
 int decode_max_waves();
+// The launch shape of a decode (streams, waves per stream, share bound, plan mode, record slots),
+// set in `a` from its sizes, the pool dtype and the device only, so that a later launch over the
+// same sizes finds this launch's records.  Returns the stream kernel's workgroups.
+int64_t decode_launch_shape(DecodeArgs& a, int kv_dtype);
 // Compute units of the current device (cached per device; 256 when the query fails).
 int device_cus();
 // Sets the workspace pointers of `a` (num_seqs set) inside a workspace of decode_workspace_bytes().
@@ -149,6 +155,11 @@ struct TailMergeArgs {
   const float* o_prev;   // [num_seqs][num_q_heads][128] normalised output over the other keys
   const float* lse_prev; // [num_seqs][num_q_heads] their natural log-sum-exp
   void* out;             // [num_seqs][num_q_heads][128] of out dtype
+  // Records mode (width > 0, one query head per KV head): the other keys' state is read from the
+  // partial records of `shared`, a records_only decode launch over groups of `width` consecutive
+  // sequences (row (s, h) is head s % width of segment (s / width, h)); o_prev and lse_prev unused.
+  int32_t width;
+  DecodeArgs shared;
 };
 // Returns 0 on success, -1 when no kernel exists for the combination, else a hipError_t.
 int launch_tail_merge(const TailMergeArgs& a, int kv_dtype, int block_size, int head_dim, int out_dtype,

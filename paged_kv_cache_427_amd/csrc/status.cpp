@@ -34,6 +34,6 @@ const char* pa_status_str(int32_t s) {
 
 const char* pa_last_error(void) { return g_err; }
 
-int32_t pa_version(void) { return (2 << 16) | 2; }
+int32_t pa_version(void) { return (2 << 16) | 3; }
 
 }  // extern "C"

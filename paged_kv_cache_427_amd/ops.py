@@ -233,6 +233,31 @@ def pa_decode_tail_merge(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Te
                                      _dev(out, "out"), pa_dtype(out), _stream(stream)))
 
 
+def pa_decode_beam(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc,
+                   tables: torch.Tensor, shared_lens: torch.Tensor, max_shared_len: int, tail_tables: torch.Tensor,
+                   tail_lens: torch.Tensor, max_tail_len: int, width: int, scale: float, workspace: torch.Tensor,
+                   out: torch.Tensor, phases: int = 3, stream=None) -> None:
+    """Beam decode of q bf16 [num_seqs, H, 128] (groups of `width` consecutive branches): each group's
+    shared blocks (tables int32 [num_seqs, max_blocks], the first member's row; shared_lens int32
+    [num_seqs / width]) once for all its branches, then each branch's tail of at most 32 keys
+    (tail_tables int32 [num_seqs, tail_max_blocks], tail_lens int32 [num_seqs]) folded in, into out.
+    phases: 1 the shared part only, 2 the tails (after a phase-1 call on the same workspace), 3 both."""
+    num_seqs, heads, head_dim = q.shape
+    for name, t in (("tables", tables), ("shared_lens", shared_lens), ("tail_tables", tail_tables),
+                    ("tail_lens", tail_lens)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if out.numel() != q.numel():
+        raise ValueError("out must have q's shape")
+    check(lib().pa_decode_beam(_dev(q, "q"), pa_dtype(q), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                               ctypes.byref(pool), _dev(tables, "tables"), int(tables.shape[1]),
+                               _dev(shared_lens, "shared_lens"), int(max_shared_len), _dev(tail_tables, "tail_tables"),
+                               int(tail_tables.shape[1]), _dev(tail_lens, "tail_lens"), int(max_tail_len),
+                               int(num_seqs), int(width), float(scale), _dev(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(), _dev(out, "out"), pa_dtype(out),
+                               int(phases), _stream(stream)))
+
+
 def pa_prefill_chunk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pool: PoolDesc,
                      block_tables: torch.Tensor, query_start_loc: torch.Tensor,
                      prior_context_lens: torch.Tensor, scale: float, max_chunk_len: int, out: torch.Tensor,
