@@ -7,9 +7,9 @@
 // query heads of each KV head), read each private tail on its own, and combine the two results of
 // every row with their log-sum-exps: the same rescaled combination as the merge of split pieces.
 //  * merge_states_kernel: one thread per 4 dims of a row, an HBM-bound elementwise pass;
-//  * tail_merge_kernel: the tail of at most 32 keys and the merge in one pass, one wave per
-//    (sequence, KV head).  Lane j and lane j + 32 dot key j's two halves of the dims with the G query
-//    heads (packed bf16 dots, fp32 sums); the softmax is a reduction over 32 lanes; each lane then adds
+//  * tail_merge_kernel: the tail of at most KM (16 or 32) keys and the merge in one pass, one wave
+//    per (sequence, KV head).  Lanes j, j + KM, ... dot key j's slices of the dims with the G query
+//    heads (packed bf16 dots, fp32 sums); the softmax is a reduction over KM lanes; each lane then adds
 //    two output dims over the keys, the probabilities read from their lanes as scalars, in fp32;
 //    and the shared part's (output, log-sum-exp) is folded in before the row is written.  In records
 //    mode (pa_decode_beam) the shared part is the partial records a records_only decode launch left
@@ -68,12 +68,15 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-template <int KV, int BS, int G, bool REC>
+template <int KV, int BS, int G, bool REC, int KM>
 __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, int out_bf16) {
   constexpr int D = 128;
   constexpr int E = KV == kBF16 ? 2 : 1;
   constexpr int TILE = BS * D * E;                 // bytes of one (block, KV head) tile
-  constexpr int NB = (kTailMax + BS - 1) / BS;     // blocks a tail can touch
+  static_assert(KM == 16 || KM == 32, "tails of at most 16 or 32 keys");
+  constexpr int LPK = 64 / KM;                     // lanes per key, each with DL of its dims
+  constexpr int DL = D / LPK;
+  constexpr int NB = (KM + BS - 1) / BS;           // blocks a tail can touch
   constexpr int NP = BS / 8;                       // 8-token pieces of a V^T row of one block
   constexpr int PW = 2 * E;                        // dwords of one piece (bf16 4, fp8 2)
   const int lane = threadIdx.x & 63;
@@ -123,18 +126,18 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
   const char* kbase = static_cast<const char*>(a.k_pool) + static_cast<int64_t>(kvh) * TILE;
   const char* vbase = static_cast<const char*>(a.v_pool) + static_cast<int64_t>(kvh) * TILE;
   const int64_t row0 = static_cast<int64_t>(seq) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
-  const int j = lane & 31, half = lane >> 5;
+  const int j = lane & (KM - 1), part = lane / KM;   // key j, dims DL part .. + DL
 
   // ---- every load first, so that the wave waits on memory once: q (for one head; a larger group
   // reads each head's q when it dots it, so as not to hold them all) and the prior state, which need
   // no table entry, then K and V ----
   auto q_row = [&](int g) __attribute__((always_inline)) {
-    return static_cast<const char*>(a.q) + ((row0 + g) * D + half * 64) * 2;
+    return static_cast<const char*>(a.q) + ((row0 + g) * D + part * DL) * 2;
   };
-  uint4 q1[8];
+  uint4 q1[DL / 8];
   if constexpr (G == 1) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) q1[c] = *reinterpret_cast<const uint4*>(q_row(0) + 16 * c);
+    for (int c = 0; c < DL / 8; ++c) q1[c] = *reinterpret_cast<const uint4*>(q_row(0) + 16 * c);
   }
   float2 po[G];
   float lp[G];
@@ -149,14 +152,14 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
   int64_t phys[NB];
 #pragma unroll
   for (int q = 0; q < NB; ++q) phys[q] = q * BS < L ? min(max(ent[q], 0), a.num_blocks - 1) : 0;
-  // K: key j's dims 64 half .. +64 (lane j and lane j + 32); zeros past the tail
-  uint32_t kraw[16 * E];   // 64 dims: 32 dwords of bf16, 16 of fp8
+  // K: key j's dims DL part .. + DL (lanes j, j + KM, ...); zeros past the tail
+  uint32_t kraw[DL * E / 4];   // DL dims: DL / 2 dwords of bf16, DL / 4 of fp8
 #pragma unroll
-  for (int c = 0; c < 16 * E; ++c) kraw[c] = 0u;
+  for (int c = 0; c < DL * E / 4; ++c) kraw[c] = 0u;
   if (j < L) {
-    const char* krow = kbase + phys[j / BS] * blk_stride + (j % BS) * (D * E) + half * 64 * E;
+    const char* krow = kbase + phys[j / BS] * blk_stride + (j % BS) * (D * E) + part * DL * E;
 #pragma unroll
-    for (int c = 0; c < 4 * E; ++c) {
+    for (int c = 0; c < DL * E / 16; ++c) {
       const uint4 v = *reinterpret_cast<const uint4*>(krow + 16 * c);
       kraw[4 * c] = v.x; kraw[4 * c + 1] = v.y; kraw[4 * c + 2] = v.z; kraw[4 * c + 3] = v.w;
     }
@@ -239,13 +242,13 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
   }
 
   // ---- base-2 logits of key j for each head (-inf past the tail) ----
-  uint32_t kw[32];   // bf16 pairs of the 64 dims
+  uint32_t kw[DL / 2];   // bf16 pairs of the DL dims
   if constexpr (E == 2) {
 #pragma unroll
-    for (int c = 0; c < 32; ++c) kw[c] = kraw[c];
+    for (int c = 0; c < DL / 2; ++c) kw[c] = kraw[c];
   } else {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < DL / 4; ++c) {
       kw[2 * c] = fp8x2_bf16<false>(kraw[c]);
       kw[2 * c + 1] = fp8x2_bf16<true>(kraw[c]);
     }
@@ -255,28 +258,29 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
   for (int g = 0; g < G; ++g) {
     float acc = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < DL / 8; ++c) {
       const uint4 qv = G == 1 ? q1[c] : *reinterpret_cast<const uint4*>(q_row(g) + 16 * c);
       acc = dot_bf16x2(kw[4 * c], qv.x, acc);
       acc = dot_bf16x2(kw[4 * c + 1], qv.y, acc);
       acc = dot_bf16x2(kw[4 * c + 2], qv.z, acc);
       acc = dot_bf16x2(kw[4 * c + 3], qv.w, acc);
     }
-    acc += shfl_xor(acc, 32);                      // the other half of the dims
+#pragma unroll
+    for (int off = KM; off < 64; off <<= 1) acc += shfl_xor(acc, off);   // the key's other dims
     x[g] = j < L ? acc * a.qk_scale : -INFINITY;
   }
-  // ---- softmax statistics over the 32 keys (both halves hold the same values) ----
+  // ---- softmax statistics over the KM keys (every lane of a key holds the same values) ----
   float p[G], m[G], l[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float mx = x[g];
 #pragma unroll
-    for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+    for (int off = KM / 2; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
     m[g] = mx;
     p[g] = L > 0 ? __builtin_amdgcn_exp2f(x[g] - mx) : 0.f;   // 0 past the tail
     float sm = p[g];
 #pragma unroll
-    for (int off = 16; off > 0; off >>= 1) sm += shfl_xor(sm, off);
+    for (int off = KM / 2; off > 0; off >>= 1) sm += shfl_xor(sm, off);
     l[g] = sm;
   }
   // ---- sum over the keys of p v, dims 2 lane and 2 lane + 1; values past the tail (any bits) are
@@ -351,29 +355,36 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
   }
 }
 
-template <int KV, int BS>
+template <int KV, int BS, int KM>
 int launch_tail_g(const TailMergeArgs& a, int ob, hipStream_t s, unsigned blocks) {
   if (a.width > 0) {
     if (a.num_q_heads != a.num_kv_heads) return -1;
-    hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 1, true>), dim3(blocks), dim3(kThreads), 0, s, a, ob);
+    hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 1, true, KM>), dim3(blocks), dim3(kThreads), 0, s, a, ob);
     return static_cast<int>(hipGetLastError());
   }
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 1, false>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
-    case 2: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 2, false>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
-    case 4: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 4, false>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
-    case 8: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 8, false>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 1: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 1, false, KM>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 2: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 2, false, KM>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 4: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 4, false, KM>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
+    case 8: hipLaunchKernelGGL((tail_merge_kernel<KV, BS, 8, false, KM>), dim3(blocks), dim3(kThreads), 0, s, a, ob); break;
     default: return -1;
   }
   return static_cast<int>(hipGetLastError());
 }
 
+// Tails of at most 16 keys take the 16-key form: four lanes per key, each with 32 of its dims, and
+// one 16-key V block at most, so the wave holds half the K, q and V registers of the 32-key form.
+template <int KV, int BS>
+int launch_tail_k(const TailMergeArgs& a, int ob, hipStream_t s, unsigned blocks) {
+  return a.max_tail <= 16 ? launch_tail_g<KV, BS, 16>(a, ob, s, blocks) : launch_tail_g<KV, BS, 32>(a, ob, s, blocks);
+}
+
 template <int KV>
 int launch_tail_bs(const TailMergeArgs& a, int block_size, int ob, hipStream_t s, unsigned blocks) {
   switch (block_size) {
-    case 8: return launch_tail_g<KV, 8>(a, ob, s, blocks);
-    case 16: return launch_tail_g<KV, 16>(a, ob, s, blocks);
-    case 32: return launch_tail_g<KV, 32>(a, ob, s, blocks);
+    case 8: return launch_tail_k<KV, 8>(a, ob, s, blocks);
+    case 16: return launch_tail_k<KV, 16>(a, ob, s, blocks);
+    case 32: return launch_tail_k<KV, 32>(a, ob, s, blocks);
     default: return -1;
   }
 }

@@ -155,21 +155,25 @@ def test_cascade_decode_of_beam_branches(size):
     assert diff <= TOL_BF16
 
 
-@pytest.mark.parametrize("kv,bs,group,out_f32", [("bf16", 16, 1, False), ("bf16", 8, 4, False),
-                                                 ("bf16", 32, 8, False), ("fp8", 16, 1, False),
-                                                 ("fp8", 8, 2, False), ("fp8", 32, 4, False),
-                                                 ("bf16", 16, 2, True), ("fp8", 16, 8, True)])
-def test_tail_merge_against_the_oracle(kv, bs, group, out_f32):
+@pytest.mark.parametrize("kv,bs,group,out_f32,kmax", [("bf16", 16, 1, False, 32), ("bf16", 8, 4, False, 32),
+                                                      ("bf16", 32, 8, False, 32), ("fp8", 16, 1, False, 32),
+                                                      ("fp8", 8, 2, False, 32), ("fp8", 32, 4, False, 32),
+                                                      ("bf16", 16, 2, True, 32), ("fp8", 16, 8, True, 32),
+                                                      ("bf16", 16, 1, False, 16), ("fp8", 8, 4, False, 16),
+                                                      ("bf16", 32, 8, True, 16)])
+def test_tail_merge_against_the_oracle(kv, bs, group, out_f32, kmax):
     """pa_decode_tail_merge: tails of 0..32 keys (every block boundary and the empty tail) merged into
     a prior (output, log-sum-exp) that is sometimes empty, against the fp64 oracle (the tail's
     attention by ref_decode and ref_lse, the merge written out), and against pa_decode_ex over the
-    tails followed by pa_merge_states."""
+    tails followed by pa_merge_states.  With kmax 16 the tails are cut to at most 16 keys and
+    max_tail_len is 16, which takes the kernel's 16-key form."""
     from paged_kv_cache_427_amd.ops import (make_pool_desc, pa_decode_ex, pa_decode_tail_merge,
                                             pa_decode_workspace_size, pa_merge_states)
     from paged_kv_cache_427_amd._lib import PA_BF16, PA_FP8_E4M3
     from oracle import decode_pool, e4m3_encode, pool_shape
     rng = np.random.default_rng(4274 + bs + group)
     lens = np.array([0, 1, 7, 8, 9, 15, 16, 17, 24, 31, 32, 5, 0, 32, 12], dtype=np.int32)
+    lens = np.minimum(lens, kmax)
     n, hkv, d = len(lens), 2, 128
     hq = hkv * group
     mb = -(-32 // bs)
@@ -205,7 +209,7 @@ def test_tail_merge_against_the_oracle(kv, bs, group, out_f32):
     op, lp = o_prev.to(dev), lse_prev.to(dev)
     out = torch.full((n, hq, d), 5.0, dtype=torch.float32 if out_f32 else torch.bfloat16, device=dev)
     _say("tail merge", kv, "b", bs, "G", group, "f32 out" if out_f32 else "bf16 out")
-    pa_decode_tail_merge(qd, kp, vp, pool, td, ld, scale, 32, op, lp, out)
+    pa_decode_tail_merge(qd, kp, vp, pool, td, ld, scale, kmax, op, lp, out)
     # the two-call path
     o_t = torch.empty((n, hq, d), dtype=torch.float32, device=dev)
     l_t = torch.empty((n, hq), dtype=torch.float32, device=dev)
@@ -242,16 +246,17 @@ def test_tail_merge_against_the_oracle(kv, bs, group, out_f32):
     assert np.max(np.abs(got[12] - on[12])) <= 1e-2
 
 
-@pytest.mark.parametrize("kv,bs,width,hkv,out_f32,long_shared", [
-    ("bf16", 16, 8, 8, False, False), ("bf16", 8, 4, 2, True, False), ("fp8", 32, 2, 8, False, False),
-    ("fp8", 16, 8, 2, False, True), ("bf16", 16, 8, 8, False, True)])
-def test_decode_beam_against_the_oracle(kv, bs, width, hkv, out_f32, long_shared):
+@pytest.mark.parametrize("kv,bs,width,hkv,out_f32,long_shared,kmax", [
+    ("bf16", 16, 8, 8, False, False, 32), ("bf16", 8, 4, 2, True, False, 32), ("fp8", 32, 2, 8, False, False, 32),
+    ("fp8", 16, 8, 2, False, True, 32), ("bf16", 16, 8, 8, False, True, 32), ("bf16", 16, 8, 8, False, True, 16),
+    ("fp8", 8, 4, 8, True, False, 16)])
+def test_decode_beam_against_the_oracle(kv, bs, width, hkv, out_f32, long_shared, kmax):
     """pa_decode_beam: groups of `width` branches whose shared parts are empty, one block, a few
     blocks or (long_shared) thousands of tokens cut into many pieces by the waves' shares, each
-    branch with a tail of 0..32 keys; against the fp64 oracle over the shared keys followed by the
-    tail's, and against the two-call path (pa_decode_ex over the shared part with its log-sum-exp,
-    then pa_decode_tail_merge).  The shared part and the tails as two calls (phases 1 then 2) give
-    the bits of one call with both phases."""
+    branch with a tail of 0..kmax keys (kmax 16 takes the tail kernel's 16-key form); against the
+    fp64 oracle over the shared keys followed by the tail's, and against the two-call path
+    (pa_decode_ex over the shared part with its log-sum-exp, then pa_decode_tail_merge).  The shared
+    part and the tails as two calls (phases 1 then 2) give the bits of one call with both phases."""
     from paged_kv_cache_427_amd.ops import (make_pool_desc, pa_decode_beam, pa_decode_ex, pa_decode_tail_merge,
                                             pa_decode_workspace_size)
     from paged_kv_cache_427_amd._lib import PA_BF16, PA_FP8_E4M3
@@ -263,8 +268,8 @@ def test_decode_beam_against_the_oracle(kv, bs, width, hkv, out_f32, long_shared
         shared[4] = 4100 // bs * bs
     groups = len(shared)
     n = groups * width
-    tails = rng.integers(0, 33, size=n).astype(np.int32)
-    tails[:3] = [0, 32, 1]
+    tails = rng.integers(0, kmax + 1, size=n).astype(np.int32)
+    tails[:3] = [0, kmax, 1]
     tails[width] = 0                                       # group 1: one shared block, no tail
     d = 128
     sblk = [s // bs for s in shared]
@@ -309,10 +314,10 @@ def test_decode_beam_against_the_oracle(kv, bs, width, hkv, out_f32, long_shared
     odt = torch.float32 if out_f32 else torch.bfloat16
     _say("beam decode", kv, "b", bs, "width", width, "kv heads", hkv, "longest shared part", smax)
     one = torch.full((n, hkv, d), 5.0, dtype=odt, device=dev)
-    pa_decode_beam(qd, kp, vp, pool, td, sl, smax, ttd, tl, 32, width, scale, ws, one, 3)
+    pa_decode_beam(qd, kp, vp, pool, td, sl, smax, ttd, tl, kmax, width, scale, ws, one, 3)
     two = torch.full((n, hkv, d), 5.0, dtype=odt, device=dev)
-    pa_decode_beam(qd, kp, vp, pool, td, sl, smax, ttd, tl, 32, width, scale, ws, two, 1)
-    pa_decode_beam(qd, kp, vp, pool, td, sl, smax, ttd, tl, 32, width, scale, ws, two, 2)
+    pa_decode_beam(qd, kp, vp, pool, td, sl, smax, ttd, tl, kmax, width, scale, ws, two, 1)
+    pa_decode_beam(qd, kp, vp, pool, td, sl, smax, ttd, tl, kmax, width, scale, ws, two, 2)
     # the two-call path: the shared part's output and log-sum-exp, then the tails merged into them
     o_pre = torch.empty((n, hkv, d), dtype=torch.float32, device=dev)
     l_pre = torch.empty((n, hkv), dtype=torch.float32, device=dev)
@@ -321,7 +326,7 @@ def test_decode_beam_against_the_oracle(kv, bs, width, hkv, out_f32, long_shared
     pa_decode_ex(qd, strides, groups, width * hkv, kp, vp, pool, td.data_ptr(), width * mb, sl, scale, o_pre,
                  strides, max(smax, 1), l_pre, ws2)
     ref2 = torch.empty((n, hkv, d), dtype=torch.float32, device=dev)
-    pa_decode_tail_merge(qd, kp, vp, pool, ttd, tl, scale, 32, o_pre, l_pre, ref2)
+    pa_decode_tail_merge(qd, kp, vp, pool, ttd, tl, scale, kmax, o_pre, l_pre, ref2)
     torch.cuda.synchronize()
     bits = torch.int32 if out_f32 else torch.int16
     assert torch.equal(one.view(bits), two.view(bits))
