@@ -56,7 +56,7 @@ __global__ void __launch_bounds__(kThreads) merge_states_kernel(MergeStatesArgs 
   if (a.lse_out && d == 0) a.lse_out[r] = m == -INFINITY ? -INFINITY : m + __logf(sum);
 }
 
-constexpr int kTailMax = 32;   // keys of a tail this kernel takes (lanes 0..31)
+constexpr int kTailMax = 32;   // keys of the longest tail this kernel takes
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot_bf16x2(uint32_t a, uint32_t b, float acc) {
