@@ -119,8 +119,11 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
     // the plan's loads complete with the table entries' (one wait before the K/V loads are issued),
     // instead of being sunk to their first use after those loads
     asm volatile("" ::"s"(p_lo), "s"(p_hi), "s"(p_all), "s"(rec_s), "s"(rec_pu));
-    rec_nj = p_hi - p_lo;
-    rec_p0 = rec_hh * p_all + p_lo;
+    // a plan that the shared launch did not write (a broken call order) gives wrong rows, never a
+    // walk outside the records: the counts are clamped to what any plan of these sizes can hold
+    rec_s = max(rec_s, 1);
+    rec_nj = min(max(p_hi - p_lo, 0), (a.shared.max_ctx + kDecodeUnit - 1) / kDecodeUnit);
+    rec_p0 = max(rec_hh * p_all + p_lo, 0);
   }
   const int64_t blk_stride = static_cast<int64_t>(a.num_kv_heads) * TILE;
   const char* kbase = static_cast<const char*>(a.k_pool) + static_cast<int64_t>(kvh) * TILE;
@@ -197,6 +200,7 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
       constexpr int kRec = D + 4;
       constexpr int kB = 4;
       const int gs = seq & (a.width - 1);
+      const int64_t rec_slots = static_cast<int64_t>(r.streams) * r.stream_slots;   // slots the records hold
       PieceWalk walk;
       walk.init(segment_slot(r, rec_x, rec_hh, rec_grp), rec_p0, rec_nj, rec_pu, rec_s);
       while (!walk.done()) {
@@ -207,7 +211,7 @@ __global__ void __launch_bounds__(kThreads) tail_merge_kernel(TailMergeArgs a, i
 #pragma unroll
         for (int b = 0; b < kB; ++b) {
           if (b == 0 || !walk.done()) {
-            off[b] = (walk.next() * a.width + gs) * kRec;
+            off[b] = (min(max(walk.next(), int64_t(0)), rec_slots - 1) * a.width + gs) * kRec;
             cnt = b + 1;
           } else {
             off[b] = off[0];
